@@ -1,0 +1,226 @@
+/*
+ * w4a16.h - C ABI of the MI355X (gfx950) W4A16 group-32 library.
+ *
+ * The operation (web page "The Weight of Precision: Building Native INT4
+ * Quantization for a Custom Speculative Decoding Engine", section "The Kernel:
+ * w4a16_gemm"): y = x * W where W is stored as symmetric INT4 codes
+ * (value = nibble - 8, range [-8, 7]) packed eight per int32 along the input
+ * dimension K, with one float32 scale per group of 32 input rows per output
+ * column.  Activations are float32 or bf16; accumulation and outputs are
+ * float32 (page "The Final Wire: How a Single Edit Integrated INT4
+ * Quantization into a Native DDTree Inference Engine", section "The
+ * Multi-Step Integration Chain").  The same path serves the dense SwiGLU MLP
+ * and the routed MoE experts (page "The Final Wire", section "What the Edit
+ * Actually Changes").
+ *
+ * Conventions for every entry point:
+ *  - Pointers to tensors are DEVICE pointers owned by the caller and must be
+ *    16-byte aligned.  Descriptors (w4a16_weight_t) and out-descriptors are
+ *    HOST pointers.  The library never allocates or frees device memory and
+ *    never synchronises the stream.
+ *  - Work is enqueued asynchronously on `stream`.  The returned status covers
+ *    host-side argument checks and launch errors only; a fault inside a kernel
+ *    surfaces at the caller's next synchronisation.
+ *  - There is no fallback path of any kind: an unsupported argument returns
+ *    an error and enqueues nothing.
+ *  - Row-major throughout: x is [M][K], y is [M][N].  y must not alias x.
+ *  - M == 0 (or a zero-sized weight) returns W4A16_OK and enqueues nothing.
+ *  - Workspaces come from the caller, sized by the matching *_workspace_bytes
+ *    query, and must be zero-filled once (w4a16_workspace_init) before their
+ *    first use; every call leaves its workspace ready for the next call.  Two
+ *    calls that may run at the same time must not share a workspace.
+ *  - The library keeps no mutable global state; calls on different streams
+ *    with different workspaces are independent.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define W4A16_API __attribute__((visibility("default")))
+#else
+#define W4A16_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, bad id range */
+  W4A16_ERR_UNSUPPORTED = 2, /* group size != 32, K % 32 != 0, N % 64 != 0, wrong layout */
+  W4A16_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace_bytes query */
+  W4A16_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} w4a16_status_t;
+
+typedef enum { W4A16_F32 = 0, W4A16_BF16 = 1 } w4a16_dtype_t;
+
+/*
+ * Weight layouts (both hold exactly K*N/8 int32 words per expert).
+ *  CANONICAL: qw[E][K/8][N]; nibble j (bits 4j..4j+3) of word (i, n) holds row
+ *             k = 8i + j.  This is the interchange format written by a
+ *             quantizer (w4a16_quantize).
+ *  GROUPED:   qw[E][K/32][N][4]; the 16-byte chunk (g, n) holds the four
+ *             canonical words 4g..4g+3 of column n, i.e. one whole 32-row
+ *             scale group of one column.  Compute entry points read this
+ *             layout only; w4a16_prepack converts.
+ * Scales are sc[E][K/32][N] float32 in both layouts.
+ */
+typedef enum { W4A16_LAYOUT_CANONICAL = 0, W4A16_LAYOUT_GROUPED = 1 } w4a16_layout_t;
+
+typedef struct {
+  const int32_t* qw;       /* device: packed codes, layout per `layout` */
+  const float* scales;     /* device: sc[E][K/32][N] */
+  int32_t K;               /* input dim, multiple of 32 */
+  int32_t N;               /* output dim, multiple of 64 */
+  int32_t group_size;      /* must be 32 */
+  int32_t num_experts;     /* 1 for a dense weight; E for an expert stack */
+  w4a16_layout_t layout;
+} w4a16_weight_t;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+W4A16_API const char* w4a16_status_string(w4a16_status_t status);
+
+/*
+ * Zero-fill a workspace of `bytes` bytes (a fill kernel, no memset node, so it
+ * may be captured in a graph).  Call once after allocating a workspace.
+ */
+W4A16_API w4a16_status_t w4a16_workspace_init(void* ws, size_t bytes, hipStream_t stream);
+
+/*
+ * Quantize float32 weights w[E][K][N] into CANONICAL codes qw[E][K/8][N] and
+ * scales sc[E][K/32][N] (page "The Weight of Precision", section "The Reference
+ * and Bundle Pipeline": the quantizer's outputs are packed int32 codes and
+ * float32 per-group scales).  The pages leave the rule open; this library
+ * uses scale = max|w| / 7 per 32-row group and column (one IEEE float32
+ * division) and code = clamp(round-half-even(w / scale), -8, 7) with the
+ * quotient formed in float64; an all-zero group gets scale 0 and code 0.
+ * Weights must be finite (not checked on the device).
+ * Errors: INVALID_ARG for null/misaligned pointers or K, N, E < 0;
+ * UNSUPPORTED for K % 32 != 0.
+ */
+W4A16_API w4a16_status_t w4a16_quantize(const float* w, int32_t K, int32_t N, int32_t num_experts,
+                              int32_t* qw, float* scales, hipStream_t stream);
+
+/*
+ * Permute CANONICAL codes into the GROUPED layout the compute kernels stream
+ * (one-time load step; the weight and scale maps of page "The Final Wire",
+ * section "The Multi-Step Integration Chain").  Scales are not moved: `out`
+ * receives a GROUPED descriptor that points at `dst_qw` and at src->scales.
+ * dst_qw must hold src->num_experts * K * N / 8 int32 and must not overlap
+ * src->qw.  Errors: INVALID_ARG (null/misaligned, out == NULL, overlap),
+ * UNSUPPORTED (src not CANONICAL, group size, K % 32, N % 64).
+ */
+W4A16_API w4a16_status_t w4a16_prepack(const w4a16_weight_t* src, int32_t* dst_qw, w4a16_weight_t* out,
+                             hipStream_t stream);
+
+/*
+ * Test hook, not on the hot path: materialise out[E][K][N] = float32(q * s),
+ * the exact product rounded once (page "The First Line of Code: Implementing
+ * W4A16 Quantization in a Native Speculative Decoding Engine", section "What
+ * the Edit Actually Does": dequantization must be identical to the
+ * reference's).  Accepts both layouts.  Same errors as w4a16_prepack, without
+ * the layout restriction.
+ */
+W4A16_API w4a16_status_t w4a16_dequantize(const w4a16_weight_t* w, float* out, hipStream_t stream);
+
+/* Bytes of workspace w4a16_gemm needs for this M, weight and activation type. */
+W4A16_API size_t w4a16_gemm_workspace_bytes(int32_t M, const w4a16_weight_t* w, w4a16_dtype_t xt);
+
+/*
+ * y[M][N] = x[M][K] * dequant(W), float32 accumulation and output (page "The
+ * Weight of Precision", section "The Kernel: w4a16_gemm").  W must be a dense
+ * (num_experts == 1) GROUPED weight.  Small M runs a split-K GEMV on the
+ * vector units; larger M runs MFMA tiles.  Deterministic: the same inputs give
+ * bitwise the same y.
+ * Errors: INVALID_ARG (null/misaligned, M < 0, bad dtype, y aliasing x),
+ * UNSUPPORTED (layout, group size, K % 32, N % 64, num_experts != 1),
+ * WORKSPACE (ws_bytes too small), HIP (launch failure).
+ */
+W4A16_API w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M, const w4a16_weight_t* w,
+                          float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of workspace w4a16_swiglu_mlp needs. */
+W4A16_API size_t w4a16_swiglu_mlp_workspace_bytes(int32_t M, w4a16_dtype_t xt, const w4a16_weight_t* gate,
+                                        const w4a16_weight_t* up, const w4a16_weight_t* down);
+
+/*
+ * Dense SwiGLU MLP: y = (silu(x Wg) * (x Wu)) Wd with silu(z) = z / (1 + e^-z)
+ * (page "The Final Wire", section "What the Edit Actually Changes": the dense
+ * MLP's gate, up and down projections run through the W4A16 path; page "The
+ * Weight of Precision", section "The Context That Produced This Message" names
+ * SwiGLU).  gate and up are [H -> I], down is [I -> H], all dense GROUPED.
+ * x is [M][H], y is [M][H] float32.  The gate and up projections run in one
+ * pass with the SiLU-times-up product formed in the epilogue; the
+ * intermediate h[M][I] lives in the workspace, float32 for float32 x and bf16
+ * for bf16 x.  Errors as w4a16_gemm, plus UNSUPPORTED if the three shapes do
+ * not chain.
+ */
+W4A16_API w4a16_status_t w4a16_swiglu_mlp(const void* x, w4a16_dtype_t xt, int32_t M,
+                                const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                const w4a16_weight_t* down, float* y, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/*
+ * Measurement variant of w4a16_swiglu_mlp: identical work and results, and in
+ * addition records the caller's events on `stream` around the kernels it
+ * launches: events[i] just before kernel i and one more after the last, at
+ * most `capacity` events; *recorded (if not NULL) receives how many were
+ * recorded.  The dense MLP launches three kernels: activation pieces, fused
+ * gate/up with the SwiGLU epilogue, down projection.  Events are created and
+ * owned by the caller.  Errors as w4a16_swiglu_mlp, plus INVALID_ARG for
+ * capacity < 0 or events == NULL with capacity > 0, and HIP if recording fails.
+ */
+W4A16_API w4a16_status_t w4a16_swiglu_mlp_timed(const void* x, w4a16_dtype_t xt, int32_t M,
+                                                const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                                const w4a16_weight_t* down, float* y, void* ws,
+                                                size_t ws_bytes, hipStream_t stream,
+                                                hipEvent_t* events, int32_t capacity,
+                                                int32_t* recorded);
+
+/*
+ * Group (token, slot) pairs by expert (page "The Final Wire", section "What
+ * the Edit Actually Changes": the router picks top-k experts per token and
+ * each expert runs its own projections).  Pair p = t * top_k + slot.  Outputs,
+ * all device int32: counts[E]; offsets[E+1] (exclusive prefix sum of counts);
+ * sorted_pairs[M*top_k], pair ids grouped by expert with ascending token
+ * inside an expert (unique, since a token's top_k ids are distinct); inv[M*top_k],
+ * the position of each pair in sorted_pairs.  topk_ids are int32 in [0, E),
+ * distinct per token; ids outside [0, E) are skipped on the device (they
+ * appear in no list and their inv entry is -1) rather than read out of bounds.
+ * Errors: INVALID_ARG (null/misaligned, M < 0, top_k < 1, top_k > E, E < 1).
+ */
+W4A16_API w4a16_status_t w4a16_moe_route(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_t E,
+                               int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                               int32_t* inv, hipStream_t stream);
+
+/* Bytes of workspace w4a16_moe_grouped needs. */
+W4A16_API size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype_t xt,
+                                 const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                 const w4a16_weight_t* down);
+
+/*
+ * Routed-expert SwiGLU MoE layer (page "The Final Wire", section "What the
+ * Edit Actually Changes"):
+ *   y[t] = sum over slot of topk_w[t][slot] * MLP_e(x[t]),  e = topk_ids[t][slot],
+ * summed in slot order, MLP_e as in w4a16_swiglu_mlp with expert e's weights.
+ * gate/up are GROUPED stacks [E][H -> Ie], down [E][Ie -> H].  x [M][H], topk_ids
+ * and topk_w [M][top_k] (int32 / float32), y [M][H] float32.  The routing lists
+ * (as w4a16_moe_route), the per-pair intermediate and the per-pair outputs
+ * live in the workspace; per-expert row counts never leave the device.
+ * Errors as w4a16_swiglu_mlp plus INVALID_ARG for top_k < 1 or top_k > E.
+ */
+W4A16_API w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int32_t M,
+                                 const int32_t* topk_ids, const float* topk_w, int32_t top_k,
+                                 const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                 const w4a16_weight_t* down, float* y, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_H */

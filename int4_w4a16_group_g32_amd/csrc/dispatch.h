@@ -1,0 +1,59 @@
+// Workspace plans and shared host helpers of the entry points (internal).
+#pragma once
+
+#include <algorithm>
+
+#include "gemv.h"
+
+namespace w4 {
+
+// Split-K arrival counters sit at the start of every workspace.
+constexpr size_t kCounterBytes = 64 * 1024;
+
+struct Carve {
+  size_t cursor = 0;
+  void take(size_t& off, size_t bytes);
+};
+
+struct GemmPlan {
+  int P = 0, S = 1;
+  int tiles = 0;
+  size_t tasks = 0;
+  size_t counters_off = 0, xq_off = 0, xf_off = 0, partials_off = 0;
+  size_t bytes = 0;
+};
+
+struct MlpPlan {
+  int P = 0;
+  int tiles_gu = 0, S_gu = 1, tiles_d = 0, S_d = 1;
+  size_t tasks_gu = 0, tasks_d = 0;
+  size_t counters_off = 0, xq_off = 0, xf_off = 0, hq_off = 0, hf_off = 0, partials_off = 0;
+  size_t bytes = 0;
+};
+
+// Optional measurement hook: records caller events on the stream between the
+// kernels an entry point launches (events[i] before kernel i, one after the last).
+struct EventMarks {
+  hipEvent_t* events = nullptr;
+  int capacity = 0;
+  int recorded = 0;
+  w4a16_status_t mark(hipStream_t stream) {
+    if (events == nullptr || recorded >= capacity) return W4A16_OK;
+    return hipEventRecord(events[recorded++], stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+  }
+};
+
+size_t gemv_partial_bytes(size_t tasks, int S);
+GemmPlan plan_gemm(int M, const w4a16_weight_t* w, w4a16_dtype_t xt);
+MlpPlan plan_mlp(int M, w4a16_dtype_t xt, const w4a16_weight_t* gate, const w4a16_weight_t* down);
+bool counters_fit(size_t tasks, int S);
+w4a16_status_t check_dense_grouped(const w4a16_weight_t* w);
+w4a16_status_t check_mlp(const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                         const w4a16_weight_t* down);
+bool ranges_overlap(const void* a, size_t abytes, const void* b, size_t bbytes);
+size_t dtype_bytes(w4a16_dtype_t xt);
+GemvArgs gemv_dense_args(int M, const w4a16_weight_t* w0, const w4a16_weight_t* w1, int mode,
+                         const int32_t* xq, const float* xf, int tiles, int S, char* ws,
+                         size_t partials_off, size_t counters_off);
+
+}  // namespace w4

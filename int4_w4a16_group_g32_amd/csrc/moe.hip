@@ -1,0 +1,320 @@
+// Routed-expert MoE layer: expert grouping of (token, slot) pairs, grouped
+// W4A16 GEMVs over the ragged per-expert row lists and the weighted combine.
+//
+// Page "The Final Wire: How a Single Edit Integrated INT4 Quantization into a
+// Native DDTree Inference Engine", section "What the Edit Actually Changes":
+// the router selects top-k experts per token and each selected expert runs its
+// own gate, up and down projections through the W4A16 path.  Per-expert row
+// counts are produced and consumed on the device only.
+#include "dispatch.h"
+
+namespace w4 {
+namespace {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteLdsInts = 12288;  // 48 KiB of per-chunk histograms
+
+// Stable counting sort of pairs p = t * top_k + slot by expert id, in one
+// workgroup.  Tokens are cut into C chunks; a per-(chunk, expert) histogram is
+// scanned along chunks per expert, then each chunk places its pairs in token
+// order.  Ids outside [0, E) are skipped (inv = -1).  Optionally also emits the
+// GEMV work items: each expert's list cut into blocks of at most `rows_per_item`.
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const int32_t* __restrict__ ids, int M, int top_k, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv,
+    int4* __restrict__ items, int32_t* __restrict__ n_items, int rows_per_item) {
+  extern __shared__ int hist[];  // [C][E]
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+  int C = kRouteLdsInts / E;
+  if (C > 64) C = 64;
+  if (C < 1) C = 1;
+  const int tok_per_chunk = (M + C - 1) / C;
+
+  for (int i = tid; i < C * E; i += kRouteThreads) hist[i] = 0;
+  __syncthreads();
+  // 1. per-chunk histograms
+  const int pairs = M * top_k;
+  for (int p = tid; p < pairs; p += kRouteThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&hist[(p / top_k / tok_per_chunk) * E + e], 1);
+  }
+  __syncthreads();
+  // 2. exclusive scan along chunks per expert; counts
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int run = 0;
+    for (int c = 0; c < C; ++c) {
+      const int v = hist[c * E + e];
+      hist[c * E + e] = run;
+      run += v;
+    }
+    counts[e] = run;
+  }
+  __syncthreads();
+  // 3. offsets = exclusive scan of counts (blocks of kRouteThreads, serial carry)
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  __shared__ int scan[kRouteThreads];
+  for (int base = 0; base < E; base += kRouteThreads) {
+    const int e = base + tid;
+    const int v = e < E ? counts[e] : 0;
+    scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kRouteThreads; off <<= 1) {
+      const int t = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += t;
+      __syncthreads();
+    }
+    if (e < E) offsets[e] = carry + scan[tid] - v;
+    __syncthreads();
+    if (tid == kRouteThreads - 1) carry += scan[tid];
+    __syncthreads();
+  }
+  if (tid == 0) offsets[E] = carry;
+  __syncthreads();
+  // 4. placement: chunk c walks its tokens in order
+  for (int c = tid; c < C; c += kRouteThreads) {
+    const int t0 = c * tok_per_chunk, t1 = min(M, t0 + tok_per_chunk);
+    for (int t = t0; t < t1; ++t) {
+      for (int s = 0; s < top_k; ++s) {
+        const int p = t * top_k + s;
+        const int e = ids[p];
+        if (e >= 0 && e < E) {
+          const int pos = offsets[e] + hist[c * E + e]++;
+          sorted_pairs[pos] = p;
+          inv[p] = pos;
+        } else {
+          inv[p] = -1;
+        }
+      }
+    }
+  }
+  if (items == nullptr) return;
+  __syncthreads();
+  // 5. GEMV items: exclusive scan of ceil(count / rows_per_item) over experts
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < E; base += kRouteThreads) {
+    const int e = base + tid;
+    const int n = e < E ? (counts[e] + rows_per_item - 1) / rows_per_item : 0;
+    scan[tid] = n;
+    __syncthreads();
+    for (int off = 1; off < kRouteThreads; off <<= 1) {
+      const int t = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += t;
+      __syncthreads();
+    }
+    if (e < E) {
+      int it = carry + scan[tid] - n;
+      const int c0 = counts[e], o0 = offsets[e];
+      for (int r = 0; r < c0; r += rows_per_item, ++it)
+        items[it] = make_int4(e, o0 + r, min(rows_per_item, c0 - r), 0);
+    }
+    __syncthreads();
+    if (tid == kRouteThreads - 1) carry += scan[tid];
+    __syncthreads();
+  }
+  if (tid == 0) *n_items = carry;
+}
+
+// y[t][n] = sum over slots, in slot order, of w[t][s] * o[inv[t*top_k+s]][n].
+__global__ void combine_kernel(const float* __restrict__ o, const int32_t* __restrict__ inv,
+                               const float* __restrict__ topk_w, int M, int top_k, int H,
+                               float* __restrict__ y) {
+  const size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  if (idx >= static_cast<size_t>(M) * H) return;
+  const int t = static_cast<int>(idx / H);
+  const int n = static_cast<int>(idx % H);
+  float acc = 0.0f;
+  for (int s = 0; s < top_k; ++s) {
+    const int pos = inv[t * top_k + s];
+    if (pos >= 0) acc = fmaf(topk_w[t * top_k + s], o[static_cast<size_t>(pos) * H + n], acc);
+  }
+  y[idx] = acc;
+}
+
+size_t route_lds_bytes(int E) {
+  int C = kRouteLdsInts / E;
+  if (C > 64) C = 64;
+  if (C < 1) C = 1;
+  return static_cast<size_t>(C) * E * sizeof(int);
+}
+
+w4a16_status_t launch_route(const int32_t* ids, int M, int top_k, int E, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_pairs, int32_t* inv, int4* items,
+                            int32_t* n_items, int rows_per_item, hipStream_t stream) {
+  if (E > kRouteLdsInts) return W4A16_ERR_UNSUPPORTED;
+  const size_t lds = route_lds_bytes(E);
+  route_kernel<<<1, kRouteThreads, lds, stream>>>(ids, M, top_k, E, counts, offsets, sorted_pairs,
+                                                   inv, items, n_items, rows_per_item);
+  return launch_status();
+}
+
+struct MoePlan {
+  int P = 0;
+  size_t pairs = 0, max_items = 0;
+  size_t counts_off, offsets_off, sorted_off, inv_off, items_off, nitems_off;
+  size_t xq_off, xf_off, hq_off, hf_off, o_off;
+  size_t bytes = 0;
+};
+
+MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate) {
+  MoePlan p;
+  p.P = pieces_for(xt);
+  const int E = gate->num_experts, H = gate->K, I = gate->N;
+  p.pairs = static_cast<size_t>(M) * top_k;
+  p.max_items = p.pairs / kMaxGemvRows + std::min<size_t>(E, p.pairs) + 1;
+  Carve c;
+  size_t dummy;
+  c.take(dummy, kCounterBytes);
+  c.take(p.counts_off, static_cast<size_t>(E) * 4);
+  c.take(p.offsets_off, static_cast<size_t>(E + 1) * 4);
+  c.take(p.sorted_off, p.pairs * 4);
+  c.take(p.inv_off, p.pairs * 4);
+  c.take(p.items_off, p.max_items * 16);
+  c.take(p.nitems_off, 16);
+  c.take(p.xq_off, p.pairs * (H / kGroup) * 8 * p.P * 4);
+  c.take(p.xf_off, p.pairs * (H / kGroup) * 4);
+  c.take(p.hq_off, p.pairs * (I / kGroup) * 8 * p.P * 4);
+  c.take(p.hf_off, p.pairs * (I / kGroup) * 4);
+  c.take(p.o_off, p.pairs * H * 4);
+  p.bytes = c.cursor;
+  return p;
+}
+
+w4a16_status_t check_moe(const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                         const w4a16_weight_t* down) {
+  const w4a16_weight_t* ws[3] = {gate, up, down};
+  for (const w4a16_weight_t* w : ws) {
+    w4a16_status_t st = check_weight(w);
+    if (st != W4A16_OK) return st;
+    if (w->layout != W4A16_LAYOUT_GROUPED) return W4A16_ERR_UNSUPPORTED;
+  }
+  if (gate->num_experts != up->num_experts || gate->num_experts != down->num_experts)
+    return W4A16_ERR_UNSUPPORTED;
+  if (gate->K != up->K || gate->N != up->N) return W4A16_ERR_UNSUPPORTED;
+  if (down->K != gate->N || down->N != gate->K) return W4A16_ERR_UNSUPPORTED;
+  return W4A16_OK;
+}
+
+}  // namespace
+}  // namespace w4
+
+using namespace w4;
+
+extern "C" w4a16_status_t w4a16_moe_route(const int32_t* topk_ids, int32_t M, int32_t top_k,
+                                          int32_t E, int32_t* counts, int32_t* offsets,
+                                          int32_t* sorted_pairs, int32_t* inv,
+                                          hipStream_t stream) {
+  if (M < 0 || E < 1 || top_k < 1 || top_k > E) return W4A16_ERR_INVALID_ARG;
+  if (counts == nullptr || offsets == nullptr) return W4A16_ERR_INVALID_ARG;
+  if (!aligned16(counts) || !aligned16(offsets)) return W4A16_ERR_INVALID_ARG;
+  if (M > 0) {
+    if (topk_ids == nullptr || sorted_pairs == nullptr || inv == nullptr) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(topk_ids) || !aligned16(sorted_pairs) || !aligned16(inv))
+      return W4A16_ERR_INVALID_ARG;
+  }
+  return launch_route(topk_ids, M, top_k, E, counts, offsets, sorted_pairs, inv, nullptr, nullptr,
+                      kMaxGemvRows, stream);
+}
+
+extern "C" size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype_t xt,
+                                            const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                            const w4a16_weight_t* down) {
+  if (M <= 0 || top_k < 1 || check_moe(gate, up, down) != W4A16_OK) return 0;
+  if (xt != W4A16_F32 && xt != W4A16_BF16) return 0;
+  return plan_moe(M, top_k, xt, gate).bytes;
+}
+
+extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int32_t M,
+                                            const int32_t* topk_ids, const float* topk_w,
+                                            int32_t top_k, const w4a16_weight_t* gate,
+                                            const w4a16_weight_t* up, const w4a16_weight_t* down,
+                                            float* y, void* ws, size_t ws_bytes,
+                                            hipStream_t stream) {
+  w4a16_status_t st = check_moe(gate, up, down);
+  if (st != W4A16_OK) return st;
+  const int E = gate->num_experts, H = gate->K, I = gate->N;
+  if (M < 0 || top_k < 1 || top_k > E || (xt != W4A16_F32 && xt != W4A16_BF16))
+    return W4A16_ERR_INVALID_ARG;
+  if (M == 0 || H == 0 || I == 0) return W4A16_OK;
+  if (x == nullptr || topk_ids == nullptr || topk_w == nullptr || y == nullptr || ws == nullptr)
+    return W4A16_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(y) ||
+      !aligned16(ws))
+    return W4A16_ERR_INVALID_ARG;
+  if (ranges_overlap(x, static_cast<size_t>(M) * H * dtype_bytes(xt), y,
+                     static_cast<size_t>(M) * H * 4))
+    return W4A16_ERR_INVALID_ARG;
+  const MoePlan p = plan_moe(M, top_k, xt, gate);
+  if (ws_bytes < p.bytes) return W4A16_ERR_WORKSPACE;
+  char* b = static_cast<char*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(b + p.counts_off);
+  int32_t* offsets = reinterpret_cast<int32_t*>(b + p.offsets_off);
+  int32_t* sorted = reinterpret_cast<int32_t*>(b + p.sorted_off);
+  int32_t* inv = reinterpret_cast<int32_t*>(b + p.inv_off);
+  int4* items = reinterpret_cast<int4*>(b + p.items_off);
+  int32_t* n_items = reinterpret_cast<int32_t*>(b + p.nitems_off);
+  int32_t* xq = reinterpret_cast<int32_t*>(b + p.xq_off);
+  float* xf = reinterpret_cast<float*>(b + p.xf_off);
+  int32_t* hq = reinterpret_cast<int32_t*>(b + p.hq_off);
+  float* hf = reinterpret_cast<float*>(b + p.hf_off);
+  float* o = reinterpret_cast<float*>(b + p.o_off);
+  const int R = static_cast<int>(p.pairs);
+
+  st = launch_route(topk_ids, M, top_k, E, counts, offsets, sorted, inv, items, n_items,
+                    kMaxGemvRows, stream);
+  if (st != W4A16_OK) return st;
+  st = launch_prep_pieces(x, xt, R, H, p.P, sorted, top_k, xq, xf, stream);
+  if (st != W4A16_OK) return st;
+
+  GemvArgs a{};
+  a.xq = xq;
+  a.xf = xf;
+  a.G = H / kGroup;
+  a.R = R;
+  a.qw0 = reinterpret_cast<const u32x4*>(gate->qw);
+  a.sc0 = gate->scales;
+  a.qw1 = reinterpret_cast<const u32x4*>(up->qw);
+  a.sc1 = up->scales;
+  a.expert_stride = static_cast<size_t>(H / kGroup) * I;
+  a.N = I;
+  a.tiles = I / 32;
+  a.S = 1;
+  a.gps = a.G;
+  a.dense_rows = 0;
+  a.items = items;
+  a.n_items = n_items;
+  a.mode = 1;
+  a.hq = hq;
+  a.hf = hf;
+  st = launch_gemv(a, p.P, p.max_items * a.tiles, stream);
+  if (st != W4A16_OK) return st;
+
+  GemvArgs d{};
+  d.xq = hq;
+  d.xf = hf;
+  d.G = I / kGroup;
+  d.R = R;
+  d.qw0 = reinterpret_cast<const u32x4*>(down->qw);
+  d.sc0 = down->scales;
+  d.expert_stride = static_cast<size_t>(I / kGroup) * H;
+  d.N = H;
+  d.tiles = H / 64;
+  d.S = 1;
+  d.gps = d.G;
+  d.dense_rows = 0;
+  d.items = items;
+  d.n_items = n_items;
+  d.mode = 0;
+  d.out = o;
+  st = launch_gemv(d, p.P, p.max_items * d.tiles, stream);
+  if (st != W4A16_OK) return st;
+
+  const size_t total = static_cast<size_t>(M) * H;
+  combine_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(o, inv, topk_w, M,
+                                                                                  top_k, H, y);
+  return launch_status();
+}

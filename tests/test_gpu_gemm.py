@@ -1,0 +1,97 @@
+"""GPU parity of w4a16_gemm against the oracle (float64 dequantize-then-matmul).
+
+Bounds: relative Frobenius error <= 1e-5 for float32 activations and <= 1e-2
+for bf16 activations; one-hot activations reproduce the oracle's float32
+dequantized weights bit for bit; repeated calls are bitwise identical."""
+import numpy as np
+import pytest
+import torch
+
+import int4_w4a16_group_g32_amd as L
+import oracle as O
+import workloads as W
+from helpers import rel_err, tol_for, weight_from_codes, x_for_dtype, x_values
+
+pytestmark = pytest.mark.gpu
+
+
+def _make(K, N, cfg, tag=W.TAG_GATE):
+    w = W.weights(K, N, cfg, tag).numpy()
+    qw, sc = O.quantize_w4a16(w)
+    return qw, sc, weight_from_codes(qw, sc)
+
+
+def _run_gemm(x, w, N):
+    y = torch.full((x.shape[0], N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = L.new_workspace(L.gemm_workspace_bytes(x.shape[0], w, L.F32 if x.dtype == torch.float32 else L.BF16))
+    L.gemm(x, w, y, ws)
+    torch.cuda.synchronize()
+    return y, ws
+
+
+SHAPES = [(32, 64), (64, 128), (192, 64), (256, 512), (1024, 192), (7168, 256)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K,N", SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 17])
+def test_gemm_small_shapes(M, K, N, dtype):
+    qw, sc, w = _make(K, N, 200 + K + N)
+    x = x_for_dtype(W.activations(M, K, 200 + M).cuda(), dtype)
+    y, _ = _run_gemm(x, w, N)
+    ref = O.gemm64(x_values(x), qw, sc)
+    err = rel_err(y, ref)
+    print(f"gemm M={M} K={K} N={N} {dtype} relF={err:.3e}", flush=True)
+    assert err <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_gemm_one_hot_rows_are_dequant_bit_exact(M):
+    """x = unit rows e_k: y row = float32(q[k][:] * s) exactly, for both the
+    in-kernel dequantization and the K-split reduction."""
+    K, N = 2048, 512
+    qw, sc, w = _make(K, N, 301)
+    ks = np.random.default_rng(M).choice(K, size=M, replace=False)
+    x = torch.zeros((M, K), dtype=torch.float32)
+    x[torch.arange(M), torch.as_tensor(ks)] = 1.0
+    y, _ = _run_gemm(x.cuda(), w, N)
+    ref = O.dequant32(qw, sc)[ks]
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_gemm_deterministic_and_workspace_reuse():
+    K, N = 7168, 1024
+    qw, sc, w = _make(K, N, 302)
+    ws = L.new_workspace(max(L.gemm_workspace_bytes(m, w, L.F32) for m in (1, 4, 8)))
+    outs = []
+    for M in (4, 1, 8, 4):
+        x = W.activations(M, K, 302).cuda()
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        L.gemm(x, w, y, ws)
+        torch.cuda.synchronize()
+        assert rel_err(y, O.gemm64(x_values(x), qw, sc)) <= 1e-5
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[3].view(np.uint32))
+
+
+def test_gemm_zero_rows_and_m0():
+    K, N = 256, 128
+    qw, sc, w = _make(K, N, 303)
+    x = torch.zeros((3, K), dtype=torch.float32, device="cuda")
+    y, ws = _run_gemm(x, w, N)
+    assert (y == 0).all()
+    y0 = torch.empty((0, N), dtype=torch.float32, device="cuda")
+    L.gemm(torch.empty((0, K), device="cuda"), w, y0, ws)  # no-op, no error
+
+
+def test_gemm_config_single_m1():
+    """The single-GEMM workload: M=1, K=256, N=512, float32, seed 0 stream."""
+    cfg = W.CONFIGS["gemm_m1"]
+    w_np = W.weights(cfg.K, cfg.N, cfg.index, W.TAG_GATE).numpy()
+    qw, sc = O.quantize_w4a16(w_np)
+    w = weight_from_codes(qw, sc)
+    x = W.activations(cfg.M, cfg.K, cfg.index).cuda()
+    y, _ = _run_gemm(x, w, cfg.N)
+    err = rel_err(y, O.gemm64(x_values(x), qw, sc))
+    print(f"gemm_m1 relF={err:.3e}", flush=True)
+    assert err <= 1e-5

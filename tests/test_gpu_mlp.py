@@ -1,0 +1,83 @@
+"""GPU parity of w4a16_swiglu_mlp against the oracle's float64 SwiGLU MLP,
+on small shapes (several tiles, ragged row counts) and on the full dense
+shape (hidden 7168, intermediate 18432) at M = 4 (float32) and M = 64
+(float32 and bf16), comparing sampled output columns."""
+import numpy as np
+import pytest
+import torch
+
+import int4_w4a16_group_g32_amd as L
+import oracle as O
+import workloads as W
+from helpers import rel_err, tol_for, weight_from_codes, x_for_dtype, x_values
+
+pytestmark = pytest.mark.gpu
+
+
+def _mlp_gpu(x, g, u, d):
+    xt = L.F32 if x.dtype == torch.float32 else L.BF16
+    ws = L.new_workspace(L.swiglu_mlp_workspace_bytes(x.shape[0], xt, g, u, d))
+    y = torch.full((x.shape[0], g.K), float("nan"), dtype=torch.float32, device="cuda")
+    L.swiglu_mlp(x, g, u, d, y, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("H,I", [(64, 128), (256, 512), (1024, 2048)])
+@pytest.mark.parametrize("M", [1, 3, 4, 8, 9])
+def test_mlp_small(M, H, I, dtype):
+    cfg = 400 + H
+    ws_np = [W.weights(H, I, cfg, W.TAG_GATE).numpy(), W.weights(H, I, cfg, W.TAG_UP).numpy(),
+             W.weights(I, H, cfg, W.TAG_DOWN).numpy()]
+    codes = [O.quantize_w4a16(w) for w in ws_np]
+    g, u, d = (weight_from_codes(*c) for c in codes)
+    x = x_for_dtype(W.activations(M, H, cfg + M).cuda(), dtype)
+    y = _mlp_gpu(x, g, u, d)
+    ref = O.swiglu_mlp64(x_values(x), *codes)
+    err = rel_err(y, ref)
+    print(f"mlp M={M} H={H} I={I} {dtype} relF={err:.3e}", flush=True)
+    assert err <= tol_for(dtype)
+
+
+@pytest.fixture(scope="module")
+def dense_mlp():
+    """The dense SwiGLU MLP (7168 -> 18432 -> 7168), weights drawn on the GPU,
+    quantized by the library and, independently, by the oracle."""
+    H, I, cfg = 7168, 18432, W.CONFIGS["mlp_decode_m4"].index
+    gpu, ora = [], []
+    for K, N, tag in ((H, I, W.TAG_GATE), (H, I, W.TAG_UP), (I, H, W.TAG_DOWN)):
+        w = W.weights(K, N, cfg, tag, device="cuda")
+        gpu.append(L.quantize_to_weight(w))
+        w_np = w.cpu().numpy()
+        del w
+        if tag == W.TAG_DOWN:
+            ora.append(w_np)  # quantized per sampled column below
+        else:
+            ora.append(O.quantize_w4a16(w_np))
+    torch.cuda.synchronize()
+    return H, I, gpu, ora
+
+
+def _sampled_down(w_down, cols):
+    return O.quantize_w4a16(np.ascontiguousarray(w_down[:, cols]))
+
+
+@pytest.mark.parametrize("name,dtype", [("mlp_decode_m4", "f32"), ("mlp_verify_m64_f32", "f32"),
+                                        ("mlp_verify_m64_bf16", "bf16")])
+def test_mlp_full_size(dense_mlp, name, dtype):
+    H, I, (g, u, d), (gq, uq, w_down) = dense_mlp
+    cfg = W.CONFIGS[name]
+    x = x_for_dtype(W.activations(cfg.M, H, cfg.index).cuda(), dtype)
+    y = _mlp_gpu(x, g, u, d)
+    cols = np.sort(np.random.default_rng(cfg.M).choice(H, size=512, replace=False))
+    xv = x_values(x)
+    h = O.silu64(O.gemm64(xv, *gq)) * O.gemm64(xv, *uq)
+    ref = h @ O.dequant64(*_sampled_down(w_down, cols))
+    err = rel_err(y[:, torch.as_tensor(cols, device="cuda")], ref)
+    print(f"{name} relF={err:.3e} (512 sampled columns)", flush=True)
+    assert err <= tol_for(dtype)
+    # the library's quantization of the same weights agrees with the oracle's
+    qd = d.qw.cpu().numpy().reshape(I // 32, H, 4)[:, cols, :]
+    qo = _sampled_down(w_down, cols)[0].reshape(I // 32, 4, len(cols)).transpose(0, 2, 1)
+    assert np.array_equal(qd, qo)
