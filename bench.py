@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 group-32 path on one MI355X.
+
+Default workload: the dense SwiGLU MLP at decode size (M = 4 tokens, hidden
+7168, intermediate 18432, float32 activations), one w4a16_swiglu_mlp call per
+step.  Weights are drawn on the GPU (seeded), quantized and prepacked by the
+library, and several copies are rotated across steps so the 256 MB Infinity
+Cache cannot serve them.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line with the step throughput (algorithmic HBM bytes per
+second), the roofline of the dominant kernel (fused gate/up GEMV, timed live
+with HIP events recorded by the library between its kernels) and the CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+METRIC = "W4A16 GEMM/MoE µs + achieved HBM GB/s (% of 8 TB/s) at decode M; TFLOP/s at M≥512"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def _events(n):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:  # torch creates the HIP event on first record
+        e.record()
+    return evs
+
+
+def _handles(evs):
+    arr = (ctypes.c_void_p * len(evs))()
+    for i, e in enumerate(evs):
+        arr[i] = e.cuda_event
+    return arr
+
+
+def mlp_bytes(M, H, I, xbytes):
+    weights = 3 * H * I * 5 // 8          # 0.5 B packed + 4/32 B scale per weight
+    return weights + M * H * xbytes + M * H * 4
+
+
+def gate_up_bytes(M, H, I, xbytes):
+    return 2 * H * I * 5 // 8 + M * H * xbytes + M * I * 4
+
+
+def run_mlp(args, cfg):
+    import torch
+    import int4_w4a16_group_g32_amd as L
+    import workloads as W
+
+    H, I, M = cfg.K, cfg.N, cfg.M
+    xt = L.F32 if cfg.x_dtype == "f32" else L.BF16
+    xbytes = 4 if cfg.x_dtype == "f32" else 2
+    base = []
+    for K, N, tag in ((H, I, W.TAG_GATE), (H, I, W.TAG_UP), (I, H, W.TAG_DOWN)):
+        w = W.weights(K, N, cfg.index, tag, device="cuda")
+        base.append(L.quantize_to_weight(w))
+        del w
+    copies = [base]
+    for _ in range(args.copies - 1):
+        copies.append([L.Weight(b.qw.clone(), b.scales.clone(), b.K, b.N, b.num_experts, b.layout) for b in base])
+    x = W.activations(M, H, cfg.index, cfg.x_dtype, device="cuda")
+    y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    ws = L.new_workspace(L.swiglu_mlp_workspace_bytes(M, xt, *base))
+    lib = L.load_library()
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    # kernels the library launches for one MLP call: decode sizes run the fused
+    # gate/up GEMV then the down GEMV; larger M runs activation pieces, gate/up
+    # MFMA, pieces of h, down MFMA
+    names = ["gate_up", "down"] if M <= 8 else ["prep_x", "gate_up", "prep_h", "down"]
+    nev = len(names) + 1
+
+    def step(i, evs=None):
+        g, u, d = copies[i % len(copies)]
+        rec = ctypes.c_int32(0)
+        st = lib.w4a16_swiglu_mlp_timed(L._ptr(x), xt, M, ctypes.byref(g.desc()), ctypes.byref(u.desc()),
+                                        ctypes.byref(d.desc()), L._ptr(y), L._ptr(ws),
+                                        ws.numel(), sptr, evs, 0 if evs is None else nev, ctypes.byref(rec))
+        if st != 0:
+            raise L.W4A16Error(st, "w4a16_swiglu_mlp_timed")
+        if evs is not None and rec.value != nev:
+            raise RuntimeError(f"expected {nev} events, got {rec.value}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [_events(nev) for _ in range(args.steps)]
+    handles = [_handles(e) for e in evs]
+    t0, t1 = _events(2)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i, handles[i])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    kern = {n: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    k_gu = kern["gate_up"]
+    step_bytes = mlp_bytes(M, H, I, xbytes)
+    gu_bytes = gate_up_bytes(M, H, I, xbytes)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = gu_bytes / (k_gu * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.x_dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "M": M, "hidden": H, "intermediate": I, "group_size": 32,
+                   "x_dtype": cfg.x_dtype, "weight_copies": args.copies, "bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": ("gemv_kernel" if M <= 8 else "mfma_kernel") +
+                     " (fused gate/up + SwiGLU epilogue)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(k_gu * 1e3, 2)},
+        "kernels_us": {n: round(v * 1e3, 2) for n, v in kern.items()},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_mlp(cfg, base)
+    return result
+
+
+def cpu_baseline_mlp(cfg, base):
+    """The oracle's float64 SwiGLU MLP on a slice of the same weights: the
+    first 2048 intermediate columns (gate/up [7168 x 2048], down [2048 x 7168]),
+    same activations.  Value in the same unit: algorithmic bytes of the slice
+    per second of oracle time (median of 3)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    import workloads as W
+
+    H, I, M = cfg.K, cfg.N, cfg.M
+    Is = 2048
+    g = W.weights(H, I, cfg.index, W.TAG_GATE, device="cuda")[:, :Is].cpu().numpy()
+    u = W.weights(H, I, cfg.index, W.TAG_UP, device="cuda")[:, :Is].cpu().numpy()
+    d = W.weights(I, H, cfg.index, W.TAG_DOWN, device="cuda")[:Is, :].cpu().numpy()
+    codes = [O.quantize_w4a16(np.ascontiguousarray(a)) for a in (g, u, d)]
+    x = W.activations(M, H, cfg.index, cfg.x_dtype, device="cuda").float().cpu().numpy()
+    times = []
+    for _ in range(3):
+        t = time.perf_counter()
+        O.swiglu_mlp64(x, *codes)
+        times.append(time.perf_counter() - t)
+    sec = statistics.median(times)
+    xbytes = 4 if cfg.x_dtype == "f32" else 2
+    nbytes = mlp_bytes(M, H, Is, xbytes)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{cfg.name} restricted to intermediate columns 0..{Is - 1} "
+                      f"({nbytes} algorithmic bytes), numpy float64, median of 3 runs of {sec:.2f}s",
+            "seconds": round(sec, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mlp_decode_m4")
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import torch
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = W.CONFIGS[args.workload]
+    if cfg.kind != "mlp":
+        print(f"workload {cfg.name} is a parity-test configuration, not a bench line", file=sys.stderr)
+        sys.exit(2)
+    result = run_mlp(args, cfg)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -170,8 +170,9 @@ W4A16_API w4a16_status_t w4a16_swiglu_mlp(const void* x, w4a16_dtype_t xt, int32
  * addition records the caller's events on `stream` around the kernels it
  * launches: events[i] just before kernel i and one more after the last, at
  * most `capacity` events; *recorded (if not NULL) receives how many were
- * recorded.  The dense MLP launches three kernels: activation pieces, fused
- * gate/up with the SwiGLU epilogue, down projection.  Events are created and
+ * recorded.  For M <= 8 the dense MLP launches two kernels (fused gate/up
+ * GEMV with the SwiGLU epilogue, down GEMV); for larger M four (activation
+ * pieces, fused gate/up MFMA tiles, pieces of the intermediate, down MFMA).  Events are created and
  * owned by the caller.  Errors as w4a16_swiglu_mlp, plus INVALID_ARG for
  * capacity < 0 or events == NULL with capacity > 0, and HIP if recording fails.
  */

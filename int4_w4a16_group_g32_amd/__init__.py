@@ -32,6 +32,7 @@ EXPORTS = (
     "w4a16_gemm",
     "w4a16_swiglu_mlp_workspace_bytes",
     "w4a16_swiglu_mlp",
+    "w4a16_swiglu_mlp_timed",
     "w4a16_moe_route",
     "w4a16_moe_workspace_bytes",
     "w4a16_moe_grouped",
@@ -78,6 +79,8 @@ def load_library() -> ctypes.CDLL:
             "w4a16_gemm": (i32, [vp, i32, i32, dp, vp, vp, sz, vp]),
             "w4a16_swiglu_mlp_workspace_bytes": (sz, [i32, i32, dp, dp, dp]),
             "w4a16_swiglu_mlp": (i32, [vp, i32, i32, dp, dp, dp, vp, vp, sz, vp]),
+            "w4a16_swiglu_mlp_timed": (i32, [vp, i32, i32, dp, dp, dp, vp, vp, sz, vp, vp, i32,
+                                             ctypes.POINTER(i32)]),
             "w4a16_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
             "w4a16_moe_workspace_bytes": (sz, [i32, i32, i32, dp, dp, dp]),
             "w4a16_moe_grouped": (i32, [vp, i32, i32, vp, vp, i32, dp, dp, dp, vp, vp, sz, vp]),

@@ -11,47 +11,132 @@ void Carve::take(size_t& off, size_t bytes) {
   cursor = round_up(cursor + bytes, 256);
 }
 
-size_t gemv_partial_bytes(size_t tasks, int S) {
-  return S > 1 ? tasks * S * kPartialTileFloats * sizeof(float) : 0;
+size_t gemv_partial_bytes(size_t tasks, int S, int sub) {
+  return S > 1 ? tasks * S * partial_tile_floats(sub) * sizeof(float) : 0;
+}
+
+MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt) {
+  MfmaPlan m;
+  m.P = mfma_pieces(xt);
+  m.Mp = mfma_rows_padded(rows);
+  m.items = (static_cast<size_t>(rows) + kMfmaRows - 1) / kMfmaRows;
+  const int per_tile = mode == 1 ? kMfmaCols / 2 : kMfmaCols;
+  m.tiles = (N + per_tile - 1) / per_tile;
+  m.tasks = m.items * m.tiles;
+  const int G = K / kGroup;
+  // split K while the grid is below about two workgroups per CU, keeping the
+  // partial tiles' write + read traffic under a quarter of the weight bytes
+  int S = static_cast<int>(512 / m.tasks);
+  const double wbytes_per_col = K * 0.625;
+  const double part_per_col_per_split = 8.0 * static_cast<double>(m.items) * kMfmaRows;
+  const int s_traffic = static_cast<int>(0.25 * wbytes_per_col / part_per_col_per_split);
+  if (S > s_traffic) S = s_traffic;
+  if (S > G / 4) S = G / 4;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (m.tasks * S * sizeof(int) > kCounterBytes) S = 1;
+  if (S < 1) S = 1;
+  m.S = S;
+  m.gps = (G + S - 1) / S;
+  return m;
+}
+
+size_t mfma_partial_bytes(const MfmaPlan& m) {
+  return m.S > 1 ? m.tasks * m.S * static_cast<size_t>(kMfmaRows) * kMfmaCols * sizeof(float) : 0;
+}
+
+MfmaArgs mfma_dense_args(const MfmaPlan& m, int rows, const w4a16_weight_t* w0,
+                         const w4a16_weight_t* w1, int mode, const _Float16* ap, const float* rs,
+                         char* ws, size_t partials_off, size_t counters_off) {
+  MfmaArgs a{};
+  a.ap = ap;
+  a.rs = rs;
+  a.Mp = m.Mp;
+  a.K = w0->K;
+  a.G = w0->K / kGroup;
+  a.qw0 = reinterpret_cast<const u32x4*>(w0->qw);
+  a.sc0 = w0->scales;
+  if (w1 != nullptr) {
+    a.qw1 = reinterpret_cast<const u32x4*>(w1->qw);
+    a.sc1 = w1->scales;
+  }
+  a.N = w0->N;
+  a.tiles = m.tiles;
+  a.S = m.S;
+  a.gps = m.gps;
+  a.dense_rows = rows;
+  a.mode = mode;
+  a.partials = reinterpret_cast<float*>(ws + partials_off);
+  a.counters = reinterpret_cast<int*>(ws + counters_off);
+  return a;
 }
 
 GemmPlan plan_gemm(int M, const w4a16_weight_t* w, w4a16_dtype_t xt) {
   GemmPlan p;
-  p.P = pieces_for(xt);
+  if (M > kMaxGemvRows) {
+    p.mfma = true;
+    p.mf = plan_mfma(M, w->N, 0, w->K, xt);
+    Carve c;
+    c.take(p.counters_off, kCounterBytes);
+    c.take(p.ap_off, static_cast<size_t>(p.mf.P) * p.mf.Mp * w->K * 2);
+    c.take(p.rs_off, static_cast<size_t>(p.mf.Mp) * 4);
+    c.take(p.partials_off, mfma_partial_bytes(p.mf));
+    p.bytes = c.cursor;
+    return p;
+  }
+  p.D = digits_for(xt);
   const int G = w->K / kGroup;
   const size_t items = (static_cast<size_t>(M) + kMaxGemvRows - 1) / kMaxGemvRows;
-  p.tiles = w->N / 64;
+  const GemvShape sh = gemv_shape(items, w->N, 0, G, kCounterBytes / sizeof(int));
+  p.sub = sh.sub;
+  p.tiles = sh.tiles;
   p.tasks = items * p.tiles;
-  p.S = gemv_splits(p.tasks, G);
+  p.S = sh.S;
   Carve c;
   c.take(p.counters_off, kCounterBytes);
-  c.take(p.xq_off, static_cast<size_t>(M) * G * 8 * p.P * 4);
-  c.take(p.xf_off, static_cast<size_t>(M) * G * 4);
-  c.take(p.partials_off, gemv_partial_bytes(p.tasks, p.S));
+  c.take(p.partials_off, gemv_partial_bytes(p.tasks, p.S, p.sub));
   p.bytes = c.cursor;
   return p;
 }
 
 MlpPlan plan_mlp(int M, w4a16_dtype_t xt, const w4a16_weight_t* gate, const w4a16_weight_t* down) {
   MlpPlan p;
-  p.P = pieces_for(xt);
+  if (M > kMaxGemvRows) {
+    const int H = gate->K, I = gate->N;
+    p.mfma = true;
+    p.gu = plan_mfma(M, I, 1, H, xt);
+    p.dn = plan_mfma(M, down->N, 0, I, xt);
+    const int P = p.gu.P, Mp = p.gu.Mp;
+    Carve c;
+    c.take(p.counters_off, kCounterBytes);
+    c.take(p.apx_off, static_cast<size_t>(P) * Mp * H * 2);
+    c.take(p.rsx_off, static_cast<size_t>(Mp) * 4);
+    c.take(p.h_off, static_cast<size_t>(Mp) * I * 4);
+    c.take(p.aph_off, static_cast<size_t>(P) * Mp * I * 2);
+    c.take(p.rsh_off, static_cast<size_t>(Mp) * 4);
+    c.take(p.partials_off, std::max(mfma_partial_bytes(p.gu), mfma_partial_bytes(p.dn)));
+    p.bytes = c.cursor;
+    return p;
+  }
+  p.D = digits_for(xt);
   const int H = gate->K, I = gate->N;
   const int GH = H / kGroup, GI = I / kGroup;
   const size_t items = (static_cast<size_t>(M) + kMaxGemvRows - 1) / kMaxGemvRows;
-  p.tiles_gu = I / 32;
+  const GemvShape gu = gemv_shape(items, I, 1, GH, kCounterBytes / sizeof(int));
+  p.sub_gu = gu.sub;
+  p.tiles_gu = gu.tiles;
   p.tasks_gu = items * p.tiles_gu;
-  p.S_gu = gemv_splits(p.tasks_gu, GH);
-  p.tiles_d = down->N / 64;
+  p.S_gu = gu.S;
+  const GemvShape dn = gemv_shape(items, down->N, 0, GI, kCounterBytes / sizeof(int));
+  p.sub_d = dn.sub;
+  p.tiles_d = dn.tiles;
   p.tasks_d = items * p.tiles_d;
-  p.S_d = gemv_splits(p.tasks_d, GI);
+  p.S_d = dn.S;
   Carve c;
   c.take(p.counters_off, kCounterBytes);
-  c.take(p.xq_off, static_cast<size_t>(M) * GH * 8 * p.P * 4);
-  c.take(p.xf_off, static_cast<size_t>(M) * GH * 4);
-  c.take(p.hq_off, static_cast<size_t>(M) * GI * 8 * p.P * 4);
+  c.take(p.hq_off, static_cast<size_t>(M) * GI * 4 * p.D * 4);
   c.take(p.hf_off, static_cast<size_t>(M) * GI * 4);
-  const size_t part = std::max(gemv_partial_bytes(p.tasks_gu, p.S_gu),
-                               gemv_partial_bytes(p.tasks_d, p.S_d));
+  const size_t part = std::max(gemv_partial_bytes(p.tasks_gu, p.S_gu, p.sub_gu),
+                               gemv_partial_bytes(p.tasks_d, p.S_d, p.sub_d));
   c.take(p.partials_off, part);
   p.bytes = c.cursor;
   return p;
@@ -76,12 +161,14 @@ bool ranges_overlap(const void* a, size_t abytes, const void* b, size_t bbytes) 
 size_t dtype_bytes(w4a16_dtype_t xt) { return xt == W4A16_F32 ? 4 : 2; }
 
 GemvArgs gemv_dense_args(int M, const w4a16_weight_t* w0, const w4a16_weight_t* w1, int mode,
-                         const int32_t* xq, const float* xf, int tiles, int S, char* ws,
-                         size_t partials_off, size_t counters_off) {
+                         const void* x, const int32_t* xq, const float* xf, int tiles, int S,
+                         char* ws, size_t partials_off, size_t counters_off) {
   GemvArgs a{};
+  a.x = x;
   a.xq = xq;
   a.xf = xf;
   a.G = w0->K / kGroup;
+  a.K = w0->K;
   a.R = M;
   a.qw0 = reinterpret_cast<const u32x4*>(w0->qw);
   a.sc0 = w0->scales;
@@ -125,16 +212,21 @@ extern "C" w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M,
     return W4A16_ERR_INVALID_ARG;
   const GemmPlan p = plan_gemm(M, w, xt);
   if (ws_bytes < p.bytes) return W4A16_ERR_WORKSPACE;
-  if (!counters_fit(p.tasks, p.S)) return W4A16_ERR_UNSUPPORTED;
   char* wsb = static_cast<char*>(ws);
-  int32_t* xq = reinterpret_cast<int32_t*>(wsb + p.xq_off);
-  float* xf = reinterpret_cast<float*>(wsb + p.xf_off);
-  st = launch_prep_pieces(x, xt, M, w->K, p.P, nullptr, 0, xq, xf, stream);
-  if (st != W4A16_OK) return st;
-  GemvArgs a = gemv_dense_args(M, w, nullptr, 0, xq, xf, p.tiles, p.S, wsb, p.partials_off,
-                               p.counters_off);
+  if (p.mfma) {
+    _Float16* ap = reinterpret_cast<_Float16*>(wsb + p.ap_off);
+    float* rs = reinterpret_cast<float*>(wsb + p.rs_off);
+    st = launch_mfma_prep(x, xt, M, p.mf.Mp, w->K, p.mf.P, nullptr, 0, ap, rs, stream);
+    if (st != W4A16_OK) return st;
+    MfmaArgs a = mfma_dense_args(p.mf, M, w, nullptr, 0, ap, rs, wsb, p.partials_off, p.counters_off);
+    a.out = y;
+    return launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream);
+  }
+  if (!counters_fit(p.tasks, p.S)) return W4A16_ERR_UNSUPPORTED;
+  GemvArgs a = gemv_dense_args(M, w, nullptr, 0, x, nullptr, nullptr, p.tiles, p.S, wsb,
+                               p.partials_off, p.counters_off);
   a.out = y;
-  return launch_gemv(a, p.P, p.tasks * p.S, stream);
+  return launch_gemv(a, p.D, p.sub, xt == W4A16_F32 ? kInF32 : kInBF16, p.tasks * p.S, stream);
 }
 
 extern "C" size_t w4a16_swiglu_mlp_workspace_bytes(int32_t M, w4a16_dtype_t xt,
@@ -175,28 +267,51 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
     return W4A16_ERR_INVALID_ARG;
   const MlpPlan p = plan_mlp(M, xt, gate, down);
   if (ws_bytes < p.bytes) return W4A16_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(ws);
+  if (p.mfma) {
+    const int H = gate->K, I = gate->N;
+    _Float16* apx = reinterpret_cast<_Float16*>(wsb + p.apx_off);
+    float* rsx = reinterpret_cast<float*>(wsb + p.rsx_off);
+    float* h = reinterpret_cast<float*>(wsb + p.h_off);
+    _Float16* aph = reinterpret_cast<_Float16*>(wsb + p.aph_off);
+    float* rsh = reinterpret_cast<float*>(wsb + p.rsh_off);
+    if ((st = ev.mark(stream)) != W4A16_OK) return st;
+    st = launch_mfma_prep(x, xt, M, p.gu.Mp, H, p.gu.P, nullptr, 0, apx, rsx, stream);
+    if (st != W4A16_OK) return st;
+    MfmaArgs a = mfma_dense_args(p.gu, M, gate, up, 1, apx, rsx, wsb, p.partials_off, p.counters_off);
+    a.h = h;
+    a.h_bf16 = 0;
+    if ((st = ev.mark(stream)) != W4A16_OK) return st;
+    st = launch_mfma(a, p.gu.P, p.gu.tasks * p.gu.S, stream);
+    if (st != W4A16_OK) return st;
+    if ((st = ev.mark(stream)) != W4A16_OK) return st;
+    st = launch_mfma_prep(h, W4A16_F32, M, p.dn.Mp, I, p.dn.P, nullptr, 0, aph, rsh, stream);
+    if (st != W4A16_OK) return st;
+    MfmaArgs d = mfma_dense_args(p.dn, M, down, nullptr, 0, aph, rsh, wsb, p.partials_off,
+                                 p.counters_off);
+    d.out = y;
+    if ((st = ev.mark(stream)) != W4A16_OK) return st;
+    st = launch_mfma(d, p.dn.P, p.dn.tasks * p.dn.S, stream);
+    if (st != W4A16_OK) return st;
+    return ev.mark(stream);
+  }
   if (!counters_fit(p.tasks_gu, p.S_gu) || !counters_fit(p.tasks_d, p.S_d))
     return W4A16_ERR_UNSUPPORTED;
-  char* wsb = static_cast<char*>(ws);
-  int32_t* xq = reinterpret_cast<int32_t*>(wsb + p.xq_off);
-  float* xf = reinterpret_cast<float*>(wsb + p.xf_off);
   int32_t* hq = reinterpret_cast<int32_t*>(wsb + p.hq_off);
   float* hf = reinterpret_cast<float*>(wsb + p.hf_off);
-  if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_prep_pieces(x, xt, M, gate->K, p.P, nullptr, 0, xq, xf, stream);
-  if (st != W4A16_OK) return st;
-  GemvArgs a = gemv_dense_args(M, gate, up, 1, xq, xf, p.tiles_gu, p.S_gu, wsb, p.partials_off,
-                               p.counters_off);
+  GemvArgs a = gemv_dense_args(M, gate, up, 1, x, nullptr, nullptr, p.tiles_gu, p.S_gu, wsb,
+                               p.partials_off, p.counters_off);
   a.hq = hq;
   a.hf = hf;
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(a, p.P, p.tasks_gu * p.S_gu, stream);
+  st = launch_gemv(a, p.D, p.sub_gu, xt == W4A16_F32 ? kInF32 : kInBF16, p.tasks_gu * p.S_gu,
+                   stream);
   if (st != W4A16_OK) return st;
-  GemvArgs d = gemv_dense_args(M, down, nullptr, 0, hq, hf, p.tiles_d, p.S_d, wsb, p.partials_off,
-                               p.counters_off);
+  GemvArgs d = gemv_dense_args(M, down, nullptr, 0, nullptr, hq, hf, p.tiles_d, p.S_d, wsb,
+                               p.partials_off, p.counters_off);
   d.out = y;
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(d, p.P, p.tasks_d * p.S_d, stream);
+  st = launch_gemv(d, p.D, p.sub_d, kInDigits, p.tasks_d * p.S_d, stream);
   if (st != W4A16_OK) return st;
   return ev.mark(stream);
 }

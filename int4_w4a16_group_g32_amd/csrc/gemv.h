@@ -5,26 +5,35 @@
 
 namespace w4 {
 
-// Activation rows enter the GEMV as signed fixed point per (row, 32-row group):
-// X = rint(x * 2^sh) with |X| <= 2^(8P-2), split into P signed bytes
-// (X = sum_p piece_p * 256^(P-1-p)).  P = 3 keeps float32 activations to
-// 2^-23 of the group's largest magnitude, P = 2 keeps bf16 activations to
-// 2^-15.  Per (row, group) the pieces take 8P dwords laid out as
-// [piece][word j][parity], byte b of dword (p, j, par) holding element
-// k = 8j + 2b + par; the float factor 2^-(sh+4) undoes the scaling and the
-// x16 carried by the byte-expanded weights.
+// Activations enter the GEMV as signed fixed point per (row, 32-row group):
+// X = rint(x * 2^sh), split into D balanced signed 4-bit digits,
+// X = sum_d digit_d * 16^(D-1-d), digit in [-8, 7].  sh is the largest integer
+// with max|x| * 2^sh <= 3 * 2^(4D-3), which keeps every digit in range and the
+// rounding error below 2^-(4D-2) of the group's largest magnitude.  D = 5 for
+// float32 activations (20 bits), D = 4 for bf16 (16 bits, above bf16's 8).
+// Per (row, group) the digits take 4D dwords, dword (d, j) holding digit d of
+// elements k = 8j .. 8j+7 in nibble order, plus one float factor 2^-sh.
 //
-// Pieces are stored group-major by position: xq[g][pos][8P], xf[g][pos], so
-// the rows of one task are adjacent and one scalar base pointer with
-// immediate offsets reaches all of them.  Positions are token rows for a
-// dense call and (expert, token) pairs in routed order for the MoE.
-inline int pieces_for(w4a16_dtype_t xt) { return xt == W4A16_F32 ? 3 : 2; }
+// Digits made by one kernel for another (the SwiGLU epilogue's output) are
+// stored group-major by position: xq[g][pos][4D], xf[g][pos], so the rows of
+// one task are adjacent.
+inline int digits_for(w4a16_dtype_t xt) { return xt == W4A16_F32 ? 5 : 4; }
+
+enum GemvInput : int {
+  kInDigits = 0,  // xq / xf digits (group-major by position)
+  kInF32 = 1,     // float32 rows of x, optionally gathered
+  kInBF16 = 2,    // bf16 rows of x, optionally gathered
+};
 
 struct GemvArgs {
-  const int32_t* xq;   // [G][R][8P] pieces of the input positions
-  const float* xf;     // [G][R] factors
+  const void* x;       // raw activations [rows][K] (kInF32 / kInBF16)
+  const int* gather;   // raw input: position p reads row gather[p] / top_k (nullptr: row p)
+  int top_k;
+  const int32_t* xq;   // kInDigits: [G][R][4D]
+  const float* xf;     // kInDigits: [G][R]
   int G;               // groups along K (K / 32)
-  int R;               // positions held in xq / xf
+  int K;
+  int R;               // positions held in xq / xf and produced into hq / hf
   const u32x4* qw0;    // GROUPED chunks, matrix 0 (plain, or gate)
   const float* sc0;
   const u32x4* qw1;    // matrix 1 (up) for the SwiGLU mode, else null
@@ -39,7 +48,7 @@ struct GemvArgs {
   const int* n_items;    // grouped mode: number of valid items (device)
   int mode;              // 0: plain float32 output, 1: SwiGLU epilogue
   float* out;            // plain: out[position][N]
-  int32_t* hq;           // SwiGLU: pieces of h, [N/32][R][8P]
+  int32_t* hq;           // SwiGLU: digits of h, [N/32][R][4D]
   float* hf;             // SwiGLU: factors of h, [N/32][R]
   void* h_raw;           // SwiGLU, optional: h[position][N] as float32 or bf16
   int h_bf16;
@@ -48,17 +57,36 @@ struct GemvArgs {
 };
 
 constexpr int kGemvThreads = 256;
-constexpr size_t kPartialTileFloats = static_cast<size_t>(kMaxGemvRows) * 64;
+constexpr int kMaxSplits = 32;  // K splits of one GEMV (partials read back together)
 
-// Pieces of R positions.  With sorted_pairs == nullptr position p is row p of
-// x; otherwise it is row sorted_pairs[p] / top_k, and a negative pair id gives
-// zero pieces and a zero factor.
-w4a16_status_t launch_prep_pieces(const void* x, w4a16_dtype_t xt, int R, int K, int P,
-                                  const int* sorted_pairs, int top_k, int32_t* xq, float* xf,
-                                  hipStream_t stream);
-w4a16_status_t launch_gemv(const GemvArgs& a, int P, size_t num_tasks, hipStream_t stream);
+// Launch-shape defaults (overridable at compile time for tuning sweeps).
+#ifndef W4_GEMV_TARGET_WGS
+#define W4_GEMV_TARGET_WGS 1024
+#endif
+#ifndef W4_GEMV_MIN_GROUPS_PER_WAVE
+#define W4_GEMV_MIN_GROUPS_PER_WAVE 6
+#endif
+#ifndef W4_GEMV_SUB
+#define W4_GEMV_SUB 4
+#endif
+#ifndef W4_GEMV_WAVES_PER_EU
+#define W4_GEMV_WAVES_PER_EU 4
+#endif
 
-// Split count for a GEMV over `tasks` (item, tile) pairs with G groups.
-int gemv_splits(size_t tasks, int G);
+// Launch shape of one GEMV: columns per lane, column tiles per row item, K
+// splits.  Chosen so the grid fills the resident capacity of the GPU (about
+// W4_GEMV_TARGET_WGS workgroups) as evenly as possible, preferring more
+// columns per lane (fewer LDS reads per dot product) when the fill is similar.
+struct GemvShape {
+  int sub = 1, tiles = 1, S = 1;
+};
+GemvShape gemv_shape(size_t items, int N, int mode, int G, size_t max_split_tasks);
+
+// floats of one split-K partial tile
+inline size_t partial_tile_floats(int sub) { return static_cast<size_t>(kMaxGemvRows) * 64 * sub; }
+
+w4a16_status_t launch_gemv(const GemvArgs& a, int D, int SUB, int input, size_t num_tasks,
+                           hipStream_t stream);
+
 
 }  // namespace w4

@@ -3,195 +3,204 @@
 // y[m][n] = sum_g s[g][n] * sum_{k in g} x[m][k] * q[k][n]   (page "The Weight
 // of Precision: Building Native INT4 Quantization for a Custom Speculative
 // Decoding Engine", section "The Kernel: w4a16_gemm": per-group scales on
-// symmetric INT4 codes).  Each lane owns one output column and streams that
-// column's 16-byte group chunks (32 codes) with one dwordx4 load per group.
-// The codes are expanded to bytes holding 16*q and contracted with the
-// activation's fixed-point pieces by v_dot4_i32_i8; the pieces are
-// wave-uniform and live in scalar registers.  The per-group integer sums are
-// exact; each becomes float32 once and is scaled by s * factor.
+// symmetric INT4 codes).
+//
+// Each lane owns SUB output columns (64 apart, so one wave load reads 1 KiB of
+// contiguous 16-byte group chunks) and streams one chunk (32 codes) per group
+// and column.  The codes need one XOR to become signed nibbles; activations
+// are signed 4-bit digits of per-group fixed point (gemv.h), staged by each
+// wave in its own LDS window and read back as uniform vectors.  v_dot8_i32_i4
+// contracts eight codes with eight digits, Horner steps by 16 join the
+// digits, and each group's exact integer sum becomes float32 once and is
+// scaled by s * 2^-sh.
 #include "gemv.h"
 
 namespace w4 {
 namespace {
 
-// ------------------------------------------------------------ fixed-point pieces
+constexpr int kWin = 8;  // groups per staging window of one wave
 
-template <int P>
-__device__ __forceinline__ int piece_shift(float amax) {
+// Largest sh with amax * 2^sh <= 3 * 2^(4D-3).
+template <int D>
+__device__ __forceinline__ int digit_shift(float amax) {
   if (!(amax > 0.0f)) return 0;
-  constexpr int L = 8 * P - 2;  // |X| <= 2^L
-  int sh = (L - 1) - ilogbf(amax);
+  const int e = ilogbf(amax);
+  const float m = ldexpf(amax, -e);  // [1, 2)
+  const int sh = (4 * D - 2 - e) - (m > 1.5f ? 1 : 0);
   return sh > 120 ? 120 : sh;
 }
 
-template <int P>
-__device__ __forceinline__ void split_pieces(float v, int sh, int pc[P]) {
-  int X = static_cast<int>(rintf(ldexpf(v, sh)));
-  if (P == 3) {
-    const int p2 = static_cast<int8_t>(X & 0xff);
-    const int t = (X - p2) >> 8;
-    const int p1 = static_cast<int8_t>(t & 0xff);
-    pc[0] = (t - p1) >> 8;
-    pc[1] = p1;
-    pc[P - 1] = p2;
-  } else {
-    const int p1 = static_cast<int8_t>(X & 0xff);
-    pc[0] = (X - p1) >> 8;
-    pc[P - 1] = p1;
+// Biased fixed point of v: the low 4D bits of the result are X + B with
+// X = round(v * 2^sh) and B = 8 * (16^D - 1) / 15, so hex digit d (from the top)
+// of X + B is the balanced digit d of X plus 8.  One FMA: adding 2^23 + B to the
+// exact product v * 2^sh leaves the rounded integer in the float's mantissa
+// bits (|X| + B < 2^23).
+template <int D>
+__device__ __forceinline__ uint32_t biased_fixed(float v, float scale) {
+  constexpr float kMagic = 8388608.0f + static_cast<float>(8 * ((1 << (4 * D)) - 1) / 15);
+  return __float_as_uint(fmaf(v, scale, kMagic));
+}
+
+// Balanced digit d (most significant first) of a biased_fixed value, as a
+// two's-complement nibble in bits 0..3.
+template <int D>
+__device__ __forceinline__ uint32_t digit_nibble(uint32_t xb, int d) {
+  return ((xb >> (4 * (D - 1 - d))) & 15u) ^ 8u;
+}
+
+template <int D>
+struct WaveWindow {
+  int32_t dig[kWin][kMaxGemvRows][4 * D];
+  float fac[kWin][kMaxGemvRows];
+};
+
+template <int D, int SUB>
+union GemvLds {
+  WaveWindow<D> win[kGemvThreads / kWave];
+  float red[kGemvThreads / kWave][kMaxGemvRows][64 * SUB];
+};
+
+template <typename XT>
+__device__ __forceinline__ float act(const void* x, size_t i) {
+  return load_act(static_cast<const XT*>(x), i);
+}
+
+// Lane (gi, r) = (lane >> 3, lane & 7) fills item (group gw + gi, row r) of the
+// wave's window.
+template <int D, int IN>
+__device__ __forceinline__ void stage_window(const GemvArgs& a, WaveWindow<D>& w, int gw, int nw,
+                                             int pos0, int nrows, int lane) {
+  const int gi = lane >> 3, r = lane & 7;
+  if (gi >= nw || r >= nrows) return;
+  const int g = gw + gi;
+  const int pos = pos0 + r;
+  if (IN == kInDigits) {
+    const int32_t* src = a.xq + (static_cast<size_t>(g) * a.R + pos) * (4 * D);
+#pragma unroll
+    for (int i = 0; i < 4 * D; ++i) w.dig[gi][r][i] = src[i];
+    w.fac[gi][r] = a.xf[static_cast<size_t>(g) * a.R + pos];
+    return;
   }
-}
-
-// Byte offset of (piece p, element c) inside one (row, group) block.
-__device__ __forceinline__ int piece_byte(int p, int c) {
-  const int j = c >> 3, b = c & 7;
-  return (((p * 4 + j) * 2 + (b & 1)) << 2) + (b >> 1);
-}
-
-// One thread per (position, group).
-template <typename XT, int P>
-__global__ void prep_pieces_kernel(const XT* __restrict__ x, int R, int K,
-                                   const int* __restrict__ sorted_pairs, int top_k,
-                                   int32_t* __restrict__ xq, float* __restrict__ xf) {
-  const int G = K / kGroup;
-  const size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
-  if (idx >= static_cast<size_t>(R) * G) return;
-  const int pos = static_cast<int>(idx % R);
-  const int g = static_cast<int>(idx / R);
   long row = pos;
-  if (sorted_pairs != nullptr) {
-    const int pr = sorted_pairs[pos];
-    row = pr < 0 ? -1 : pr / top_k;
+  if (a.gather != nullptr) {
+    const int pr = a.gather[pos];
+    row = pr < 0 ? -1 : pr / a.top_k;
   }
-  float v[kGroup];
+  // two passes over the group's 32 activations (the second hits the cache):
+  // the largest magnitude first, then the digits, eight elements at a time
+  const size_t base = static_cast<size_t>(row < 0 ? 0 : row) * a.K + static_cast<size_t>(g) * kGroup;
   float amax = 0.0f;
-  const XT* src = x + (row < 0 ? 0 : row) * K + static_cast<size_t>(g) * kGroup;
+  if (row >= 0) {
+#pragma unroll
+    for (int c = 0; c < kGroup; ++c)
+      amax = fmaxf(amax, fabsf(IN == kInF32 ? act<float>(a.x, base + c) : act<uint16_t>(a.x, base + c)));
+  }
+  const int sh = digit_shift<D>(amax);
+  const float scale = row < 0 ? 0.0f : ldexpf(1.0f, sh);
+  uint32_t dw[4 * D];
+#pragma unroll
+  for (int i = 0; i < 4 * D; ++i) dw[i] = 0;
 #pragma unroll
   for (int c = 0; c < kGroup; ++c) {
-    v[c] = row < 0 ? 0.0f : load_act(src, c);
-    amax = fmaxf(amax, fabsf(v[c]));
+    const float xv = row < 0 ? 0.0f : (IN == kInF32 ? act<float>(a.x, base + c) : act<uint16_t>(a.x, base + c));
+    const uint32_t xb = biased_fixed<D>(xv, scale);
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      dw[d * 4 + (c >> 3)] |= ((xb >> (4 * (D - 1 - d))) & 15u) << (4 * (c & 7));
   }
-  const int sh = piece_shift<P>(amax);
-  uint32_t dw[8 * P];
 #pragma unroll
-  for (int i = 0; i < 8 * P; ++i) dw[i] = 0;
-#pragma unroll
-  for (int c = 0; c < kGroup; ++c) {
-    int pc[P];
-    split_pieces<P>(v[c], sh, pc);
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int byte = piece_byte(p, c);
-      dw[byte >> 2] |= (static_cast<uint32_t>(pc[p]) & 0xffu) << (8 * (byte & 3));
-    }
-  }
-  u32x4* dst = reinterpret_cast<u32x4*>(xq + idx * (8 * P));  // idx == g * R + pos
-#pragma unroll
-  for (int i = 0; i < 2 * P; ++i) {
-    u32x4 t = {dw[4 * i], dw[4 * i + 1], dw[4 * i + 2], dw[4 * i + 3]};
-    dst[i] = t;
-  }
-  xf[idx] = amax > 0.0f ? ldexpf(1.0f, -sh - 4) : 0.0f;
+  for (int i = 0; i < 4 * D; ++i) w.dig[gi][r][i] = static_cast<int32_t>(dw[i] ^ 0x88888888u);
+  w.fac[gi][r] = amax > 0.0f ? ldexpf(1.0f, -sh) : 0.0f;
 }
 
-// ------------------------------------------------------------ the GEMV core
-
-// Integer dot of one row's pieces with one group's byte-expanded codes.
-template <int P>
-__device__ __forceinline__ float group_dot(const int32_t* __restrict__ xp, const int32_t we[4],
-                                           const int32_t wo[4]) {
-  int a = 0;
+template <int SUB>
+__device__ __forceinline__ void load_group(const u32x4* __restrict__ wq, const float* __restrict__ ws,
+                                           size_t gstride, int cstride, int g, u32x4 w[SUB],
+                                           float s[SUB]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    a = __builtin_amdgcn_sdot4(xp[j * 2 + 0], we[j], a, false);
-    a = __builtin_amdgcn_sdot4(xp[j * 2 + 1], wo[j], a, false);
-  }
-  a *= 256;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    a = __builtin_amdgcn_sdot4(xp[8 + j * 2 + 0], we[j], a, false);
-    a = __builtin_amdgcn_sdot4(xp[8 + j * 2 + 1], wo[j], a, false);
-  }
-  if (P == 2) return static_cast<float>(a);
-  int b = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    b = __builtin_amdgcn_sdot4(xp[16 + j * 2 + 0], we[j], b, false);
-    b = __builtin_amdgcn_sdot4(xp[16 + j * 2 + 1], wo[j], b, false);
-  }
-  return fmaf(static_cast<float>(a), 256.0f, static_cast<float>(b));
-}
-
-__device__ __forceinline__ void expand_codes(const u32x4 w, int32_t we[4], int32_t wo[4]) {
-  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // byte b of we: 16*(nibble 2b - 8); byte b of wo: 16*(nibble 2b+1 - 8)
-    we[j] = static_cast<int32_t>(((v[j] << 4) & 0xf0f0f0f0u) ^ 0x80808080u);
-    wo[j] = static_cast<int32_t>((v[j] & 0xf0f0f0f0u) ^ 0x80808080u);
+  for (int j = 0; j < SUB; ++j) {
+    w[j] = __builtin_nontemporal_load(wq + static_cast<size_t>(g) * gstride + cstride * j);
+    s[j] = __builtin_nontemporal_load(ws + static_cast<size_t>(g) * gstride + cstride * j);
   }
 }
 
-constexpr int kUnroll = 4;
-
-template <int P, int NR>
-__device__ __forceinline__ void gemv_rows(const u32x4* __restrict__ wq, const float* __restrict__ ws,
-                                          size_t gstride, const int32_t* __restrict__ xq,
-                                          const float* __restrict__ xf, size_t R, int g_lo,
-                                          int g_hi, float acc[NR]) {
+// One wave: groups [g_lo, g_hi) of its columns, NR rows from position pos0.
+template <int D, int NR, int SUB, int IN>
+__device__ __forceinline__ void wave_gemv(const GemvArgs& a, const u32x4* wq, const float* ws,
+                                          int cstride, int pos0, int g_lo, int g_hi,
+                                          WaveWindow<D>& win, int lane, float acc[SUB][NR]) {
 #pragma unroll
-  for (int r = 0; r < NR; ++r) acc[r] = 0.0f;
-  int g = g_lo;
-  for (; g + kUnroll <= g_hi; g += kUnroll) {
-    u32x4 w[kUnroll];
-    float s[kUnroll];
+  for (int j = 0; j < SUB; ++j)
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      w[u] = __builtin_nontemporal_load(wq + static_cast<size_t>(g + u) * gstride);
-      s[u] = __builtin_nontemporal_load(ws + static_cast<size_t>(g + u) * gstride);
-    }
+    for (int r = 0; r < NR; ++r) acc[j][r] = 0.0f;
+  const size_t gstride = static_cast<size_t>(a.N);
+  for (int gw = g_lo; gw < g_hi; gw += kWin) {
+    const int nw = min(kWin, g_hi - gw);
+    u32x4 wc[SUB];
+    float sc[SUB];
+    load_group<SUB>(wq, ws, gstride, cstride, gw, wc, sc);
+    stage_window<D, IN>(a, win, gw, nw, pos0, NR, lane);
+    __builtin_amdgcn_wave_barrier();
+    for (int gi = 0; gi < nw; ++gi) {
+      u32x4 wn[SUB];
+      float sn[SUB];
+      load_group<SUB>(wq, ws, gstride, cstride, gw + min(gi + 1, nw - 1), wn, sn);
+      int32_t q[SUB][4];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      int32_t we[4], wo[4];
-      expand_codes(w[u], we, wo);
-      const int32_t* xg = xq + static_cast<size_t>(g + u) * R * (8 * P);
-      const float* fg = xf + static_cast<size_t>(g + u) * R;
+      for (int j = 0; j < SUB; ++j) {
+        q[j][0] = static_cast<int32_t>(wc[j].x ^ 0x88888888u);
+        q[j][1] = static_cast<int32_t>(wc[j].y ^ 0x88888888u);
+        q[j][2] = static_cast<int32_t>(wc[j].z ^ 0x88888888u);
+        q[j][3] = static_cast<int32_t>(wc[j].w ^ 0x88888888u);
+      }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const float F = group_dot<P>(xg + r * (8 * P), we, wo);
-        acc[r] = fmaf(s[u] * fg[r], F, acc[r]);
+        const int32_t* dp = win.dig[gi][r];
+        int32_t dg[4 * D];
+#pragma unroll
+        for (int i = 0; i < 4 * D; ++i) dg[i] = dp[i];
+        const float f = win.fac[gi][r];
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+          int t = 0;
+#pragma unroll
+          for (int d = 0; d < D; ++d) {
+            t *= 16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_sdot8(dg[d * 4 + i], q[j][i], t, false);
+          }
+          acc[j][r] = fmaf(sc[j] * f, static_cast<float>(t), acc[j][r]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) {
+        wc[j] = wn[j];
+        sc[j] = sn[j];
       }
     }
-  }
-  for (; g < g_hi; ++g) {
-    const u32x4 w = __builtin_nontemporal_load(wq + static_cast<size_t>(g) * gstride);
-    const float s = __builtin_nontemporal_load(ws + static_cast<size_t>(g) * gstride);
-    int32_t we[4], wo[4];
-    expand_codes(w, we, wo);
-    const int32_t* xg = xq + static_cast<size_t>(g) * R * (8 * P);
-    const float* fg = xf + static_cast<size_t>(g) * R;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const float F = group_dot<P>(xg + r * (8 * P), we, wo);
-      acc[r] = fmaf(s * fg[r], F, acc[r]);
-    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
-template <int P, int NR>
+template <int D, int NR, int SUB, int IN>
 __device__ __forceinline__ void run_rows(const GemvArgs& a, const u32x4* wq, const float* ws,
-                                         int pos0, int g_lo, int g_hi,
-                                         float red[][kMaxGemvRows][64], int wv, int lane) {
-  float acc[NR];
-  gemv_rows<P, NR>(wq, ws, a.N, a.xq + static_cast<size_t>(pos0) * (8 * P), a.xf + pos0,
-                   static_cast<size_t>(a.R), g_lo, g_hi, acc);
+                                         int cstride, int pos0, int g_lo, int g_hi,
+                                         GemvLds<D, SUB>& lds, int wv, int lane) {
+  float acc[SUB][NR];
+  wave_gemv<D, NR, SUB, IN>(a, wq, ws, cstride, pos0, g_lo, g_hi, lds.win[wv], lane, acc);
+  __syncthreads();  // every wave is done with its window before the buffer is reused
 #pragma unroll
-  for (int r = 0; r < NR; ++r) red[wv][r][lane] = acc[r];
+  for (int j = 0; j < SUB; ++j)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) lds.red[wv][r][64 * j + lane] = acc[j][r];
 }
 
-template <int P>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvArgs a) {
-  __shared__ float red[kGemvThreads / kWave][kMaxGemvRows][64];
-  __shared__ int sh_last;
+template <int D, int SUB, int IN>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(W4_GEMV_WAVES_PER_EU)))
+void gemv_kernel(const GemvArgs a) {
+  __shared__ GemvLds<D, SUB> lds;
+  __shared__ int last;
+  constexpr int TW = 64 * SUB;  // values per row of one tile
 
   const int task = blockIdx.x;
   const int split = task % a.S;
@@ -213,16 +222,20 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvArgs a) {
 
   const int wv = wave_id();
   const int lane = lane_id();
-  int mat = 0, col;
+  // plain tiles: 64*SUB consecutive columns, sub-column j at +64j; SwiGLU tiles:
+  // 32*SUB gate columns (lanes 0..31) and the same up columns (lanes 32..63),
+  // sub-column j at +32j
+  int mat = 0, col0;
   if (a.mode == 1) {
     mat = lane >> 5;
-    col = tile * 32 + (lane & 31);
+    col0 = tile * 32 * SUB + (lane & 31);
   } else {
-    col = tile * 64 + lane;
+    col0 = tile * TW + lane;
   }
+  const int cstride = a.mode == 1 ? 32 : 64;
   const size_t ebase = static_cast<size_t>(expert) * a.expert_stride;
-  const u32x4* wq = (mat ? a.qw1 : a.qw0) + ebase + col;
-  const float* ws = (mat ? a.sc1 : a.sc0) + ebase + col;
+  const u32x4* wq = (mat ? a.qw1 : a.qw0) + ebase + col0;
+  const float* wsc = (mat ? a.sc1 : a.sc0) + ebase + col0;
 
   const int sg_lo = split * a.gps;
   const int sg_hi = min(a.G, sg_lo + a.gps);
@@ -232,78 +245,108 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvArgs a) {
   const int g_hi = min(sg_hi, g_lo + span);
 
   switch (nrows) {
-    case 1: run_rows<P, 1>(a, wq, ws, pos0, g_lo, g_hi, red, wv, lane); break;
-    case 2: run_rows<P, 2>(a, wq, ws, pos0, g_lo, g_hi, red, wv, lane); break;
-    case 3: run_rows<P, 3>(a, wq, ws, pos0, g_lo, g_hi, red, wv, lane); break;
-    case 4: run_rows<P, 4>(a, wq, ws, pos0, g_lo, g_hi, red, wv, lane); break;
-    case 5: run_rows<P, 5>(a, wq, ws, pos0, g_lo, g_hi, red, wv, lane); break;
-    case 6: run_rows<P, 6>(a, wq, ws, pos0, g_lo, g_hi, red, wv, lane); break;
-    case 7: run_rows<P, 7>(a, wq, ws, pos0, g_lo, g_hi, red, wv, lane); break;
-    default: run_rows<P, 8>(a, wq, ws, pos0, g_lo, g_hi, red, wv, lane); break;
+#define W4_CASE(n) \
+  case n: run_rows<D, n, SUB, IN>(a, wq, wsc, cstride, pos0, g_lo, g_hi, lds, wv, lane); break;
+    W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
+    default: run_rows<D, 8, SUB, IN>(a, wq, wsc, cstride, pos0, g_lo, g_hi, lds, wv, lane); break;
+#undef W4_CASE
   }
   __syncthreads();
 
-  // fixed-order reduction over the four waves, then over the K splits
-  float v[kMaxGemvRows];
-  if (wv == 0) {
+  // Fixed-order reduction over the four waves, then over the K splits.  Thread
+  // t owns elements e = t + 256i of the tile [nrows][TW].
+  constexpr int kEl = kMaxGemvRows * TW / kGemvThreads;  // elements per thread (upper bound)
+  float* tilev = &lds.red[0][0][0];  // reduced tile, row stride TW
+  float v[kEl];
 #pragma unroll
-    for (int r = 0; r < kMaxGemvRows; ++r) {
-      if (r < nrows) v[r] = ((red[0][r][lane] + red[1][r][lane]) + red[2][r][lane]) + red[3][r][lane];
-    }
+  for (int i = 0; i < kEl; ++i) {
+    const int e = static_cast<int>(threadIdx.x) + kGemvThreads * i;
+    const int r = e / TW, cc = e % TW;
+    v[i] = r < nrows ? ((lds.red[0][r][cc] + lds.red[1][r][cc]) + lds.red[2][r][cc]) + lds.red[3][r][cc]
+                     : 0.0f;
   }
   if (a.S > 1) {
+    // Partials are written through to the device coherence point (agent-scope
+    // stores), the arrival counter is an agent-scope atomic, and the last
+    // workgroup of the tile reads every partial back with agent-scope loads,
+    // all issued before any is summed, and sums them in split order.
     const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
-    float* base = a.partials + ct * a.S * kPartialTileFloats;
-    if (wv == 0) {
-      for (int r = 0; r < nrows; ++r) base[split * kPartialTileFloats + r * 64 + lane] = v[r];
+    const size_t tf = static_cast<size_t>(kMaxGemvRows) * TW;
+    float* base = a.partials + ct * a.S * tf;
+#pragma unroll
+    for (int i = 0; i < kEl; ++i) {
+      const int e = static_cast<int>(threadIdx.x) + kGemvThreads * i;
+      if (e / TW < nrows)
+        __hip_atomic_store(base + split * tf + e, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int prev = atomicAdd(&a.counters[ct], 1);
-      sh_last = (prev == a.S - 1);
+      const int prev = __hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      last = (prev == a.S - 1);
     }
     __syncthreads();
-    if (!sh_last) return;
-    __threadfence();
-    if (wv == 0) {
-      for (int r = 0; r < nrows; ++r) {
-        float t = 0.0f;
-        for (int s = 0; s < a.S; ++s) t += base[s * kPartialTileFloats + r * 64 + lane];
-        v[r] = t;
-      }
+    if (!last) return;
+#pragma unroll
+    for (int i = 0; i < kEl; ++i) {
+      const int e = static_cast<int>(threadIdx.x) + kGemvThreads * i;
+      if (e / TW >= nrows) continue;
+      float part[kMaxSplits];
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplits; ++s2)
+        part[s2] = s2 < a.S ? __hip_atomic_load(base + s2 * tf + e, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                            : 0.0f;
+      float t = 0.0f;
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxSplits; ++s2)
+        if (s2 < a.S) t += part[s2];
+      v[i] = t;
     }
-    if (threadIdx.x == 0) a.counters[ct] = 0;
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (wv != 0) return;
-
-  if (a.mode == 0) {
-    for (int r = 0; r < nrows; ++r)
-      a.out[static_cast<size_t>(pos0 + r) * a.N + col] = v[r];
-    return;
-  }
-
-  // SwiGLU epilogue: lanes 0..31 hold gate, 32..63 up, for columns tile*32 + c.
-  // The 32 columns are one scale group of the down projection's input, so the
-  // pieces of h are formed here directly.
-  const int c = lane & 31;
-  for (int r = 0; r < nrows; ++r) {
-    const float up = __shfl_down(v[r], 32);
-    const float h = silu(v[r]) * up;
-    float amax = lane < 32 ? fabsf(h) : 0.0f;
+  __syncthreads();  // all reads of the per-wave buffers are done
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    const size_t prow = static_cast<size_t>(pos0 + r);
-    if (lane < 32) {
-      const int sh = piece_shift<P>(amax);
-      int pc[P];
-      split_pieces<P>(h, sh, pc);
-      uint8_t* blk = reinterpret_cast<uint8_t*>(a.hq + (static_cast<size_t>(tile) * a.R + prow) * (8 * P));
+  for (int i = 0; i < kEl; ++i) tilev[threadIdx.x + kGemvThreads * i] = v[i];
+  __syncthreads();
+
+  // Epilogue: wave w takes sub-columns j = w, w + 4, ...
+  for (int j = wv; j < SUB; j += kGemvThreads / kWave) {
+    if (a.mode == 0) {
+      for (int r = 0; r < nrows; ++r)
+        a.out[static_cast<size_t>(pos0 + r) * a.N + col0 + 64 * j] = tilev[r * TW + 64 * j + lane];
+      continue;
+    }
+    // SwiGLU: lanes 0..31 hold gate and 32..63 up of h columns (tile*SUB + j)*32 + c.
+    // Those 32 columns are one scale group of the down projection's input, so
+    // its digits are formed here directly.
+    const int c = lane & 31;
+    const int hg = tile * SUB + j;  // h group index
+    for (int r = 0; r < nrows; ++r) {
+      const float gv = tilev[r * TW + 64 * j + c];
+      const float uv = tilev[r * TW + 64 * j + 32 + c];
+      const float h = silu(gv) * uv;
+      float amax = fabsf(h);
 #pragma unroll
-      for (int p = 0; p < P; ++p) blk[piece_byte(p, c)] = static_cast<uint8_t>(pc[p] & 0xff);
-      if (c == 0) a.hf[static_cast<size_t>(tile) * a.R + prow] = amax > 0.0f ? ldexpf(1.0f, -sh - 4) : 0.0f;
-      if (a.h_raw != nullptr) {
-        const size_t hi = prow * a.N + tile * 32 + c;
+      for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const int sh = digit_shift<D>(amax);
+      const uint32_t xb = biased_fixed<D>(h, ldexpf(1.0f, sh));
+      const size_t prow = static_cast<size_t>(pos0 + r);
+      int32_t* blk = a.hq + (static_cast<size_t>(hg) * a.R + prow) * (4 * D);
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        // gather the nibbles of lanes 8j'..8j'+7 into dword (d, j')
+        uint32_t nib = digit_nibble<D>(xb, d) << (4 * (c & 7));
+        nib |= __shfl_xor(nib, 1);
+        nib |= __shfl_xor(nib, 2);
+        nib |= __shfl_xor(nib, 4);
+        if (lane < 32 && (c & 7) == 0) blk[d * 4 + (c >> 3)] = static_cast<int32_t>(nib);
+      }
+      if (lane == 0) a.hf[static_cast<size_t>(hg) * a.R + prow] = amax > 0.0f ? ldexpf(1.0f, -sh) : 0.0f;
+      if (a.h_raw != nullptr && lane < 32) {
+        const size_t hi = prow * a.N + static_cast<size_t>(hg) * 32 + c;
         if (a.h_bf16)
           static_cast<uint16_t*>(a.h_raw)[hi] = f32_to_bf16(h);
         else
@@ -315,45 +358,57 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvArgs a) {
 
 }  // namespace
 
-int gemv_splits(size_t tasks, int G) {
-  // aim for about 1024 workgroups (4 per CU) while keeping >= 8 groups per wave
-  const size_t target = 1024;
-  int S = static_cast<int>((target + tasks - 1) / tasks);
-  const int max_s = G / (8 * (kGemvThreads / kWave));
-  if (S > max_s) S = max_s;
-  if (S < 1) S = 1;
-  return S;
+GemvShape gemv_shape(size_t items, int N, int mode, int G, size_t max_split_tasks) {
+  const int per_sub = mode == 1 ? 32 : 64;
+  const double cap = W4_GEMV_TARGET_WGS;
+  GemvShape best;
+  double best_fill = -1.0;
+  for (int sub = W4_GEMV_SUB; sub >= 1; sub >>= 1) {
+    if (N % (per_sub * sub) != 0) continue;
+    GemvShape sh;
+    sh.sub = sub;
+    sh.tiles = N / (per_sub * sub);
+    const size_t tasks = items * static_cast<size_t>(sh.tiles);
+    int max_s = G / (W4_GEMV_MIN_GROUPS_PER_WAVE * (kGemvThreads / kWave));
+    if (max_s > kMaxSplits) max_s = kMaxSplits;
+    if (tasks > max_split_tasks) max_s = 1;
+    int S = static_cast<int>(cap / static_cast<double>(tasks));
+    if (S > max_s) S = max_s;
+    if (S < 1) S = 1;
+    sh.S = S;
+    const double wgs = static_cast<double>(tasks) * S;
+    const double rounds = wgs <= cap ? 1.0 : static_cast<double>(static_cast<size_t>((wgs + cap - 1) / cap));
+    // many rounds (grouped calls size the grid for the worst case) balance by themselves
+    const double fill = rounds >= 4.0 ? 1.0 : wgs / (rounds * cap);
+    if (fill > best_fill * 1.05) {  // a smaller sub must fill clearly better
+      best = sh;
+      best_fill = fill;
+    }
+  }
+  return best;
 }
 
-w4a16_status_t launch_prep_pieces(const void* x, w4a16_dtype_t xt, int R, int K, int P,
-                                  const int* sorted_pairs, int top_k, int32_t* xq, float* xf,
-                                  hipStream_t stream) {
-  const size_t total = static_cast<size_t>(R) * (K / kGroup);
-  if (total == 0) return W4A16_OK;
-  const unsigned grid = static_cast<unsigned>((total + 127) / 128);
-  if (xt == W4A16_F32 && P == 3)
-    prep_pieces_kernel<float, 3><<<grid, 128, 0, stream>>>(static_cast<const float*>(x), R, K,
-                                                           sorted_pairs, top_k, xq, xf);
-  else if (xt == W4A16_BF16 && P == 2)
-    prep_pieces_kernel<uint16_t, 2><<<grid, 128, 0, stream>>>(static_cast<const uint16_t*>(x), R, K,
-                                                              sorted_pairs, top_k, xq, xf);
-  else if (xt == W4A16_F32 && P == 2)
-    prep_pieces_kernel<float, 2><<<grid, 128, 0, stream>>>(static_cast<const float*>(x), R, K,
-                                                           sorted_pairs, top_k, xq, xf);
-  else
-    prep_pieces_kernel<uint16_t, 3><<<grid, 128, 0, stream>>>(static_cast<const uint16_t*>(x), R, K,
-                                                              sorted_pairs, top_k, xq, xf);
-  return launch_status();
-}
-
-w4a16_status_t launch_gemv(const GemvArgs& a, int P, size_t num_tasks, hipStream_t stream) {
+w4a16_status_t launch_gemv(const GemvArgs& a, int D, int SUB, int input, size_t num_tasks,
+                           hipStream_t stream) {
   if (num_tasks == 0) return W4A16_OK;
   if (num_tasks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   const unsigned grid = static_cast<unsigned>(num_tasks);
-  if (P == 3)
-    gemv_kernel<3><<<grid, kGemvThreads, 0, stream>>>(a);
-  else
-    gemv_kernel<2><<<grid, kGemvThreads, 0, stream>>>(a);
+#define W4_GO(d, sub, in) gemv_kernel<d, sub, in><<<grid, kGemvThreads, 0, stream>>>(a)
+#define W4_SUBS(d, in)                 \
+  if (SUB == 4) W4_GO(d, 4, in);       \
+  else if (SUB == 2) W4_GO(d, 2, in);  \
+  else W4_GO(d, 1, in);
+  if (D == 5) {
+    if (input == kInF32) { W4_SUBS(5, kInF32) }
+    else if (input == kInBF16) { W4_SUBS(5, kInBF16) }
+    else { W4_SUBS(5, kInDigits) }
+  } else {
+    if (input == kInF32) { W4_SUBS(4, kInF32) }
+    else if (input == kInBF16) { W4_SUBS(4, kInBF16) }
+    else { W4_SUBS(4, kInDigits) }
+  }
+#undef W4_SUBS
+#undef W4_GO
   return launch_status();
 }
 

@@ -1,0 +1,55 @@
+// MFMA tile GEMM for row counts above the GEMV range (internal interface).
+#pragma once
+
+#include "common.h"
+
+namespace w4 {
+
+// Activations enter the MFMA kernel as f16 "pieces" of a per-row power-of-two
+// rescaling: v = x * 2^e with max|x_row| * 2^e in [2^14, 2^15), piece 0 =
+// f16(v), piece 1 = f16(v - piece 0) (float32 activations only).  Two pieces
+// carry 22 significant bits; bf16 activations fit in one.  Within every block
+// of 8 consecutive k the pieces are stored in the order k = 0,4,1,5,2,6,3,7,
+// the order in which one packed code word expands into f16 pairs.
+// Layout: ap[p][Mp][K] f16, rs[Mp] = 2^-e (0 for an all-zero or absent row).
+inline int mfma_pieces(w4a16_dtype_t xt) { return xt == W4A16_F32 ? 2 : 1; }
+
+constexpr int kMfmaRows = 64;     // rows per tile
+constexpr int kMfmaCols = 256;    // weight columns per tile (4 waves x 4 blocks of 16)
+constexpr int kMfmaThreads = 256;
+
+struct MfmaArgs {
+  const _Float16* ap;  // [P][Mp][K]
+  const float* rs;     // [Mp]
+  int Mp;              // rows per piece plane (a multiple of 64, >= positions + 64)
+  int K, G;
+  const u32x4* qw0;    // GROUPED chunks, matrix 0 (plain, or gate)
+  const float* sc0;
+  const u32x4* qw1;    // up (SwiGLU mode)
+  const float* sc1;
+  size_t expert_stride;  // chunks (and scales) per expert
+  int N;                 // columns per matrix
+  int tiles;             // column tiles per row item
+  int S, gps;            // K splits, groups per split
+  int dense_rows;        // > 0: dense rows, items of 64 rows
+  const int4* items;     // grouped mode: {expert, first position, rows, 0}
+  const int* n_items;
+  int mode;              // 0: plain float32 out[pos][N]; 1: SwiGLU, h[pos][N]
+  float* out;
+  void* h;
+  int h_bf16;
+  float* partials;
+  int* counters;
+};
+
+// Pieces of R positions (rows of x, or gathered rows sorted_pairs[p] / top_k);
+// rows R .. Mp-1 are zero-filled.
+w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, int K, int P,
+                                const int* gather, int top_k, _Float16* ap, float* rs,
+                                hipStream_t stream);
+w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream_t stream);
+
+// Rows of the piece planes for R positions.
+inline int mfma_rows_padded(int R) { return (R + kMfmaRows - 1) / kMfmaRows * kMfmaRows + kMfmaRows; }
+
+}  // namespace w4

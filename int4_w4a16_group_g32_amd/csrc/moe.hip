@@ -153,16 +153,16 @@ w4a16_status_t launch_route(const int32_t* ids, int M, int top_k, int E, int32_t
 }
 
 struct MoePlan {
-  int P = 0;
+  int D = 0;
   size_t pairs = 0, max_items = 0;
   size_t counts_off, offsets_off, sorted_off, inv_off, items_off, nitems_off;
-  size_t xq_off, xf_off, hq_off, hf_off, o_off;
+  size_t hq_off, hf_off, o_off;
   size_t bytes = 0;
 };
 
 MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate) {
   MoePlan p;
-  p.P = pieces_for(xt);
+  p.D = digits_for(xt);
   const int E = gate->num_experts, H = gate->K, I = gate->N;
   p.pairs = static_cast<size_t>(M) * top_k;
   p.max_items = p.pairs / kMaxGemvRows + std::min<size_t>(E, p.pairs) + 1;
@@ -175,9 +175,7 @@ MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate)
   c.take(p.inv_off, p.pairs * 4);
   c.take(p.items_off, p.max_items * 16);
   c.take(p.nitems_off, 16);
-  c.take(p.xq_off, p.pairs * (H / kGroup) * 8 * p.P * 4);
-  c.take(p.xf_off, p.pairs * (H / kGroup) * 4);
-  c.take(p.hq_off, p.pairs * (I / kGroup) * 8 * p.P * 4);
+  c.take(p.hq_off, p.pairs * (I / kGroup) * 4 * p.D * 4);
   c.take(p.hf_off, p.pairs * (I / kGroup) * 4);
   c.take(p.o_off, p.pairs * H * 4);
   p.bytes = c.cursor;
@@ -257,8 +255,6 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   int32_t* inv = reinterpret_cast<int32_t*>(b + p.inv_off);
   int4* items = reinterpret_cast<int4*>(b + p.items_off);
   int32_t* n_items = reinterpret_cast<int32_t*>(b + p.nitems_off);
-  int32_t* xq = reinterpret_cast<int32_t*>(b + p.xq_off);
-  float* xf = reinterpret_cast<float*>(b + p.xf_off);
   int32_t* hq = reinterpret_cast<int32_t*>(b + p.hq_off);
   float* hf = reinterpret_cast<float*>(b + p.hf_off);
   float* o = reinterpret_cast<float*>(b + p.o_off);
@@ -267,13 +263,12 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   st = launch_route(topk_ids, M, top_k, E, counts, offsets, sorted, inv, items, n_items,
                     kMaxGemvRows, stream);
   if (st != W4A16_OK) return st;
-  st = launch_prep_pieces(x, xt, R, H, p.P, sorted, top_k, xq, xf, stream);
-  if (st != W4A16_OK) return st;
-
   GemvArgs a{};
-  a.xq = xq;
-  a.xf = xf;
+  a.x = x;
+  a.gather = sorted;
+  a.top_k = top_k;
   a.G = H / kGroup;
+  a.K = H;
   a.R = R;
   a.qw0 = reinterpret_cast<const u32x4*>(gate->qw);
   a.sc0 = gate->scales;
@@ -281,7 +276,10 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   a.sc1 = up->scales;
   a.expert_stride = static_cast<size_t>(H / kGroup) * I;
   a.N = I;
-  a.tiles = I / 32;
+  // grouped GEMVs run one workgroup per (item, tile) over the whole K range
+  const GemvShape gu = gemv_shape(p.max_items, I, 1, H / kGroup, 0);
+  const int sub_gu = gu.sub;
+  a.tiles = gu.tiles;
   a.S = 1;
   a.gps = a.G;
   a.dense_rows = 0;
@@ -290,19 +288,23 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   a.mode = 1;
   a.hq = hq;
   a.hf = hf;
-  st = launch_gemv(a, p.P, p.max_items * a.tiles, stream);
+  st = launch_gemv(a, p.D, sub_gu, xt == W4A16_F32 ? kInF32 : kInBF16, p.max_items * a.tiles,
+                   stream);
   if (st != W4A16_OK) return st;
 
   GemvArgs d{};
   d.xq = hq;
   d.xf = hf;
   d.G = I / kGroup;
+  d.K = I;
   d.R = R;
   d.qw0 = reinterpret_cast<const u32x4*>(down->qw);
   d.sc0 = down->scales;
   d.expert_stride = static_cast<size_t>(I / kGroup) * H;
   d.N = H;
-  d.tiles = H / 64;
+  const GemvShape dn = gemv_shape(p.max_items, H, 0, I / kGroup, 0);
+  const int sub_d = dn.sub;
+  d.tiles = dn.tiles;
   d.S = 1;
   d.gps = d.G;
   d.dense_rows = 0;
@@ -310,7 +312,7 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   d.n_items = n_items;
   d.mode = 0;
   d.out = o;
-  st = launch_gemv(d, p.P, p.max_items * d.tiles, stream);
+  st = launch_gemv(d, p.D, sub_d, kInDigits, p.max_items * d.tiles, stream);
   if (st != W4A16_OK) return st;
 
   const size_t total = static_cast<size_t>(M) * H;

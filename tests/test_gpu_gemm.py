@@ -34,7 +34,7 @@ SHAPES = [(32, 64), (64, 128), (192, 64), (256, 512), (1024, 192), (7168, 256)]
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("K,N", SHAPES)
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 17])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 17, 64, 65, 130])
 def test_gemm_small_shapes(M, K, N, dtype):
     qw, sc, w = _make(K, N, 200 + K + N)
     x = x_for_dtype(W.activations(M, K, 200 + M).cuda(), dtype)
@@ -45,10 +45,10 @@ def test_gemm_small_shapes(M, K, N, dtype):
     assert err <= tol_for(dtype)
 
 
-@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 64])
 def test_gemm_one_hot_rows_are_dequant_bit_exact(M):
-    """x = unit rows e_k: y row = float32(q[k][:] * s) exactly, for both the
-    in-kernel dequantization and the K-split reduction."""
+    """x = unit rows e_k: y row = float32(q[k][:] * s) exactly, on the GEMV
+    path (M <= 8) and the MFMA path (M > 8), through the K-split reduction."""
     K, N = 2048, 512
     qw, sc, w = _make(K, N, 301)
     ks = np.random.default_rng(M).choice(K, size=M, replace=False)
@@ -62,16 +62,16 @@ def test_gemm_one_hot_rows_are_dequant_bit_exact(M):
 def test_gemm_deterministic_and_workspace_reuse():
     K, N = 7168, 1024
     qw, sc, w = _make(K, N, 302)
-    ws = L.new_workspace(max(L.gemm_workspace_bytes(m, w, L.F32) for m in (1, 4, 8)))
+    ws = L.new_workspace(max(L.gemm_workspace_bytes(m, w, L.F32) for m in (1, 4, 8, 40)))
     outs = []
-    for M in (4, 1, 8, 4):
+    for M in (4, 1, 8, 40, 4):
         x = W.activations(M, K, 302).cuda()
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         L.gemm(x, w, y, ws)
         torch.cuda.synchronize()
         assert rel_err(y, O.gemm64(x_values(x), qw, sc)) <= 1e-5
         outs.append(y.cpu().numpy())
-    assert np.array_equal(outs[0].view(np.uint32), outs[3].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[4].view(np.uint32))
 
 
 def test_gemm_zero_rows_and_m0():
