@@ -213,6 +213,8 @@ W4A16_API size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype
  * and topk_w [M][top_k] (int32 / float32), y [M][H] float32.  The routing lists
  * (as w4a16_moe_route), the per-pair intermediate and the per-pair outputs
  * live in the workspace; per-expert row counts never leave the device.
+ * Experts with at most 8 rows run on the GEMV kernels, heavier experts on MFMA
+ * tiles of 64 rows.
  * Errors as w4a16_swiglu_mlp plus INVALID_ARG for top_k < 1 or top_k > E.
  */
 W4A16_API w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int32_t M,
@@ -220,6 +222,19 @@ W4A16_API w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int3
                                  const w4a16_weight_t* gate, const w4a16_weight_t* up,
                                  const w4a16_weight_t* down, float* y, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
+
+/*
+ * Measurement variant of w4a16_moe_grouped, with the event convention of
+ * w4a16_swiglu_mlp_timed.  Kernels in launch order: expert grouping; gate/up
+ * GEMV for experts with at most 8 rows; when M > 8, activation pieces and
+ * gate/up MFMA tiles for heavier experts; down GEMV; when M > 8, pieces of the
+ * intermediate and down MFMA tiles; weighted combine.
+ */
+W4A16_API w4a16_status_t w4a16_moe_grouped_timed(
+    const void* x, w4a16_dtype_t xt, int32_t M, const int32_t* topk_ids, const float* topk_w,
+    int32_t top_k, const w4a16_weight_t* gate, const w4a16_weight_t* up,
+    const w4a16_weight_t* down, float* y, void* ws, size_t ws_bytes, hipStream_t stream,
+    hipEvent_t* events, int32_t capacity, int32_t* recorded);
 
 #ifdef __cplusplus
 }

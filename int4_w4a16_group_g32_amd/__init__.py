@@ -36,6 +36,7 @@ EXPORTS = (
     "w4a16_moe_route",
     "w4a16_moe_workspace_bytes",
     "w4a16_moe_grouped",
+    "w4a16_moe_grouped_timed",
 )
 
 
@@ -84,6 +85,8 @@ def load_library() -> ctypes.CDLL:
             "w4a16_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
             "w4a16_moe_workspace_bytes": (sz, [i32, i32, i32, dp, dp, dp]),
             "w4a16_moe_grouped": (i32, [vp, i32, i32, vp, vp, i32, dp, dp, dp, vp, vp, sz, vp]),
+            "w4a16_moe_grouped_timed": (i32, [vp, i32, i32, vp, vp, i32, dp, dp, dp, vp, vp, sz, vp, vp,
+                                              i32, ctypes.POINTER(i32)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)

@@ -216,7 +216,7 @@ extern "C" w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M,
   if (p.mfma) {
     _Float16* ap = reinterpret_cast<_Float16*>(wsb + p.ap_off);
     float* rs = reinterpret_cast<float*>(wsb + p.rs_off);
-    st = launch_mfma_prep(x, xt, M, p.mf.Mp, w->K, p.mf.P, nullptr, 0, ap, rs, stream);
+    st = launch_mfma_prep(x, xt, M, p.mf.Mp, w->K, p.mf.P, nullptr, 0, nullptr, ap, rs, stream);
     if (st != W4A16_OK) return st;
     MfmaArgs a = mfma_dense_args(p.mf, M, w, nullptr, 0, ap, rs, wsb, p.partials_off, p.counters_off);
     a.out = y;
@@ -276,7 +276,7 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
     _Float16* aph = reinterpret_cast<_Float16*>(wsb + p.aph_off);
     float* rsh = reinterpret_cast<float*>(wsb + p.rsh_off);
     if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma_prep(x, xt, M, p.gu.Mp, H, p.gu.P, nullptr, 0, apx, rsx, stream);
+    st = launch_mfma_prep(x, xt, M, p.gu.Mp, H, p.gu.P, nullptr, 0, nullptr, apx, rsx, stream);
     if (st != W4A16_OK) return st;
     MfmaArgs a = mfma_dense_args(p.gu, M, gate, up, 1, apx, rsx, wsb, p.partials_off, p.counters_off);
     a.h = h;
@@ -285,7 +285,7 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
     st = launch_mfma(a, p.gu.P, p.gu.tasks * p.gu.S, stream);
     if (st != W4A16_OK) return st;
     if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma_prep(h, W4A16_F32, M, p.dn.Mp, I, p.dn.P, nullptr, 0, aph, rsh, stream);
+    st = launch_mfma_prep(h, W4A16_F32, M, p.dn.Mp, I, p.dn.P, nullptr, 0, nullptr, aph, rsh, stream);
     if (st != W4A16_OK) return st;
     MfmaArgs d = mfma_dense_args(p.dn, M, down, nullptr, 0, aph, rsh, wsb, p.partials_off,
                                  p.counters_off);

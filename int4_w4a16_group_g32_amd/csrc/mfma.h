@@ -42,11 +42,12 @@ struct MfmaArgs {
   int* counters;
 };
 
-// Pieces of R positions (rows of x, or gathered rows sorted_pairs[p] / top_k);
-// rows R .. Mp-1 are zero-filled.
+// Pieces of R positions (rows of x, or gathered rows gather[p] / top_k); rows
+// R .. Mp-1 are zero-filled.  With `need` set, only positions p < R with
+// need[p] != 0 are written (the others are never read).
 w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, int K, int P,
-                                const int* gather, int top_k, _Float16* ap, float* rs,
-                                hipStream_t stream);
+                                const int* gather, int top_k, const int* need, _Float16* ap,
+                                float* rs, hipStream_t stream);
 w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream_t stream);
 
 // Rows of the piece planes for R positions.

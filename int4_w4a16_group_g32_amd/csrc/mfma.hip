@@ -31,10 +31,12 @@ constexpr int kRowPad = 40;  // halves per staged row of 32 (80-byte stride)
 template <typename XT, int P>
 __global__ __launch_bounds__(256) void mfma_prep_kernel(const XT* __restrict__ x, int R, int Mp,
                                                         int K, const int* __restrict__ gather,
-                                                        int top_k, _Float16* __restrict__ ap,
+                                                        int top_k, const int* __restrict__ need,
+                                                        _Float16* __restrict__ ap,
                                                         float* __restrict__ rs) {
   __shared__ float red[256];
   const int row = blockIdx.x;
+  if (need != nullptr && (row >= R || need[row] == 0)) return;
   long src = row < R ? row : -1;
   if (src >= 0 && gather != nullptr) {
     const int pr = gather[row];
@@ -291,21 +293,21 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(const MfmaArgs a) {
 }  // namespace
 
 w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, int K, int P,
-                                const int* gather, int top_k, _Float16* ap, float* rs,
-                                hipStream_t stream) {
+                                const int* gather, int top_k, const int* need, _Float16* ap,
+                                float* rs, hipStream_t stream) {
   if (Mp == 0) return W4A16_OK;
   if (xt == W4A16_F32 && P == 2)
     mfma_prep_kernel<float, 2><<<Mp, 256, 0, stream>>>(static_cast<const float*>(x), R, Mp, K, gather,
-                                                       top_k, ap, rs);
+                                                       top_k, need, ap, rs);
   else if (xt == W4A16_F32)
     mfma_prep_kernel<float, 1><<<Mp, 256, 0, stream>>>(static_cast<const float*>(x), R, Mp, K, gather,
-                                                       top_k, ap, rs);
+                                                       top_k, need, ap, rs);
   else if (P == 2)
     mfma_prep_kernel<uint16_t, 2><<<Mp, 256, 0, stream>>>(static_cast<const uint16_t*>(x), R, Mp, K,
-                                                          gather, top_k, ap, rs);
+                                                          gather, top_k, need, ap, rs);
   else
     mfma_prep_kernel<uint16_t, 1><<<Mp, 256, 0, stream>>>(static_cast<const uint16_t*>(x), R, Mp, K,
-                                                          gather, top_k, ap, rs);
+                                                          gather, top_k, need, ap, rs);
   return launch_status();
 }
 

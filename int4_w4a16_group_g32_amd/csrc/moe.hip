@@ -18,11 +18,14 @@ constexpr int kRouteLdsInts = 12288;  // 48 KiB of per-chunk histograms
 // workgroup.  Tokens are cut into C chunks; a per-(chunk, expert) histogram is
 // scanned along chunks per expert, then each chunk places its pairs in token
 // order.  Ids outside [0, E) are skipped (inv = -1).  Optionally also emits the
-// GEMV work items: each expert's list cut into blocks of at most `rows_per_item`.
+// work items of the grouped layer: an expert with at most kMaxGemvRows rows is
+// one GEMV item, a heavier one is cut into MFMA items of kMfmaRows rows, and
+// heavy[p] marks the positions that belong to MFMA items.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int32_t* __restrict__ ids, int M, int top_k, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv,
-    int4* __restrict__ items, int32_t* __restrict__ n_items, int rows_per_item) {
+    int4* __restrict__ items_g, int4* __restrict__ items_m, int32_t* __restrict__ n_items,
+    int32_t* __restrict__ heavy) {
   extern __shared__ int hist[];  // [C][E]
   __shared__ int carry;
   const int tid = threadIdx.x;
@@ -90,33 +93,48 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       }
     }
   }
-  if (items == nullptr) return;
+  if (items_g == nullptr) return;
   __syncthreads();
-  // 5. GEMV items: exclusive scan of ceil(count / rows_per_item) over experts
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < E; base += kRouteThreads) {
-    const int e = base + tid;
-    const int n = e < E ? (counts[e] + rows_per_item - 1) / rows_per_item : 0;
-    scan[tid] = n;
+  // 5. work items: exclusive scans over experts of the GEMV and MFMA item counts
+  for (int kind = 0; kind < 2; ++kind) {
+    if (tid == 0) carry = 0;
     __syncthreads();
-    for (int off = 1; off < kRouteThreads; off <<= 1) {
-      const int t = tid >= off ? scan[tid - off] : 0;
+    for (int base = 0; base < E; base += kRouteThreads) {
+      const int e = base + tid;
+      const int c0 = e < E ? counts[e] : 0;
+      int n = 0;
+      if (kind == 0) n = (c0 > 0 && c0 <= kMaxGemvRows) ? 1 : 0;
+      else n = c0 > kMaxGemvRows ? (c0 + kMfmaRows - 1) / kMfmaRows : 0;
+      scan[tid] = n;
       __syncthreads();
-      scan[tid] += t;
+      for (int off = 1; off < kRouteThreads; off <<= 1) {
+        const int t = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += t;
+        __syncthreads();
+      }
+      if (n > 0) {
+        int it = carry + scan[tid] - n;
+        const int o0 = offsets[e];
+        if (kind == 0) {
+          items_g[it] = make_int4(e, o0, c0, 0);
+        } else {
+          for (int r = 0; r < c0; r += kMfmaRows, ++it)
+            items_m[it] = make_int4(e, o0 + r, min(kMfmaRows, c0 - r), 0);
+        }
+      }
+      if (kind == 1 && e < E) {
+        const int o0 = offsets[e];
+        const int hv = c0 > kMaxGemvRows ? 1 : 0;
+        for (int r = 0; r < c0; ++r) heavy[o0 + r] = hv;
+      }
+      __syncthreads();
+      if (tid == kRouteThreads - 1) carry += scan[tid];
       __syncthreads();
     }
-    if (e < E) {
-      int it = carry + scan[tid] - n;
-      const int c0 = counts[e], o0 = offsets[e];
-      for (int r = 0; r < c0; r += rows_per_item, ++it)
-        items[it] = make_int4(e, o0 + r, min(rows_per_item, c0 - r), 0);
-    }
-    __syncthreads();
-    if (tid == kRouteThreads - 1) carry += scan[tid];
+    if (tid == 0) n_items[kind] = carry;
     __syncthreads();
   }
-  if (tid == 0) *n_items = carry;
 }
 
 // y[t][n] = sum over slots, in slot order, of w[t][s] * o[inv[t*top_k+s]][n].
@@ -143,29 +161,35 @@ size_t route_lds_bytes(int E) {
 }
 
 w4a16_status_t launch_route(const int32_t* ids, int M, int top_k, int E, int32_t* counts,
-                            int32_t* offsets, int32_t* sorted_pairs, int32_t* inv, int4* items,
-                            int32_t* n_items, int rows_per_item, hipStream_t stream) {
+                            int32_t* offsets, int32_t* sorted_pairs, int32_t* inv, int4* items_g,
+                            int4* items_m, int32_t* n_items, int32_t* heavy, hipStream_t stream) {
   if (E > kRouteLdsInts) return W4A16_ERR_UNSUPPORTED;
   const size_t lds = route_lds_bytes(E);
   route_kernel<<<1, kRouteThreads, lds, stream>>>(ids, M, top_k, E, counts, offsets, sorted_pairs,
-                                                   inv, items, n_items, rows_per_item);
+                                                   inv, items_g, items_m, n_items, heavy);
   return launch_status();
 }
 
 struct MoePlan {
-  int D = 0;
-  size_t pairs = 0, max_items = 0;
-  size_t counts_off, offsets_off, sorted_off, inv_off, items_off, nitems_off;
+  int D = 0, P = 0, Mp = 0;
+  size_t pairs = 0, max_items = 0, max_mitems = 0;
+  size_t counts_off, offsets_off, sorted_off, inv_off, items_off, mitems_off, nitems_off, heavy_off;
   size_t hq_off, hf_off, o_off;
+  size_t apx_off, rsx_off, h_off, aph_off, rsh_off;
+  bool mfma = false;  // some expert can have more than kMaxGemvRows rows
   size_t bytes = 0;
 };
 
 MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate) {
   MoePlan p;
   p.D = digits_for(xt);
+  p.P = mfma_pieces(xt);
   const int E = gate->num_experts, H = gate->K, I = gate->N;
   p.pairs = static_cast<size_t>(M) * top_k;
-  p.max_items = p.pairs / kMaxGemvRows + std::min<size_t>(E, p.pairs) + 1;
+  p.max_items = std::min<size_t>(E, p.pairs) + 1;  // one GEMV item per light expert
+  p.mfma = M > kMaxGemvRows;                       // an expert gets at most M rows
+  p.max_mitems = p.mfma ? p.pairs / kMfmaRows + std::min<size_t>(E, p.pairs / (kMaxGemvRows + 1)) + 1 : 0;
+  p.Mp = p.mfma ? mfma_rows_padded(static_cast<int>(p.pairs)) : 0;
   Carve c;
   size_t dummy;
   c.take(dummy, kCounterBytes);
@@ -174,10 +198,17 @@ MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate)
   c.take(p.sorted_off, p.pairs * 4);
   c.take(p.inv_off, p.pairs * 4);
   c.take(p.items_off, p.max_items * 16);
+  c.take(p.mitems_off, std::max<size_t>(p.max_mitems, 1) * 16);
   c.take(p.nitems_off, 16);
+  c.take(p.heavy_off, p.pairs * 4);
   c.take(p.hq_off, p.pairs * (I / kGroup) * 4 * p.D * 4);
   c.take(p.hf_off, p.pairs * (I / kGroup) * 4);
   c.take(p.o_off, p.pairs * H * 4);
+  c.take(p.apx_off, static_cast<size_t>(p.P) * p.Mp * H * 2);
+  c.take(p.rsx_off, static_cast<size_t>(p.Mp) * 4);
+  c.take(p.h_off, static_cast<size_t>(p.Mp) * I * 4);
+  c.take(p.aph_off, static_cast<size_t>(p.P) * p.Mp * I * 2);
+  c.take(p.rsh_off, static_cast<size_t>(p.Mp) * 4);
   p.bytes = c.cursor;
   return p;
 }
@@ -215,7 +246,7 @@ extern "C" w4a16_status_t w4a16_moe_route(const int32_t* topk_ids, int32_t M, in
       return W4A16_ERR_INVALID_ARG;
   }
   return launch_route(topk_ids, M, top_k, E, counts, offsets, sorted_pairs, inv, nullptr, nullptr,
-                      kMaxGemvRows, stream);
+                      nullptr, nullptr, stream);
 }
 
 extern "C" size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype_t xt,
@@ -226,12 +257,11 @@ extern "C" size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtyp
   return plan_moe(M, top_k, xt, gate).bytes;
 }
 
-extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int32_t M,
-                                            const int32_t* topk_ids, const float* topk_w,
-                                            int32_t top_k, const w4a16_weight_t* gate,
-                                            const w4a16_weight_t* up, const w4a16_weight_t* down,
-                                            float* y, void* ws, size_t ws_bytes,
-                                            hipStream_t stream) {
+namespace w4 {
+static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const int32_t* topk_ids,
+                               const float* topk_w, int32_t top_k, const w4a16_weight_t* gate,
+                               const w4a16_weight_t* up, const w4a16_weight_t* down, float* y,
+                               void* ws, size_t ws_bytes, hipStream_t stream, EventMarks& ev) {
   w4a16_status_t st = check_moe(gate, up, down);
   if (st != W4A16_OK) return st;
   const int E = gate->num_experts, H = gate->K, I = gate->N;
@@ -254,15 +284,21 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   int32_t* sorted = reinterpret_cast<int32_t*>(b + p.sorted_off);
   int32_t* inv = reinterpret_cast<int32_t*>(b + p.inv_off);
   int4* items = reinterpret_cast<int4*>(b + p.items_off);
+  int4* mitems = reinterpret_cast<int4*>(b + p.mitems_off);
   int32_t* n_items = reinterpret_cast<int32_t*>(b + p.nitems_off);
+  int32_t* heavy = reinterpret_cast<int32_t*>(b + p.heavy_off);
   int32_t* hq = reinterpret_cast<int32_t*>(b + p.hq_off);
   float* hf = reinterpret_cast<float*>(b + p.hf_off);
   float* o = reinterpret_cast<float*>(b + p.o_off);
   const int R = static_cast<int>(p.pairs);
 
-  st = launch_route(topk_ids, M, top_k, E, counts, offsets, sorted, inv, items, n_items,
-                    kMaxGemvRows, stream);
+  // 1. expert grouping and work items
+  if ((st = ev.mark(stream)) != W4A16_OK) return st;
+  st = launch_route(topk_ids, M, top_k, E, counts, offsets, sorted, inv, items, mitems, n_items,
+                    heavy, stream);
   if (st != W4A16_OK) return st;
+
+  // 2. gate/up with the SwiGLU epilogue: light experts on the GEMV, heavy on MFMA tiles
   GemvArgs a{};
   a.x = x;
   a.gather = sorted;
@@ -276,9 +312,7 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   a.sc1 = up->scales;
   a.expert_stride = static_cast<size_t>(H / kGroup) * I;
   a.N = I;
-  // grouped GEMVs run one workgroup per (item, tile) over the whole K range
   const GemvShape gu = gemv_shape(p.max_items, I, 1, H / kGroup, 0);
-  const int sub_gu = gu.sub;
   a.tiles = gu.tiles;
   a.S = 1;
   a.gps = a.G;
@@ -288,10 +322,46 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   a.mode = 1;
   a.hq = hq;
   a.hf = hf;
-  st = launch_gemv(a, p.D, sub_gu, xt == W4A16_F32 ? kInF32 : kInBF16, p.max_items * a.tiles,
-                   stream);
+  if ((st = ev.mark(stream)) != W4A16_OK) return st;
+  st = launch_gemv(a, p.D, gu.sub, xt == W4A16_F32 ? kInF32 : kInBF16, p.max_items * a.tiles, stream);
   if (st != W4A16_OK) return st;
 
+  _Float16* apx = reinterpret_cast<_Float16*>(b + p.apx_off);
+  float* rsx = reinterpret_cast<float*>(b + p.rsx_off);
+  float* hraw = reinterpret_cast<float*>(b + p.h_off);
+  _Float16* aph = reinterpret_cast<_Float16*>(b + p.aph_off);
+  float* rsh = reinterpret_cast<float*>(b + p.rsh_off);
+  MfmaArgs ma{};
+  if (p.mfma) {
+    if ((st = ev.mark(stream)) != W4A16_OK) return st;
+    st = launch_mfma_prep(x, xt, R, p.Mp, H, p.P, sorted, top_k, heavy, apx, rsx, stream);
+    if (st != W4A16_OK) return st;
+    ma.ap = apx;
+    ma.rs = rsx;
+    ma.Mp = p.Mp;
+    ma.K = H;
+    ma.G = H / kGroup;
+    ma.qw0 = a.qw0;
+    ma.sc0 = a.sc0;
+    ma.qw1 = a.qw1;
+    ma.sc1 = a.sc1;
+    ma.expert_stride = a.expert_stride;
+    ma.N = I;
+    ma.tiles = (I + kMfmaCols / 2 - 1) / (kMfmaCols / 2);
+    ma.S = 1;
+    ma.gps = ma.G;
+    ma.dense_rows = 0;
+    ma.items = mitems;
+    ma.n_items = n_items + 1;
+    ma.mode = 1;
+    ma.h = hraw;
+    ma.h_bf16 = 0;
+    if ((st = ev.mark(stream)) != W4A16_OK) return st;
+    st = launch_mfma(ma, p.P, p.max_mitems * ma.tiles, stream);
+    if (st != W4A16_OK) return st;
+  }
+
+  // 3. down projection into per-pair outputs
   GemvArgs d{};
   d.xq = hq;
   d.xf = hf;
@@ -303,7 +373,6 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   d.expert_stride = static_cast<size_t>(I / kGroup) * H;
   d.N = H;
   const GemvShape dn = gemv_shape(p.max_items, H, 0, I / kGroup, 0);
-  const int sub_d = dn.sub;
   d.tiles = dn.tiles;
   d.S = 1;
   d.gps = d.G;
@@ -312,11 +381,65 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
   d.n_items = n_items;
   d.mode = 0;
   d.out = o;
-  st = launch_gemv(d, p.D, sub_d, kInDigits, p.max_items * d.tiles, stream);
+  if ((st = ev.mark(stream)) != W4A16_OK) return st;
+  st = launch_gemv(d, p.D, dn.sub, kInDigits, p.max_items * d.tiles, stream);
   if (st != W4A16_OK) return st;
+  if (p.mfma) {
+    if ((st = ev.mark(stream)) != W4A16_OK) return st;
+    st = launch_mfma_prep(hraw, W4A16_F32, R, p.Mp, I, p.P, nullptr, 0, heavy, aph, rsh, stream);
+    if (st != W4A16_OK) return st;
+    MfmaArgs md = ma;
+    md.ap = aph;
+    md.rs = rsh;
+    md.K = I;
+    md.G = I / kGroup;
+    md.qw0 = d.qw0;
+    md.sc0 = d.sc0;
+    md.qw1 = nullptr;
+    md.sc1 = nullptr;
+    md.expert_stride = d.expert_stride;
+    md.N = H;
+    md.tiles = (H + kMfmaCols - 1) / kMfmaCols;
+    md.gps = md.G;
+    md.mode = 0;
+    md.out = o;
+    md.h = nullptr;
+    if ((st = ev.mark(stream)) != W4A16_OK) return st;
+    st = launch_mfma(md, p.P, p.max_mitems * md.tiles, stream);
+    if (st != W4A16_OK) return st;
+  }
 
+  // 4. weighted combine in slot order
+  if ((st = ev.mark(stream)) != W4A16_OK) return st;
   const size_t total = static_cast<size_t>(M) * H;
   combine_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(o, inv, topk_w, M,
                                                                                   top_k, H, y);
-  return launch_status();
+  if ((st = launch_status()) != W4A16_OK) return st;
+  return ev.mark(stream);
+}
+}  // namespace w4
+
+extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int32_t M,
+                                            const int32_t* topk_ids, const float* topk_w,
+                                            int32_t top_k, const w4a16_weight_t* gate,
+                                            const w4a16_weight_t* up, const w4a16_weight_t* down,
+                                            float* y, void* ws, size_t ws_bytes,
+                                            hipStream_t stream) {
+  EventMarks none;
+  return moe_impl(x, xt, M, topk_ids, topk_w, top_k, gate, up, down, y, ws, ws_bytes, stream, none);
+}
+
+extern "C" w4a16_status_t w4a16_moe_grouped_timed(
+    const void* x, w4a16_dtype_t xt, int32_t M, const int32_t* topk_ids, const float* topk_w,
+    int32_t top_k, const w4a16_weight_t* gate, const w4a16_weight_t* up,
+    const w4a16_weight_t* down, float* y, void* ws, size_t ws_bytes, hipStream_t stream,
+    hipEvent_t* events, int32_t capacity, int32_t* recorded) {
+  if (capacity < 0 || (capacity > 0 && events == nullptr)) return W4A16_ERR_INVALID_ARG;
+  EventMarks ev;
+  ev.events = events;
+  ev.capacity = capacity;
+  w4a16_status_t st =
+      moe_impl(x, xt, M, topk_ids, topk_w, top_k, gate, up, down, y, ws, ws_bytes, stream, ev);
+  if (recorded != nullptr) *recorded = ev.recorded;
+  return st;
 }

@@ -66,13 +66,20 @@ def _moe_gpu(x, ids, wts, g, u, d):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("M,E,k,H,I", [(1, 4, 2, 64, 128), (9, 8, 3, 128, 64), (40, 6, 2, 256, 128),
-                                       (64, 16, 8, 64, 64)])
-def test_moe_small(M, E, k, H, I, dtype):
+@pytest.mark.parametrize("M,E,k,H,I,routing", [
+    (1, 4, 2, 64, 128, "uniform"), (9, 8, 3, 128, 64, "uniform"), (40, 6, 2, 256, 128, "uniform"),
+    (64, 16, 8, 64, 64, "uniform"),
+    (200, 4, 2, 128, 256, "uniform"),   # every expert heavy: MFMA tiles only, ragged last tile
+    (300, 64, 4, 256, 128, "zipf"),     # heavy head, light tail: both paths in one call
+])
+def test_moe_small(M, E, k, H, I, routing, dtype):
     cfg = 500 + M
     (gq, gs), (uq, us), (dq, ds) = _experts(E, H, I, cfg)
     g, u, d = weight_from_codes(gq, gs), weight_from_codes(uq, us), weight_from_codes(dq, ds)
-    ids = W.topk_uniform(M, E, k, cfg)
+    ids = W.topk_zipf(M, E, k, 1.1, cfg) if routing == "zipf" else W.topk_uniform(M, E, k, cfg)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    if routing == "zipf":
+        assert counts.max() > 64 and (counts[counts > 0] <= 8).any()
     wts = W.gate_weights(M, k, cfg)
     x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
     y = _moe_gpu(x, to_dev(ids), to_dev(wts), g, u, d)
@@ -122,3 +129,15 @@ def _full_moe(name, sample_tokens):
 
 def test_moe_decode_full_size():
     _full_moe("moe_decode_m64", [0, 37])
+
+
+def test_moe_prefill_full_size():
+    """2048 tokens, Zipf(1.1) routing: the sampled tokens include one routed to
+    the most popular expert (over a thousand rows, MFMA tiles) and their other
+    experts cover the light tail."""
+    cfg = W.CONFIGS["moe_prefill_m2048"]
+    ids = W.topk_zipf(cfg.M, cfg.experts, cfg.top_k, cfg.zipf_alpha, cfg.index)
+    counts = np.bincount(ids.ravel(), minlength=cfg.experts)
+    hot = int(np.argmax(counts))
+    t_hot = int(np.argwhere((ids == hot).any(axis=1))[0, 0])
+    _full_moe("moe_prefill_m2048", [t_hot, 2047])
