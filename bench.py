@@ -18,11 +18,14 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import statistics
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 METRIC = "W4A16 GEMM/MoE µs + achieved HBM GB/s (% of 8 TB/s) at decode M; TFLOP/s at M≥512"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
@@ -41,6 +44,54 @@ def _handles(evs):
     for i, e in enumerate(evs):
         arr[i] = e.cuda_event
     return arr
+
+
+# Sources of the dominant decode kernel; a stored counter summary is only used
+# while they are unchanged.
+TRAFFIC_SOURCES = ("int4_w4a16_group_g32_amd/csrc/gemv.hip", "int4_w4a16_group_g32_amd/csrc/gemv.h")
+
+
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload, kernel_key):
+    """HBM bytes per launch from profiles/traffic_<kernel>_<workload>.txt: the
+    FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) each scaled by the
+    factor the same counter shows on a plain copy of known size.  None if the
+    file is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != sources_sha(TRAFFIC_SOURCES):
+        return None
+    fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"]) * 1024
+    write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"]) * 1024
+    return int(round(fetch + write))
+
+
+def copy_calibration():
+    """A plain device copy of 256 MiB, three times: the reference for scaling
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 64 * 1024 * 1024
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "repeats": 3}), flush=True)
 
 
 def mlp_bytes(M, H, I, xbytes):
@@ -130,7 +181,8 @@ def run_mlp(args, cfg):
         "roofline": {"bound": "hbm", "kernel": ("gemv_kernel" if M <= 8 else "mfma_kernel") +
                      " (fused gate/up + SwiGLU epilogue)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(cfg.name, "gate_up") if M <= 8 else None,
                      "bytes_per_launch": gu_bytes, "avg_launch_us": round(k_gu * 1e3, 2)},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in kern.items()},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
@@ -140,11 +192,85 @@ def run_mlp(args, cfg):
     return result
 
 
-def cpu_baseline_mlp(cfg, base):
-    """The oracle's float64 SwiGLU MLP on a slice of the same weights: the
-    first 2048 intermediate columns (gate/up [7168 x 2048], down [2048 x 7168]),
-    same activations.  Value in the same unit: algorithmic bytes of the slice
-    per second of oracle time (median of 3)."""
+def run_moe(args, cfg):
+    """One routed MoE layer per step (route, grouped gate/up + SwiGLU, grouped
+    down, combine).  Expert weights are drawn and quantized on the GPU; the
+    expert stacks (10.6 GB) are far larger than any cache."""
+    import numpy as np
+    import torch
+    import int4_w4a16_group_g32_amd as L
+    import workloads as W
+
+    E, H, I, M, k = cfg.experts, cfg.K, cfg.N, cfg.M, cfg.top_k
+    xt = L.F32 if cfg.x_dtype == "f32" else L.BF16
+    xbytes = 4 if cfg.x_dtype == "f32" else 2
+    stacks = []
+    for tag, (K, N) in ((W.TAG_GATE, (H, I)), (W.TAG_UP, (H, I)), (W.TAG_DOWN, (I, H))):
+        qw = torch.empty((E, K // 8, N), dtype=torch.int32, device="cuda")
+        sc = torch.empty((E, K // 32, N), dtype=torch.float32, device="cuda")
+        for e in range(E):
+            L.quantize(W.weights(K, N, cfg.index, tag, e, device="cuda"), qw[e], sc[e])
+        stacks.append(L.prepack(L.Weight(qw, sc, K, N, E, L.LAYOUT_CANONICAL), torch.empty_like(qw)))
+        del qw
+    if cfg.routing == "zipf":
+        ids_np = W.topk_zipf(M, E, k, cfg.zipf_alpha, cfg.index)
+    else:
+        ids_np = W.topk_uniform(M, E, k, cfg.index)
+    ids = torch.as_tensor(ids_np).cuda()
+    wts = torch.as_tensor(W.gate_weights(M, k, cfg.index)).cuda()
+    x = W.activations(M, H, cfg.index, cfg.x_dtype, device="cuda")
+    y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    ws = L.new_workspace(L.moe_workspace_bytes(M, k, xt, *stacks))
+    lib = L.load_library()
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    names = (["route", "gate_up_gemv", "down_gemv", "combine"] if M <= 8 else
+             ["route", "gate_up_gemv", "prep_x", "gate_up_mfma", "down_gemv", "prep_h", "down_mfma", "combine"])
+    nev = len(names) + 1
+
+    def step(evs=None):
+        rec = ctypes.c_int32(0)
+        st = lib.w4a16_moe_grouped_timed(L._ptr(x), xt, M, L._ptr(ids), L._ptr(wts), k,
+                                         ctypes.byref(stacks[0].desc()), ctypes.byref(stacks[1].desc()),
+                                         ctypes.byref(stacks[2].desc()), L._ptr(y), L._ptr(ws), ws.numel(),
+                                         sptr, evs, 0 if evs is None else nev, ctypes.byref(rec))
+        if st != 0:
+            raise L.W4A16Error(st, "w4a16_moe_grouped_timed")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(nev) for _ in range(args.steps)]
+    handles = [_handles(e) for e in evs]
+    t0, t1 = _events(2)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(handles[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    kern = {n: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    active = int((np.bincount(ids_np.ravel(), minlength=E) > 0).sum())
+    step_bytes = active * 3 * H * I * 5 // 8 + M * H * xbytes + M * H * 4
+    flops = 2 * 3 * H * I * M * k
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.x_dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "M": M, "experts": E, "top_k": k, "hidden": H, "intermediate": I,
+                   "routing": cfg.routing, "active_experts": active, "bytes_per_step": step_bytes},
+        "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "kernels_us": {n: round(v * 1e3, 2) for n, v in kern.items()},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+    }
+
+
+def cpu_baseline_mlp(cfg, base, repeats=7):
+    """The oracle's float64 SwiGLU MLP (dequantize, then matmul) on the same
+    weights and activations, median of `repeats` runs, after the oracle has
+    quantized the weights itself (not timed).  Value in the metric's unit:
+    algorithmic bytes of the workload per second of oracle time."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -153,14 +279,15 @@ def cpu_baseline_mlp(cfg, base):
     import workloads as W
 
     H, I, M = cfg.K, cfg.N, cfg.M
-    Is = 2048
-    g = W.weights(H, I, cfg.index, W.TAG_GATE, device="cuda")[:, :Is].cpu().numpy()
-    u = W.weights(H, I, cfg.index, W.TAG_UP, device="cuda")[:, :Is].cpu().numpy()
-    d = W.weights(I, H, cfg.index, W.TAG_DOWN, device="cuda")[:Is, :].cpu().numpy()
+    Is = I
+    g = W.weights(H, I, cfg.index, W.TAG_GATE, device="cuda").cpu().numpy()
+    u = W.weights(H, I, cfg.index, W.TAG_UP, device="cuda").cpu().numpy()
+    d = W.weights(I, H, cfg.index, W.TAG_DOWN, device="cuda").cpu().numpy()
     codes = [O.quantize_w4a16(np.ascontiguousarray(a)) for a in (g, u, d)]
+    del g, u, d
     x = W.activations(M, H, cfg.index, cfg.x_dtype, device="cuda").float().cpu().numpy()
     times = []
-    for _ in range(3):
+    for _ in range(repeats):
         t = time.perf_counter()
         O.swiglu_mlp64(x, *codes)
         times.append(time.perf_counter() - t)
@@ -169,8 +296,8 @@ def cpu_baseline_mlp(cfg, base):
     nbytes = mlp_bytes(M, H, Is, xbytes)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{cfg.name} restricted to intermediate columns 0..{Is - 1} "
-                      f"({nbytes} algorithmic bytes), numpy float64, median of 3 runs of {sec:.2f}s",
+            "sample": f"the whole {cfg.name} step ({nbytes} algorithmic bytes), numpy float64 "
+                      f"dequantize-then-matmul, median of {repeats} runs of {sec:.2f}s",
             "seconds": round(sec, 3)}
 
 
@@ -182,6 +309,8 @@ def main():
     ap.add_argument("--workload", default="mlp_decode_m4")
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -196,11 +325,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     cfg = W.CONFIGS[args.workload]
-    if cfg.kind != "mlp":
-        print(f"workload {cfg.name} is a parity-test configuration, not a bench line", file=sys.stderr)
+    if cfg.kind == "mlp":
+        result = run_mlp(args, cfg)
+    elif cfg.kind == "moe":
+        result = run_moe(args, cfg)
+    else:
+        print(f"workload {cfg.name} has no bench line", file=sys.stderr)
         sys.exit(2)
-    result = run_mlp(args, cfg)
     print(json.dumps(result), flush=True)
 
 
