@@ -48,7 +48,8 @@ def _handles(evs):
 
 # Sources of the dominant decode kernel; a stored counter summary is only used
 # while they are unchanged.
-TRAFFIC_SOURCES = ("int4_w4a16_group_g32_amd/csrc/gemv.hip", "int4_w4a16_group_g32_amd/csrc/gemv.h")
+TRAFFIC_SOURCES = ("int4_w4a16_group_g32_amd/csrc/gemv.hip", "int4_w4a16_group_g32_amd/csrc/gemv.h",
+                   "int4_w4a16_group_g32_amd/csrc/mfma_ops.h")
 
 
 def sources_sha(paths):

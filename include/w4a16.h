@@ -64,10 +64,13 @@ typedef enum { W4A16_F32 = 0, W4A16_BF16 = 1 } w4a16_dtype_t;
  *  CANONICAL: qw[E][K/8][N]; nibble j (bits 4j..4j+3) of word (i, n) holds row
  *             k = 8i + j.  This is the interchange format written by a
  *             quantizer (w4a16_quantize).
- *  GROUPED:   qw[E][K/32][N][4]; the 16-byte chunk (g, n) holds the four
- *             canonical words 4g..4g+3 of column n, i.e. one whole 32-row
- *             scale group of one column.  Compute entry points read this
- *             layout only; w4a16_prepack converts.
+ *  GROUPED:   qw[E][K/32][N/64][64][4]; for scale group g and 64-column
+ *             block j, the 16-byte slot 16b + l (b = 0..3, l = 0..15) holds
+ *             canonical word 4g + b (rows 32g + 8b .. 32g + 8b + 7) of the
+ *             columns 64j + 4l .. 64j + 4l + 3, in column order.  One matrix
+ *             core lane reads one slot per group: its four columns' codes for
+ *             one 8-row block.  Compute entry points read this layout only;
+ *             w4a16_prepack converts.
  * Scales are sc[E][K/32][N] float32 in both layouts.
  */
 typedef enum { W4A16_LAYOUT_CANONICAL = 0, W4A16_LAYOUT_GROUPED = 1 } w4a16_layout_t;
@@ -134,9 +137,9 @@ W4A16_API size_t w4a16_gemm_workspace_bytes(int32_t M, const w4a16_weight_t* w, 
 /*
  * y[M][N] = x[M][K] * dequant(W), float32 accumulation and output (page "The
  * Weight of Precision", section "The Kernel: w4a16_gemm").  W must be a dense
- * (num_experts == 1) GROUPED weight.  Small M runs a split-K GEMV on the
- * vector units; larger M runs MFMA tiles.  Deterministic: the same inputs give
- * bitwise the same y.
+ * (num_experts == 1) GROUPED weight.  M <= 8 runs a split-K GEMV on the
+ * matrix cores (all rows in one MFMA tile); larger M runs 64-row MFMA tiles.
+ * Deterministic: the same inputs give bitwise the same y.
  * Errors: INVALID_ARG (null/misaligned, M < 0, bad dtype, y aliasing x),
  * UNSUPPORTED (layout, group size, K % 32, N % 64, num_experts != 1),
  * WORKSPACE (ws_bytes too small), HIP (launch failure).

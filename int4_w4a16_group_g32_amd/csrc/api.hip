@@ -11,8 +11,8 @@ void Carve::take(size_t& off, size_t bytes) {
   cursor = round_up(cursor + bytes, 256);
 }
 
-size_t gemv_partial_bytes(size_t tasks, int S, int sub) {
-  return S > 1 ? tasks * S * partial_tile_floats(sub) * sizeof(float) : 0;
+size_t gemv_partial_bytes(size_t tasks, int S) {
+  return S > 1 ? tasks * S * kPartialTileFloats * sizeof(float) : 0;
 }
 
 MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt) {
@@ -83,17 +83,16 @@ GemmPlan plan_gemm(int M, const w4a16_weight_t* w, w4a16_dtype_t xt) {
     p.bytes = c.cursor;
     return p;
   }
-  p.D = digits_for(xt);
   const int G = w->K / kGroup;
   const size_t items = (static_cast<size_t>(M) + kMaxGemvRows - 1) / kMaxGemvRows;
   const GemvShape sh = gemv_shape(items, w->N, 0, G, kCounterBytes / sizeof(int));
-  p.sub = sh.sub;
   p.tiles = sh.tiles;
   p.tasks = items * p.tiles;
   p.S = sh.S;
+  p.gps = sh.gps;
   Carve c;
   c.take(p.counters_off, kCounterBytes);
-  c.take(p.partials_off, gemv_partial_bytes(p.tasks, p.S, p.sub));
+  c.take(p.partials_off, gemv_partial_bytes(p.tasks, p.S));
   p.bytes = c.cursor;
   return p;
 }
@@ -117,27 +116,23 @@ MlpPlan plan_mlp(int M, w4a16_dtype_t xt, const w4a16_weight_t* gate, const w4a1
     p.bytes = c.cursor;
     return p;
   }
-  p.D = digits_for(xt);
   const int H = gate->K, I = gate->N;
   const int GH = H / kGroup, GI = I / kGroup;
   const size_t items = (static_cast<size_t>(M) + kMaxGemvRows - 1) / kMaxGemvRows;
   const GemvShape gu = gemv_shape(items, I, 1, GH, kCounterBytes / sizeof(int));
-  p.sub_gu = gu.sub;
   p.tiles_gu = gu.tiles;
   p.tasks_gu = items * p.tiles_gu;
   p.S_gu = gu.S;
+  p.gps_gu = gu.gps;
   const GemvShape dn = gemv_shape(items, down->N, 0, GI, kCounterBytes / sizeof(int));
-  p.sub_d = dn.sub;
   p.tiles_d = dn.tiles;
   p.tasks_d = items * p.tiles_d;
   p.S_d = dn.S;
+  p.gps_d = dn.gps;
   Carve c;
   c.take(p.counters_off, kCounterBytes);
-  c.take(p.hq_off, static_cast<size_t>(M) * GI * 4 * p.D * 4);
-  c.take(p.hf_off, static_cast<size_t>(M) * GI * 4);
-  const size_t part = std::max(gemv_partial_bytes(p.tasks_gu, p.S_gu, p.sub_gu),
-                               gemv_partial_bytes(p.tasks_d, p.S_d, p.sub_d));
-  c.take(p.partials_off, part);
+  c.take(p.h_off, static_cast<size_t>(M) * I * 4);
+  c.take(p.partials_off, std::max(gemv_partial_bytes(p.tasks_gu, p.S_gu), gemv_partial_bytes(p.tasks_d, p.S_d)));
   p.bytes = c.cursor;
   return p;
 }
@@ -161,15 +156,13 @@ bool ranges_overlap(const void* a, size_t abytes, const void* b, size_t bbytes) 
 size_t dtype_bytes(w4a16_dtype_t xt) { return xt == W4A16_F32 ? 4 : 2; }
 
 GemvArgs gemv_dense_args(int M, const w4a16_weight_t* w0, const w4a16_weight_t* w1, int mode,
-                         const void* x, const int32_t* xq, const float* xf, int tiles, int S,
-                         char* ws, size_t partials_off, size_t counters_off) {
+                         const void* x, bool x_bf16, int tiles, int S, int gps, char* ws,
+                         size_t partials_off, size_t counters_off) {
   GemvArgs a{};
   a.x = x;
-  a.xq = xq;
-  a.xf = xf;
+  a.x_bf16 = x_bf16 ? 1 : 0;
   a.G = w0->K / kGroup;
   a.K = w0->K;
-  a.R = M;
   a.qw0 = reinterpret_cast<const u32x4*>(w0->qw);
   a.sc0 = w0->scales;
   if (w1 != nullptr) {
@@ -180,7 +173,7 @@ GemvArgs gemv_dense_args(int M, const w4a16_weight_t* w0, const w4a16_weight_t* 
   a.N = w0->N;
   a.tiles = tiles;
   a.S = S;
-  a.gps = (a.G + S - 1) / S;
+  a.gps = gps;
   a.dense_rows = M;
   a.mode = mode;
   a.partials = reinterpret_cast<float*>(ws + partials_off);
@@ -223,10 +216,10 @@ extern "C" w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M,
     return launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream);
   }
   if (!counters_fit(p.tasks, p.S)) return W4A16_ERR_UNSUPPORTED;
-  GemvArgs a = gemv_dense_args(M, w, nullptr, 0, x, nullptr, nullptr, p.tiles, p.S, wsb,
+  GemvArgs a = gemv_dense_args(M, w, nullptr, 0, x, xt == W4A16_BF16, p.tiles, p.S, p.gps, wsb,
                                p.partials_off, p.counters_off);
   a.out = y;
-  return launch_gemv(a, p.D, p.sub, xt == W4A16_F32 ? kInF32 : kInBF16, p.tasks * p.S, stream);
+  return launch_gemv(a, p.tasks * p.S, stream);
 }
 
 extern "C" size_t w4a16_swiglu_mlp_workspace_bytes(int32_t M, w4a16_dtype_t xt,
@@ -297,21 +290,18 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
   }
   if (!counters_fit(p.tasks_gu, p.S_gu) || !counters_fit(p.tasks_d, p.S_d))
     return W4A16_ERR_UNSUPPORTED;
-  int32_t* hq = reinterpret_cast<int32_t*>(wsb + p.hq_off);
-  float* hf = reinterpret_cast<float*>(wsb + p.hf_off);
-  GemvArgs a = gemv_dense_args(M, gate, up, 1, x, nullptr, nullptr, p.tiles_gu, p.S_gu, wsb,
-                               p.partials_off, p.counters_off);
-  a.hq = hq;
-  a.hf = hf;
+  float* h = reinterpret_cast<float*>(wsb + p.h_off);
+  GemvArgs a = gemv_dense_args(M, gate, up, 1, x, xt == W4A16_BF16, p.tiles_gu, p.S_gu, p.gps_gu,
+                               wsb, p.partials_off, p.counters_off);
+  a.h = h;
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(a, p.D, p.sub_gu, xt == W4A16_F32 ? kInF32 : kInBF16, p.tasks_gu * p.S_gu,
-                   stream);
+  st = launch_gemv(a, p.tasks_gu * p.S_gu, stream);
   if (st != W4A16_OK) return st;
-  GemvArgs d = gemv_dense_args(M, down, nullptr, 0, nullptr, hq, hf, p.tiles_d, p.S_d, wsb,
+  GemvArgs d = gemv_dense_args(M, down, nullptr, 0, h, false, p.tiles_d, p.S_d, p.gps_d, wsb,
                                p.partials_off, p.counters_off);
   d.out = y;
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(d, p.D, p.sub_d, kInDigits, p.tasks_d * p.S_d, stream);
+  st = launch_gemv(d, p.tasks_d * p.S_d, stream);
   if (st != W4A16_OK) return st;
   return ev.mark(stream);
 }

@@ -24,7 +24,7 @@ struct MfmaPlan {
 MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt);
 
 struct GemmPlan {
-  int D = 0, S = 1, sub = 1;
+  int S = 1, gps = 1;
   int tiles = 0;
   size_t tasks = 0;
   size_t counters_off = 0, partials_off = 0;
@@ -35,14 +35,13 @@ struct GemmPlan {
 };
 
 struct MlpPlan {
-  int D = 0;
-  int tiles_gu = 0, S_gu = 1, tiles_d = 0, S_d = 1, sub_gu = 1, sub_d = 1;
+  int tiles_gu = 0, S_gu = 1, gps_gu = 1, tiles_d = 0, S_d = 1, gps_d = 1;
   size_t tasks_gu = 0, tasks_d = 0;
-  size_t counters_off = 0, hq_off = 0, hf_off = 0, partials_off = 0;
+  size_t counters_off = 0, h_off = 0, partials_off = 0;
   // MFMA path
   bool mfma = false;
   MfmaPlan gu, dn;
-  size_t apx_off = 0, rsx_off = 0, h_off = 0, aph_off = 0, rsh_off = 0;
+  size_t apx_off = 0, rsx_off = 0, aph_off = 0, rsh_off = 0;
   size_t bytes = 0;
 };
 
@@ -58,7 +57,7 @@ struct EventMarks {
   }
 };
 
-size_t gemv_partial_bytes(size_t tasks, int S, int sub);
+size_t gemv_partial_bytes(size_t tasks, int S);
 GemmPlan plan_gemm(int M, const w4a16_weight_t* w, w4a16_dtype_t xt);
 MlpPlan plan_mlp(int M, w4a16_dtype_t xt, const w4a16_weight_t* gate, const w4a16_weight_t* down);
 bool counters_fit(size_t tasks, int S);
@@ -68,7 +67,7 @@ w4a16_status_t check_mlp(const w4a16_weight_t* gate, const w4a16_weight_t* up,
 bool ranges_overlap(const void* a, size_t abytes, const void* b, size_t bbytes);
 size_t dtype_bytes(w4a16_dtype_t xt);
 GemvArgs gemv_dense_args(int M, const w4a16_weight_t* w0, const w4a16_weight_t* w1, int mode,
-                         const void* x, const int32_t* xq, const float* xf, int tiles, int S,
-                         char* ws, size_t partials_off, size_t counters_off);
+                         const void* x, bool x_bf16, int tiles, int S, int gps, char* ws,
+                         size_t partials_off, size_t counters_off);
 
 }  // namespace w4

@@ -50,25 +50,29 @@ __global__ void quantize_kernel(const float* __restrict__ w, int K, int N, int E
   sc[eg * N + n] = s;
 }
 
-// One thread per (expert, group, column): gathers the four canonical words of
-// the group into one 16-byte chunk.
+// Word index of canonical word (4g + b, n) of expert e in the GROUPED layout:
+// in 64-column block j = n / 64 of group g, the 16-byte slot 16b + (n % 64) / 4
+// holds word b of the four columns 4((n % 64) / 4) .. + 3, in column order.
+__device__ __forceinline__ size_t grouped_word(size_t eg, int N, int n, int b) {
+  const int j = n >> 6, l = (n >> 2) & 15, c = n & 3;
+  return (eg * static_cast<size_t>(N / 64) + j) * 256 + 64 * b + 4 * l + c;
+}
+
+// One thread per (expert, group, column): moves the group's four canonical
+// words of the column to their GROUPED slots.
 __global__ void prepack_kernel(const int32_t* __restrict__ src, int K, int N, int E,
-                               uint4* __restrict__ dst) {
+                               int32_t* __restrict__ dst) {
   const int G = K / kGroup;
   size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
   size_t total = static_cast<size_t>(E) * G * N;
   if (idx >= total) return;
   const int n = static_cast<int>(idx % N);
-  const size_t eg = idx / N;
+  const size_t eg = idx / N;  // e * G + g
   const size_t e = eg / G;
   const int g = static_cast<int>(eg % G);
   const int32_t* in = src + (e * (K / 8) + static_cast<size_t>(g) * 4) * N + n;
-  uint4 v;
-  v.x = static_cast<uint32_t>(in[0]);
-  v.y = static_cast<uint32_t>(in[static_cast<size_t>(N)]);
-  v.z = static_cast<uint32_t>(in[2 * static_cast<size_t>(N)]);
-  v.w = static_cast<uint32_t>(in[3 * static_cast<size_t>(N)]);
-  dst[idx] = v;  // idx == (e * G + g) * N + n
+#pragma unroll
+  for (int b = 0; b < 4; ++b) dst[grouped_word(eg, N, n, b)] = in[static_cast<size_t>(b) * N];
 }
 
 // One thread per (expert, word row, column): writes float32(q * s) for the
@@ -86,8 +90,7 @@ __global__ void dequantize_kernel(const int32_t* __restrict__ qw, const float* _
   const int g = i >> 2;
   uint32_t word;
   if (grouped) {
-    const size_t chunk = (e * (K / kGroup) + g) * N + n;
-    word = static_cast<uint32_t>(qw[chunk * 4 + (i & 3)]);
+    word = static_cast<uint32_t>(qw[grouped_word(e * (K / kGroup) + g, N, n, i & 3)]);
   } else {
     word = static_cast<uint32_t>(qw[ei * N + n]);
   }
@@ -160,8 +163,7 @@ extern "C" w4a16_status_t w4a16_prepack(const w4a16_weight_t* src, int32_t* dst_
   const size_t total = static_cast<size_t>(src->num_experts) * (src->K / kGroup) * src->N;
   if (total == 0) return W4A16_OK;
   prepack_kernel<<<grid_for(total, 256), 256, 0, stream>>>(src->qw, src->K, src->N,
-                                                           src->num_experts,
-                                                           reinterpret_cast<uint4*>(dst_qw));
+                                                           src->num_experts, dst_qw);
   return launch_status();
 }
 

@@ -1,206 +1,223 @@
-// Split-K W4A16 GEMV for decode-sized row counts (vector units only).
+// Split-K W4A16 GEMV on the matrix cores for decode-sized row counts.
 //
 // y[m][n] = sum_g s[g][n] * sum_{k in g} x[m][k] * q[k][n]   (page "The Weight
 // of Precision: Building Native INT4 Quantization for a Custom Speculative
 // Decoding Engine", section "The Kernel: w4a16_gemm": per-group scales on
 // symmetric INT4 codes).
 //
-// Each lane owns SUB output columns (64 apart, so one wave load reads 1 KiB of
-// contiguous 16-byte group chunks) and streams one chunk (32 codes) per group
-// and column.  The codes need one XOR to become signed nibbles; activations
-// are signed 4-bit digits of per-group fixed point (gemv.h), staged by each
-// wave in its own LDS window and read back as uniform vectors.  v_dot8_i32_i4
-// contracts eight codes with eight digits, Horner steps by 16 join the
-// digits, and each group's exact integer sum becomes float32 once and is
-// scaled by s * 2^-sh.
+// A task covers up to eight rows.  One v_mfma_f32_16x16x32_f16 spans exactly
+// one 32-row scale group and 16 weight columns: its B operand holds the exact
+// codes (codes_f16), its 16 A rows the two f16 pieces of the rescaled
+// activations of the eight rows (A rows 0..7: piece 0, rows 8..15: piece 1).
+// Each group's 16x16 result is scaled by s[g][n] on float32 accumulators and
+// the two pieces are added once at the end.  The vector work per 16 columns
+// and group (nine instructions of code expansion, four scale fmas) does not
+// depend on the row count, so the kernel streams the weights at memory speed
+// from one row to eight.
+//
+// A workgroup owns 256 weight columns (a 64-column block per wave; in SwiGLU
+// mode 128 gate and the same 128 up columns) and one K split.  A lane reads
+// one 16-byte GROUPED slot and one 16-byte run of scales per group: the codes
+// of four adjacent columns for one 8-row block, which are column lc of the
+// four MFMA blocks.  The activations of the split
+// are staged in LDS one window of groups at a time, with one power-of-two
+// rescale per row and window (the row's largest magnitude maps into
+// [2^14, 2^15), so f16 neither overflows nor loses the large values); each
+// window's accumulators are scaled back by 2^-e before they join the total.
 #include "gemv.h"
+#include "mfma_ops.h"
 
 namespace w4 {
 namespace {
 
-constexpr int kWin = 8;  // groups per staging window of one wave
+constexpr int kWin = 32;                 // groups per staging window
+constexpr int kRing = 4;                 // groups of codes in flight per wave
+constexpr int kUnitsPerGroup = 16 * 4;   // 16-byte units of one group's A (16 rows x 4 k blocks)
 
-// Largest sh with amax * 2^sh <= 3 * 2^(4D-3).
-template <int D>
-__device__ __forceinline__ int digit_shift(float amax) {
-  if (!(amax > 0.0f)) return 0;
-  const int e = ilogbf(amax);
-  const float m = ldexpf(amax, -e);  // [1, 2)
-  const int sh = (4 * D - 2 - e) - (m > 1.5f ? 1 : 0);
-  return sh > 120 ? 120 : sh;
-}
-
-// Biased fixed point of v: the low 4D bits of the result are X + B with
-// X = round(v * 2^sh) and B = 8 * (16^D - 1) / 15, so hex digit d (from the top)
-// of X + B is the balanced digit d of X plus 8.  One FMA: adding 2^23 + B to the
-// exact product v * 2^sh leaves the rounded integer in the float's mantissa
-// bits (|X| + B < 2^23).
-template <int D>
-__device__ __forceinline__ uint32_t biased_fixed(float v, float scale) {
-  constexpr float kMagic = 8388608.0f + static_cast<float>(8 * ((1 << (4 * D)) - 1) / 15);
-  return __float_as_uint(fmaf(v, scale, kMagic));
-}
-
-// Balanced digit d (most significant first) of a biased_fixed value, as a
-// two's-complement nibble in bits 0..3.
-template <int D>
-__device__ __forceinline__ uint32_t digit_nibble(uint32_t xb, int d) {
-  return ((xb >> (4 * (D - 1 - d))) & 15u) ^ 8u;
-}
-
-template <int D>
-struct WaveWindow {
-  int32_t dig[kWin][kMaxGemvRows][4 * D];
-  float fac[kWin][kMaxGemvRows];
+struct GemvLds {
+  // A operand of the window, unit (g, r, kb) at a_unit(g, r, kb); reused after
+  // the main loop as the tile buffer [kMaxGemvRows][kGemvCols] of floats
+  uint4 buf[kWin * kUnitsPerGroup];
+  float f[kMaxGemvRows];  // 2^-e per row for the current window
 };
+static_assert(kWin % kRing == 0, "ring slots must stay aligned across windows");
+static_assert(sizeof(uint4) * kWin * kUnitsPerGroup >= sizeof(float) * kMaxGemvRows * kGemvCols,
+              "tile buffer must fit in the staging buffer");
 
-template <int D, int SUB>
-union GemvLds {
-  WaveWindow<D> win[kGemvThreads / kWave];
-  float red[kGemvThreads / kWave][kMaxGemvRows][64 * SUB];
-};
-
-template <typename XT>
-__device__ __forceinline__ float act(const void* x, size_t i) {
-  return load_act(static_cast<const XT*>(x), i);
+// k blocks are XOR-swizzled by row so the 16 rows of one k block fall in
+// distinct LDS banks.
+__device__ __forceinline__ int a_unit(int g, int r, int kb) {
+  return (g * 16 + r) * 4 + (kb ^ ((r >> 2) & 3));
 }
 
-// Lane (gi, r) = (lane >> 3, lane & 7) fills item (group gw + gi, row r) of the
-// wave's window.
-template <int D, int IN>
-__device__ __forceinline__ void stage_window(const GemvArgs& a, WaveWindow<D>& w, int gw, int nw,
-                                             int pos0, int nrows, int lane) {
-  const int gi = lane >> 3, r = lane & 7;
-  if (gi >= nw || r >= nrows) return;
-  const int g = gw + gi;
-  const int pos = pos0 + r;
-  if (IN == kInDigits) {
-    const int32_t* src = a.xq + (static_cast<size_t>(g) * a.R + pos) * (4 * D);
-#pragma unroll
-    for (int i = 0; i < 4 * D; ++i) w.dig[gi][r][i] = src[i];
-    w.fac[gi][r] = a.xf[static_cast<size_t>(g) * a.R + pos];
-    return;
-  }
-  long row = pos;
-  if (a.gather != nullptr) {
-    const int pr = a.gather[pos];
-    row = pr < 0 ? -1 : pr / a.top_k;
-  }
-  // two passes over the group's 32 activations (the second hits the cache):
-  // the largest magnitude first, then the digits, eight elements at a time
-  const size_t base = static_cast<size_t>(row < 0 ? 0 : row) * a.K + static_cast<size_t>(g) * kGroup;
-  float amax = 0.0f;
-  if (row >= 0) {
-#pragma unroll
-    for (int c = 0; c < kGroup; ++c)
-      amax = fmaxf(amax, fabsf(IN == kInF32 ? act<float>(a.x, base + c) : act<uint16_t>(a.x, base + c)));
-  }
-  const int sh = digit_shift<D>(amax);
-  const float scale = row < 0 ? 0.0f : ldexpf(1.0f, sh);
-  uint32_t dw[4 * D];
-#pragma unroll
-  for (int i = 0; i < 4 * D; ++i) dw[i] = 0;
-#pragma unroll
-  for (int c = 0; c < kGroup; ++c) {
-    const float xv = row < 0 ? 0.0f : (IN == kInF32 ? act<float>(a.x, base + c) : act<uint16_t>(a.x, base + c));
-    const uint32_t xb = biased_fixed<D>(xv, scale);
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-      dw[d * 4 + (c >> 3)] |= ((xb >> (4 * (D - 1 - d))) & 15u) << (4 * (c & 7));
-  }
-#pragma unroll
-  for (int i = 0; i < 4 * D; ++i) w.dig[gi][r][i] = static_cast<int32_t>(dw[i] ^ 0x88888888u);
-  w.fac[gi][r] = amax > 0.0f ? ldexpf(1.0f, -sh) : 0.0f;
-}
+// Staging of groups [gw, gw + nw) of rows pos0 .. pos0 + nrows - 1.  Wave wv
+// takes rows wv and wv + 4; lane l takes 16 consecutive activations of a row:
+// group l >> 1, k blocks 2(l & 1) and 2(l & 1) + 1.  The raw loads are split
+// from the conversion so they can be issued ahead of the weight prefetch
+// (vector loads complete in order).
+constexpr int kRowsPerWave = kMaxGemvRows / (kGemvThreads / kWave);
 
-template <int SUB>
-__device__ __forceinline__ void load_group(const u32x4* __restrict__ wq, const float* __restrict__ ws,
-                                           size_t gstride, int cstride, int g, u32x4 w[SUB],
-                                           float s[SUB]) {
+__device__ __forceinline__ void load_window(const GemvArgs& a, int gw, int nw, int pos0, int nrows,
+                                            int wv, int lane, float v[kRowsPerWave][16]) {
+  const int gl = lane >> 1, hb = lane & 1;
 #pragma unroll
-  for (int j = 0; j < SUB; ++j) {
-    w[j] = __builtin_nontemporal_load(wq + static_cast<size_t>(g) * gstride + cstride * j);
-    s[j] = __builtin_nontemporal_load(ws + static_cast<size_t>(g) * gstride + cstride * j);
-  }
-}
-
-// One wave: groups [g_lo, g_hi) of its columns, NR rows from position pos0.
-template <int D, int NR, int SUB, int IN>
-__device__ __forceinline__ void wave_gemv(const GemvArgs& a, const u32x4* wq, const float* ws,
-                                          int cstride, int pos0, int g_lo, int g_hi,
-                                          WaveWindow<D>& win, int lane, float acc[SUB][NR]) {
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int m = wv + j * (kGemvThreads / kWave);
 #pragma unroll
-  for (int j = 0; j < SUB; ++j)
+    for (int i = 0; i < 16; ++i) v[j][i] = 0.0f;
+    if (m >= nrows) continue;
+    long src = pos0 + m;
+    if (a.gather != nullptr) {
+      const int pr = a.gather[pos0 + m];
+      src = pr < 0 ? -1 : pr / a.top_k;
+    }
+    if (src < 0 || gl >= nw) continue;
+    const size_t base = static_cast<size_t>(src) * a.K + static_cast<size_t>(gw + gl) * kGroup + 16 * hb;
+    if (a.x_bf16) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + base);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[j][r] = 0.0f;
-  const size_t gstride = static_cast<size_t>(a.N);
-  for (int gw = g_lo; gw < g_hi; gw += kWin) {
-    const int nw = min(kWin, g_hi - gw);
-    u32x4 wc[SUB];
-    float sc[SUB];
-    load_group<SUB>(wq, ws, gstride, cstride, gw, wc, sc);
-    stage_window<D, IN>(a, win, gw, nw, pos0, NR, lane);
-    __builtin_amdgcn_wave_barrier();
-    for (int gi = 0; gi < nw; ++gi) {
-      u32x4 wn[SUB];
-      float sn[SUB];
-      load_group<SUB>(wq, ws, gstride, cstride, gw + min(gi + 1, nw - 1), wn, sn);
-      int32_t q[SUB][4];
+      for (int q = 0; q < 2; ++q) {
+        const uint4 u = p[q];
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int j = 0; j < SUB; ++j) {
-        q[j][0] = static_cast<int32_t>(wc[j].x ^ 0x88888888u);
-        q[j][1] = static_cast<int32_t>(wc[j].y ^ 0x88888888u);
-        q[j][2] = static_cast<int32_t>(wc[j].z ^ 0x88888888u);
-        q[j][3] = static_cast<int32_t>(wc[j].w ^ 0x88888888u);
-      }
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int32_t* dp = win.dig[gi][r];
-        int32_t dg[4 * D];
-#pragma unroll
-        for (int i = 0; i < 4 * D; ++i) dg[i] = dp[i];
-        const float f = win.fac[gi][r];
-#pragma unroll
-        for (int j = 0; j < SUB; ++j) {
-          int t = 0;
-#pragma unroll
-          for (int d = 0; d < D; ++d) {
-            t *= 16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_sdot8(dg[d * 4 + i], q[j][i], t, false);
-          }
-          acc[j][r] = fmaf(sc[j] * f, static_cast<float>(t), acc[j][r]);
+        for (int t = 0; t < 4; ++t) {
+          v[j][8 * q + 2 * t] = __uint_as_float(wd[t] << 16);
+          v[j][8 * q + 2 * t + 1] = __uint_as_float(wd[t] & 0xffff0000u);
         }
       }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + base);
 #pragma unroll
-      for (int j = 0; j < SUB; ++j) {
-        wc[j] = wn[j];
-        sc[j] = sn[j];
+      for (int q = 0; q < 4; ++q) {
+        const float4 u = p[q];
+        v[j][4 * q] = u.x;
+        v[j][4 * q + 1] = u.y;
+        v[j][4 * q + 2] = u.z;
+        v[j][4 * q + 3] = u.w;
       }
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
-template <int D, int NR, int SUB, int IN>
-__device__ __forceinline__ void run_rows(const GemvArgs& a, const u32x4* wq, const float* ws,
-                                         int cstride, int pos0, int g_lo, int g_hi,
-                                         GemvLds<D, SUB>& lds, int wv, int lane) {
-  float acc[SUB][NR];
-  wave_gemv<D, NR, SUB, IN>(a, wq, ws, cstride, pos0, g_lo, g_hi, lds.win[wv], lane, acc);
-  __syncthreads();  // every wave is done with its window before the buffer is reused
+// Per row: the window's largest magnitude sets e (max * 2^e in [2^14, 2^15)),
+// the pieces of x * 2^e go to LDS in the A layout and 2^-e to lds.f.  Absent
+// rows get the factor 0 and are never read as A.
+__device__ __forceinline__ void convert_window(GemvLds& lds, int nw, int nrows, int wv, int lane,
+                                               const float v[kRowsPerWave][16]) {
+  const int gl = lane >> 1, hb = lane & 1;
 #pragma unroll
-  for (int j = 0; j < SUB; ++j)
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int m = wv + j * (kGemvThreads / kWave);
+    if (m >= nrows) {
+      if (lane == 0) lds.f[m] = 0.0f;
+      continue;
+    }
+    float amax = 0.0f;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) lds.red[wv][r][64 * j + lane] = acc[j][r];
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    int e = 0;
+    if (amax > 0.0f) {
+      int lg = ilogbf(amax);
+      lg = lg > 120 ? 120 : (lg < -120 ? -120 : lg);
+      e = 14 - lg;
+    }
+    const float scale = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
+    if (lane == 0) lds.f[m] = amax > 0.0f ? ldexpf(1.0f, -e) : 0.0f;
+    if (gl < nw) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        half8 p0, p1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float t = v[j][8 * b + kCodeOrder[i]] * scale;
+          const _Float16 h0 = static_cast<_Float16>(t);
+          p0[i] = h0;
+          p1[i] = static_cast<_Float16>(t - static_cast<float>(h0));
+        }
+        const int kb = 2 * hb + b;
+        *reinterpret_cast<half8*>(&lds.buf[a_unit(gl, m, kb)]) = p0;
+        *reinterpret_cast<half8*>(&lds.buf[a_unit(gl, 8 + m, kb)]) = p1;
+      }
+    }
+  }
 }
 
-template <int D, int SUB, int IN>
-__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(W4_GEMV_WAVES_PER_EU)))
+struct GroupCodes {
+  uint32_t w[4];  // word kb of the lane's four columns (one per 16-column MFMA block)
+  float s[4];     // the four columns' scales
+};
+
+// Codes and scales of group g (clamped to the split's last group, so the
+// prefetch past the end re-reads a group that is still in cache instead of
+// branching): the lane's 16-byte GROUPED slot and its four scales.
+__device__ __forceinline__ void load_group(const u32x4* __restrict__ wp, const f32x4* __restrict__ sp,
+                                           size_t gstride, int g, int g_last, GroupCodes& c) {
+  const size_t gg = static_cast<size_t>(min(g, g_last));
+  const u32x4 w = __builtin_nontemporal_load(wp + gg * gstride);
+  const f32x4 v = __builtin_nontemporal_load(sp + gg * (gstride / 4));
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    c.w[cb] = w[cb];
+    c.s[cb] = v[cb];
+  }
+}
+
+__device__ __forceinline__ void mma_group(const GemvLds& lds, int gl, int lc, int kb, bool on,
+                                          uint32_t magic, const GroupCodes& c, f32x4 acc[4]) {
+  half8 af = *reinterpret_cast<const half8*>(&lds.buf[a_unit(gl, lc, kb)]);
+  if (!on) af = half8{};
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const half8 bq = codes_f16(c.w[cb], magic);
+    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bq, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[cb][i] = fmaf(c.s[cb], d[i], acc[cb][i]);
+  }
+}
+
+// Sums of the S split partials of rows 0..nrows-1, column t, in split order:
+// blocks of 4 rows x kB splits are loaded together (indices clamped into
+// range, so no load is predicated) and then added.
+template <int kB>
+__device__ __forceinline__ void read_partials(const float* base, int S, int nrows, int t,
+                                              float v[kMaxGemvRows]) {
+  constexpr size_t tf = kPartialTileFloats;
+#pragma unroll
+  for (int r0 = 0; r0 < kMaxGemvRows; r0 += 4) {
+    if (r0 >= nrows) break;
+    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < S; s0 += kB) {
+      float p[4][kB];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+          const int r = min(r0 + rr, nrows - 1);
+          const int s2 = min(s0 + j, S - 1);
+          p[rr][j] = __hip_atomic_load(base + s2 * tf + r * kGemvCols + t, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int j = 0; j < kB; ++j)
+          if (s0 + j < S) sum[rr] += p[rr][j];
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      if (r0 + rr < nrows) v[r0 + rr] = sum[rr];
+  }
+}
+
+// kMulti: the split spans more than one staging window (each window's
+// accumulators are scaled by its own 2^-e before they join the total).
+template <bool kMulti>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void gemv_kernel(const GemvArgs a) {
-  __shared__ GemvLds<D, SUB> lds;
+  __shared__ GemvLds lds;
   __shared__ int last;
-  constexpr int TW = 64 * SUB;  // values per row of one tile
 
   const int task = blockIdx.x;
   const int split = task % a.S;
@@ -222,193 +239,192 @@ void gemv_kernel(const GemvArgs a) {
 
   const int wv = wave_id();
   const int lane = lane_id();
-  // plain tiles: 64*SUB consecutive columns, sub-column j at +64j; SwiGLU tiles:
-  // 32*SUB gate columns (lanes 0..31) and the same up columns (lanes 32..63),
-  // sub-column j at +32j
-  int mat = 0, col0;
+  const int lc = lane & 15, kb = lane >> 4;
+  // plain: wave wv owns columns tile*256 + 64wv ..; SwiGLU: waves 0, 1 the gate
+  // and waves 2, 3 the up columns tile*128 + 64(wv & 1) ..
+  int mat = 0, c0;
   if (a.mode == 1) {
-    mat = lane >> 5;
-    col0 = tile * 32 * SUB + (lane & 31);
+    mat = wv >> 1;
+    c0 = tile * (kGemvCols / 2) + (wv & 1) * 64;
   } else {
-    col0 = tile * TW + lane;
+    c0 = tile * kGemvCols + wv * 64;
   }
-  const int cstride = a.mode == 1 ? 32 : 64;
+  const bool wave_ok = c0 < a.N;
   const size_t ebase = static_cast<size_t>(expert) * a.expert_stride;
-  const u32x4* wq = (mat ? a.qw1 : a.qw0) + ebase + col0;
-  const float* wsc = (mat ? a.sc1 : a.sc0) + ebase + col0;
+  const int g_lo = split * a.gps;
+  const int g_hi = min(a.G, g_lo + a.gps);
+  // the lane reads GROUPED slot 16kb + lc of the wave's 64-column block: word
+  // kb of columns c0 + 4lc + cb, cb = 0..3 (MFMA block cb, column lc)
+  const int cbase = wave_ok ? c0 : 0;
+  const u32x4* wp = (mat ? a.qw1 : a.qw0) + ebase + cbase + 16 * kb + lc;
+  const f32x4* sp = reinterpret_cast<const f32x4*>((mat ? a.sc1 : a.sc0) + ebase + cbase + 4 * lc);
+  const size_t gstride = static_cast<size_t>(a.N);  // chunks (and scales) per group row
+  const int g_last = g_hi - 1;
+  const uint32_t magic = magic_vgpr();
+  // A rows whose activations are absent read as zero (lc & 7 is the row)
+  const bool arow = (lc & 7) < nrows;
 
-  const int sg_lo = split * a.gps;
-  const int sg_hi = min(a.G, sg_lo + a.gps);
-  const int nw = kGemvThreads / kWave;
-  const int span = (sg_hi - sg_lo + nw - 1) / nw;
-  const int g_lo = min(sg_hi, sg_lo + wv * span);
-  const int g_hi = min(sg_hi, g_lo + span);
+  f32x4 tot[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) tot[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // ring of kRing groups in flight: group g sits in slot (g - g_lo) % kRing
+  GroupCodes ring[kRing];
+  float xv[kRowsPerWave][16];
+  load_window(a, g_lo, min(kWin, g_hi - g_lo), pos0, nrows, wv, lane, xv);  // ahead of the weights
+  if (wave_ok) {
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) load_group(wp, sp, gstride, g_lo + j, g_last, ring[j]);
+  }
 
-  switch (nrows) {
-#define W4_CASE(n) \
-  case n: run_rows<D, n, SUB, IN>(a, wq, wsc, cstride, pos0, g_lo, g_hi, lds, wv, lane); break;
-    W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6) W4_CASE(7)
-    default: run_rows<D, 8, SUB, IN>(a, wq, wsc, cstride, pos0, g_lo, g_hi, lds, wv, lane); break;
-#undef W4_CASE
+  for (int gw = g_lo; gw < g_hi; gw += kWin) {
+    const int nw = min(kWin, g_hi - gw);
+    if (gw != g_lo) {
+      __syncthreads();  // the previous window is consumed
+      load_window(a, gw, nw, pos0, nrows, wv, lane, xv);
+    }
+    convert_window(lds, nw, nrows, wv, lane, xv);
+    __syncthreads();
+    if (wave_ok) {
+      f32x4 wacc[4];
+      f32x4* acc = kMulti ? wacc : tot;
+      if (kMulti) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) wacc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      // kWin is a multiple of kRing, so slots stay aligned across windows; the
+      // loads run kRing groups ahead
+      for (int gl = 0; gl < nw; gl += kRing) {
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+          const bool on = gl + j < nw;
+          mma_group(lds, on ? gl + j : gl, lc, kb, arow && on, magic, ring[j], acc);
+          load_group(wp, sp, gstride, gw + gl + j + kRing, g_last, ring[j]);
+          // keep each refill right behind its consumer: the scheduler would
+          // otherwise sink all refills to the end and drain the ring
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // accumulator element i of this lane is A row 4kb + i: row (4kb + i) & 7
+      const float4 f4 = *reinterpret_cast<const float4*>(&lds.f[4 * (kb & 1)]);
+      const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
+      if (kMulti) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tot[cb][i] = fmaf(wacc[cb][i], fr[i], tot[cb][i]);
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tot[cb][i] *= fr[i];
+      }
+    }
+  }
+
+  // piece 0 (lanes 0..31) + piece 1 (lanes 32..63) of rows 4kb + i
+  float pv[4][4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[cb][i] = tot[cb][i] + __shfl_xor(tot[cb][i], 32);
+  __syncthreads();  // every wave is done with the staged activations
+  float* red = reinterpret_cast<float*>(lds.buf);  // [kMaxGemvRows][kGemvCols]
+  if (lane < 32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * kb + i;
+      if (m < nrows) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) red[m * kGemvCols + wv * 64 + 4 * lc + cb] = pv[cb][i];
+      }
+    }
   }
   __syncthreads();
 
-  // Fixed-order reduction over the four waves, then over the K splits.  Thread
-  // t owns elements e = t + 256i of the tile [nrows][TW].
-  constexpr int kEl = kMaxGemvRows * TW / kGemvThreads;  // elements per thread (upper bound)
-  float* tilev = &lds.red[0][0][0];  // reduced tile, row stride TW
-  float v[kEl];
+  // Thread t owns column t of the tile, rows 0 .. nrows - 1.
+  const int t = static_cast<int>(threadIdx.x);
+  float v[kMaxGemvRows];
 #pragma unroll
-  for (int i = 0; i < kEl; ++i) {
-    const int e = static_cast<int>(threadIdx.x) + kGemvThreads * i;
-    const int r = e / TW, cc = e % TW;
-    v[i] = r < nrows ? ((lds.red[0][r][cc] + lds.red[1][r][cc]) + lds.red[2][r][cc]) + lds.red[3][r][cc]
-                     : 0.0f;
-  }
+  for (int r = 0; r < kMaxGemvRows; ++r) v[r] = r < nrows ? red[r * kGemvCols + t] : 0.0f;
+
   if (a.S > 1) {
     // Partials are written through to the device coherence point (agent-scope
     // stores), the arrival counter is an agent-scope atomic, and the last
-    // workgroup of the tile reads every partial back with agent-scope loads,
-    // all issued before any is summed, and sums them in split order.
+    // workgroup of the tile reads the partials back with agent-scope loads,
+    // many in flight at once, and sums them in split order.
     const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
-    const size_t tf = static_cast<size_t>(kMaxGemvRows) * TW;
+    const size_t tf = kPartialTileFloats;
     float* base = a.partials + ct * a.S * tf;
 #pragma unroll
-    for (int i = 0; i < kEl; ++i) {
-      const int e = static_cast<int>(threadIdx.x) + kGemvThreads * i;
-      if (e / TW < nrows)
-        __hip_atomic_store(base + split * tf + e, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int r = 0; r < kMaxGemvRows; ++r)
+      if (r < nrows)
+        __hip_atomic_store(base + split * tf + r * kGemvCols + t, v[r], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int prev = __hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+      const int prev = __hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last = (prev == a.S - 1);
     }
     __syncthreads();
     if (!last) return;
-#pragma unroll
-    for (int i = 0; i < kEl; ++i) {
-      const int e = static_cast<int>(threadIdx.x) + kGemvThreads * i;
-      if (e / TW >= nrows) continue;
-      float part[kMaxSplits];
-#pragma unroll
-      for (int s2 = 0; s2 < kMaxSplits; ++s2)
-        part[s2] = s2 < a.S ? __hip_atomic_load(base + s2 * tf + e, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT)
-                            : 0.0f;
-      float t = 0.0f;
-#pragma unroll
-      for (int s2 = 0; s2 < kMaxSplits; ++s2)
-        if (s2 < a.S) t += part[s2];
-      v[i] = t;
-    }
+    if (a.S <= 8)
+      read_partials<8>(base, a.S, nrows, t, v);
+    else
+      read_partials<16>(base, a.S, nrows, t, v);
     if (threadIdx.x == 0)
       __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();  // all reads of the per-wave buffers are done
-#pragma unroll
-  for (int i = 0; i < kEl; ++i) tilev[threadIdx.x + kGemvThreads * i] = v[i];
-  __syncthreads();
 
-  // Epilogue: wave w takes sub-columns j = w, w + 4, ...
-  for (int j = wv; j < SUB; j += kGemvThreads / kWave) {
-    if (a.mode == 0) {
-      for (int r = 0; r < nrows; ++r)
-        a.out[static_cast<size_t>(pos0 + r) * a.N + col0 + 64 * j] = tilev[r * TW + 64 * j + lane];
-      continue;
-    }
-    // SwiGLU: lanes 0..31 hold gate and 32..63 up of h columns (tile*SUB + j)*32 + c.
-    // Those 32 columns are one scale group of the down projection's input, so
-    // its digits are formed here directly.
-    const int c = lane & 31;
-    const int hg = tile * SUB + j;  // h group index
-    for (int r = 0; r < nrows; ++r) {
-      const float gv = tilev[r * TW + 64 * j + c];
-      const float uv = tilev[r * TW + 64 * j + 32 + c];
-      const float h = silu(gv) * uv;
-      float amax = fabsf(h);
+  if (a.mode == 0) {
+    const int n = tile * kGemvCols + t;
+    if (n < a.N) {
 #pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-      const int sh = digit_shift<D>(amax);
-      const uint32_t xb = biased_fixed<D>(h, ldexpf(1.0f, sh));
-      const size_t prow = static_cast<size_t>(pos0 + r);
-      int32_t* blk = a.hq + (static_cast<size_t>(hg) * a.R + prow) * (4 * D);
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        // gather the nibbles of lanes 8j'..8j'+7 into dword (d, j')
-        uint32_t nib = digit_nibble<D>(xb, d) << (4 * (c & 7));
-        nib |= __shfl_xor(nib, 1);
-        nib |= __shfl_xor(nib, 2);
-        nib |= __shfl_xor(nib, 4);
-        if (lane < 32 && (c & 7) == 0) blk[d * 4 + (c >> 3)] = static_cast<int32_t>(nib);
-      }
-      if (lane == 0) a.hf[static_cast<size_t>(hg) * a.R + prow] = amax > 0.0f ? ldexpf(1.0f, -sh) : 0.0f;
-      if (a.h_raw != nullptr && lane < 32) {
-        const size_t hi = prow * a.N + static_cast<size_t>(hg) * 32 + c;
-        if (a.h_bf16)
-          static_cast<uint16_t*>(a.h_raw)[hi] = f32_to_bf16(h);
-        else
-          static_cast<float*>(a.h_raw)[hi] = h;
-      }
+      for (int r = 0; r < kMaxGemvRows; ++r)
+        if (r < nrows) a.out[static_cast<size_t>(pos0 + r) * a.N + n] = v[r];
     }
+    return;
+  }
+  // SwiGLU: columns 0..127 of the tile are gate, 128..255 the matching up columns
+#pragma unroll
+  for (int r = 0; r < kMaxGemvRows; ++r)
+    if (r < nrows) red[r * kGemvCols + t] = v[r];
+  __syncthreads();
+  const int n = tile * (kGemvCols / 2) + t;
+  if (t < kGemvCols / 2 && n < a.N) {
+#pragma unroll
+    for (int r = 0; r < kMaxGemvRows; ++r)
+      if (r < nrows)
+        a.h[static_cast<size_t>(pos0 + r) * a.N + n] =
+            silu(red[r * kGemvCols + t]) * red[r * kGemvCols + kGemvCols / 2 + t];
   }
 }
 
 }  // namespace
 
 GemvShape gemv_shape(size_t items, int N, int mode, int G, size_t max_split_tasks) {
-  const int per_sub = mode == 1 ? 32 : 64;
-  const double cap = W4_GEMV_TARGET_WGS;
-  GemvShape best;
-  double best_fill = -1.0;
-  for (int sub = W4_GEMV_SUB; sub >= 1; sub >>= 1) {
-    if (N % (per_sub * sub) != 0) continue;
-    GemvShape sh;
-    sh.sub = sub;
-    sh.tiles = N / (per_sub * sub);
-    const size_t tasks = items * static_cast<size_t>(sh.tiles);
-    int max_s = G / (W4_GEMV_MIN_GROUPS_PER_WAVE * (kGemvThreads / kWave));
-    if (max_s > kMaxSplits) max_s = kMaxSplits;
-    if (tasks > max_split_tasks) max_s = 1;
-    int S = static_cast<int>(cap / static_cast<double>(tasks));
-    if (S > max_s) S = max_s;
-    if (S < 1) S = 1;
-    sh.S = S;
-    const double wgs = static_cast<double>(tasks) * S;
-    const double rounds = wgs <= cap ? 1.0 : static_cast<double>(static_cast<size_t>((wgs + cap - 1) / cap));
-    // many rounds (grouped calls size the grid for the worst case) balance by themselves
-    const double fill = rounds >= 4.0 ? 1.0 : wgs / (rounds * cap);
-    if (fill > best_fill * 1.05) {  // a smaller sub must fill clearly better
-      best = sh;
-      best_fill = fill;
-    }
-  }
-  return best;
+  GemvShape sh;
+  const int per_tile = mode == 1 ? kGemvCols / 2 : kGemvCols;
+  sh.tiles = (N + per_tile - 1) / per_tile;
+  const size_t tasks = items * static_cast<size_t>(sh.tiles);
+  int S = tasks > 0 ? static_cast<int>(W4_GEMV_TARGET_WGS / tasks) : 1;
+  int max_s = G / W4_GEMV_MIN_GROUPS_PER_SPLIT;
+  if (max_s > kMaxSplits) max_s = kMaxSplits;
+  if (S > max_s) S = max_s;
+  if (tasks > max_split_tasks) S = 1;
+  if (S < 1) S = 1;
+  sh.gps = G > 0 ? (G + S - 1) / S : 1;
+  sh.S = G > 0 ? (G + sh.gps - 1) / sh.gps : 1;  // no empty split
+  return sh;
 }
 
-w4a16_status_t launch_gemv(const GemvArgs& a, int D, int SUB, int input, size_t num_tasks,
-                           hipStream_t stream) {
+w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stream) {
   if (num_tasks == 0) return W4A16_OK;
   if (num_tasks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
-  const unsigned grid = static_cast<unsigned>(num_tasks);
-#define W4_GO(d, sub, in) gemv_kernel<d, sub, in><<<grid, kGemvThreads, 0, stream>>>(a)
-#define W4_SUBS(d, in)                 \
-  if (SUB == 4) W4_GO(d, 4, in);       \
-  else if (SUB == 2) W4_GO(d, 2, in);  \
-  else W4_GO(d, 1, in);
-  if (D == 5) {
-    if (input == kInF32) { W4_SUBS(5, kInF32) }
-    else if (input == kInBF16) { W4_SUBS(5, kInBF16) }
-    else { W4_SUBS(5, kInDigits) }
-  } else {
-    if (input == kInF32) { W4_SUBS(4, kInF32) }
-    else if (input == kInBF16) { W4_SUBS(4, kInBF16) }
-    else { W4_SUBS(4, kInDigits) }
-  }
-#undef W4_SUBS
-#undef W4_GO
+  if (a.gps > kWin)
+    gemv_kernel<true><<<static_cast<unsigned>(num_tasks), kGemvThreads, 0, stream>>>(a);
+  else
+    gemv_kernel<false><<<static_cast<unsigned>(num_tasks), kGemvThreads, 0, stream>>>(a);
   return launch_status();
 }
 

@@ -5,21 +5,18 @@
 // Decoding Engine", section "The Kernel: w4a16_gemm").
 //
 // One v_mfma_f32_16x16x32_f16 spans exactly one 32-row scale group: B holds
-// the exact codes q = (1024 + nibble) - 1032 in f16 (two bit operations and a
-// packed f16 subtraction per pair), A holds the f16 pieces of the rescaled
-// activations (mfma.h), and the group's 16x16 result is scaled by s[g][n] on
-// the float32 accumulators.  A tile is 64 rows x 256 weight columns; the
-// activation pieces of a window of groups are staged once in LDS and shared by
-// the four waves, each of which streams its own 64 columns of codes (one dword
-// per lane per 16 columns and group, 256 contiguous bytes per wave load).
+// the exact codes (codes_f16), A the f16 pieces of the rescaled activations
+// (mfma.h), and the group's 16x16 result is scaled by s[g][n] on the float32
+// accumulators.  A tile is 64 rows x 256 weight columns; the activation
+// pieces of a window of groups are staged once in LDS and shared by the four
+// waves, each of which streams its own 64 columns of codes: one 16-byte
+// GROUPED slot per lane and group (a contiguous kilobyte per wave load), whose
+// four words are column lc of the four MFMA blocks.
 #include "mfma.h"
+#include "mfma_ops.h"
 
 namespace w4 {
 namespace {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGw = 4;       // groups per staged activation window
 constexpr int kRowPad = 40;  // halves per staged row of 32 (80-byte stride)
@@ -60,12 +57,11 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const XT* __restrict__ x
   }
   const float scale = (src >= 0 && amax > 0.0f) ? ldexpf(1.0f, e) : 0.0f;
   if (threadIdx.x == 0) rs[row] = scale > 0.0f ? ldexpf(1.0f, -e) : 0.0f;
-  constexpr int kPerm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
   for (int b = threadIdx.x; b < K / 8; b += 256) {
     half8 h0, h1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float v = scale == 0.0f ? 0.0f : load_act(xr, 8 * b + kPerm[i]) * scale;
+      const float v = scale == 0.0f ? 0.0f : load_act(xr, 8 * b + kCodeOrder[i]) * scale;
       const _Float16 hi = static_cast<_Float16>(v);
       h0[i] = hi;
       if (P == 2) h1[i] = static_cast<_Float16>(v - static_cast<float>(hi));
@@ -76,20 +72,6 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const XT* __restrict__ x
 }
 
 // ------------------------------------------------------------ the MFMA kernel
-
-// Exact f16 codes of one packed word, in the order 0,4,1,5,2,6,3,7.
-__device__ __forceinline__ half8 codes_f16(uint32_t w) {
-  half8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t p = ((w >> (4 * i)) & 0x000f000fu) | 0x64006400u;  // (1024+n_i, 1024+n_{i+4})
-    half2v h = __builtin_bit_cast(half2v, p);
-    h = h - half2v{static_cast<_Float16>(1032.0f), static_cast<_Float16>(1032.0f)};
-    r[2 * i] = h[0];
-    r[2 * i + 1] = h[1];
-  }
-  return r;
-}
 
 template <int P>
 struct MfmaLds {
@@ -119,39 +101,33 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(const MfmaArgs a) {
   const int wv = wave_id();
   const int lane = lane_id();
   const int lc = lane & 15, kb = lane >> 4;
+  const uint32_t magic = magic_vgpr();
 
-  // columns of the four 16-column blocks of this wave
-  int ncol[4];
-  int mat[4];
+  // The lane reads one 16-byte GROUPED slot per group: word kb of four
+  // adjacent columns col0 .. col0 + 3, which are column lc of MFMA blocks
+  // cb = 0..3.  Plain: the wave's 64-column block, slot 16kb + lc.  SwiGLU:
+  // the wave's 32 h columns h0 .. h0 + 31, lanes lc < 8 from gate and lanes
+  // lc >= 8 from up (the same h columns), so a lane pair (lc, lc + 8) holds
+  // gate and up of one output.
+  int mat, col0, chunk;
   bool wave_ok;
   if (a.mode == 1) {
     const int h0 = tile * 128 + wv * 32;
     wave_ok = h0 < a.N;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      mat[cb] = cb >> 1;
-      ncol[cb] = h0 + (cb & 1) * 16 + lc;
-    }
+    mat = lc >> 3;
+    col0 = h0 + 4 * (lc & 7);
+    chunk = (h0 >> 6) * 64 + 16 * kb + ((h0 >> 5) & 1) * 8 + (lc & 7);
   } else {
     const int c0 = tile * kMfmaCols + wv * 64;
     wave_ok = c0 < a.N;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      mat[cb] = 0;
-      ncol[cb] = c0 + cb * 16 + lc;
-    }
+    mat = 0;
+    col0 = c0 + 4 * lc;
+    chunk = c0 + 16 * kb + lc;
   }
   const size_t ebase = static_cast<size_t>(expert) * a.expert_stride;
-  const uint32_t* wp[4];
-  const float* sp[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const size_t n = wave_ok ? static_cast<size_t>(ncol[cb]) : 0;
-    wp[cb] = reinterpret_cast<const uint32_t*>((mat[cb] ? a.qw1 : a.qw0) + ebase + n) + kb;
-    sp[cb] = (mat[cb] ? a.sc1 : a.sc0) + ebase + n;
-  }
-  const size_t gstride_w = static_cast<size_t>(a.N) * 4;  // dwords per group row
-  const size_t gstride_s = static_cast<size_t>(a.N);
+  const u32x4* wp = (mat ? a.qw1 : a.qw0) + ebase + (wave_ok ? chunk : 0);
+  const float* sp = (mat ? a.sc1 : a.sc0) + ebase + (wave_ok ? col0 : 0);
+  const size_t gstride = static_cast<size_t>(a.N);  // chunks (and scales) per group row
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -176,31 +152,19 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(const MfmaArgs a) {
     }
     __syncthreads();
     if (wave_ok) {
-      uint32_t wn[4];
-      float sn[4];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        wn[cb] = __builtin_nontemporal_load(wp[cb] + static_cast<size_t>(gw) * gstride_w);
-        sn[cb] = __builtin_nontemporal_load(sp[cb] + static_cast<size_t>(gw) * gstride_s);
-      }
+      u32x4 wn = __builtin_nontemporal_load(wp + static_cast<size_t>(gw) * gstride);
+      f32x4 sn = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + static_cast<size_t>(gw) * gstride));
       for (int gl = 0; gl < nw; ++gl) {
-        uint32_t wc[4];
-        float sc[4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          wc[cb] = wn[cb];
-          sc[cb] = sn[cb];
-        }
+        const u32x4 wc = wn;
+        const f32x4 sc = sn;
         if (gl + 1 < nw) {
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            wn[cb] = __builtin_nontemporal_load(wp[cb] + static_cast<size_t>(gw + gl + 1) * gstride_w);
-            sn[cb] = __builtin_nontemporal_load(sp[cb] + static_cast<size_t>(gw + gl + 1) * gstride_s);
-          }
+          wn = __builtin_nontemporal_load(wp + static_cast<size_t>(gw + gl + 1) * gstride);
+          sn = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4*>(sp + static_cast<size_t>(gw + gl + 1) * gstride));
         }
         half8 bq[4];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) bq[cb] = codes_f16(wc[cb]);
+        for (int cb = 0; cb < 4; ++cb) bq[cb] = codes_f16(wc[cb], magic);
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
           half8 af[P];
@@ -270,21 +234,26 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(const MfmaArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rb * 16 + 4 * kb + i;
-      if (r >= nrows) continue;
-      const size_t prow = static_cast<size_t>(pos0 + r);
-      const float f = a.rs[prow];
+      const bool live = r < nrows;
+      const size_t prow = static_cast<size_t>(pos0 + (live ? r : 0));
+      const float f = live ? a.rs[prow] : 0.0f;
       if (a.mode == 0) {
+        if (live) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) a.out[prow * a.N + ncol[cb]] = acc[rb][cb][i] * f;
+          for (int cb = 0; cb < 4; ++cb) a.out[prow * a.N + col0 + cb] = acc[rb][cb][i] * f;
+        }
       } else {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          const float h = silu(acc[rb][cb][i] * f) * (acc[rb][cb + 2][i] * f);
-          const size_t hi = prow * a.N + ncol[cb];
-          if (a.h_bf16)
-            static_cast<uint16_t*>(a.h)[hi] = f32_to_bf16(h);
-          else
-            static_cast<float*>(a.h)[hi] = h;
+        for (int cb = 0; cb < 4; ++cb) {
+          const float up = __shfl_xor(acc[rb][cb][i], 8);  // every lane takes part
+          if (live && lc < 8) {
+            const float h = silu(acc[rb][cb][i] * f) * (up * f);
+            const size_t hi = prow * a.N + col0 + cb;
+            if (a.h_bf16)
+              static_cast<uint16_t*>(a.h)[hi] = f32_to_bf16(h);
+            else
+              static_cast<float*>(a.h)[hi] = h;
+          }
         }
       }
     }

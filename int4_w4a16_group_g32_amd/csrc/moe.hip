@@ -171,18 +171,17 @@ w4a16_status_t launch_route(const int32_t* ids, int M, int top_k, int E, int32_t
 }
 
 struct MoePlan {
-  int D = 0, P = 0, Mp = 0;
+  int P = 0, Mp = 0;
   size_t pairs = 0, max_items = 0, max_mitems = 0;
   size_t counts_off, offsets_off, sorted_off, inv_off, items_off, mitems_off, nitems_off, heavy_off;
-  size_t hq_off, hf_off, o_off;
-  size_t apx_off, rsx_off, h_off, aph_off, rsh_off;
+  size_t h_off, o_off;
+  size_t apx_off, rsx_off, aph_off, rsh_off;
   bool mfma = false;  // some expert can have more than kMaxGemvRows rows
   size_t bytes = 0;
 };
 
 MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate) {
   MoePlan p;
-  p.D = digits_for(xt);
   p.P = mfma_pieces(xt);
   const int E = gate->num_experts, H = gate->K, I = gate->N;
   p.pairs = static_cast<size_t>(M) * top_k;
@@ -201,12 +200,10 @@ MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate)
   c.take(p.mitems_off, std::max<size_t>(p.max_mitems, 1) * 16);
   c.take(p.nitems_off, 16);
   c.take(p.heavy_off, p.pairs * 4);
-  c.take(p.hq_off, p.pairs * (I / kGroup) * 4 * p.D * 4);
-  c.take(p.hf_off, p.pairs * (I / kGroup) * 4);
+  c.take(p.h_off, std::max<size_t>(p.pairs, p.Mp) * I * 4);
   c.take(p.o_off, p.pairs * H * 4);
   c.take(p.apx_off, static_cast<size_t>(p.P) * p.Mp * H * 2);
   c.take(p.rsx_off, static_cast<size_t>(p.Mp) * 4);
-  c.take(p.h_off, static_cast<size_t>(p.Mp) * I * 4);
   c.take(p.aph_off, static_cast<size_t>(p.P) * p.Mp * I * 2);
   c.take(p.rsh_off, static_cast<size_t>(p.Mp) * 4);
   p.bytes = c.cursor;
@@ -287,8 +284,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   int4* mitems = reinterpret_cast<int4*>(b + p.mitems_off);
   int32_t* n_items = reinterpret_cast<int32_t*>(b + p.nitems_off);
   int32_t* heavy = reinterpret_cast<int32_t*>(b + p.heavy_off);
-  int32_t* hq = reinterpret_cast<int32_t*>(b + p.hq_off);
-  float* hf = reinterpret_cast<float*>(b + p.hf_off);
+  float* hraw = reinterpret_cast<float*>(b + p.h_off);
   float* o = reinterpret_cast<float*>(b + p.o_off);
   const int R = static_cast<int>(p.pairs);
 
@@ -301,34 +297,31 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   // 2. gate/up with the SwiGLU epilogue: light experts on the GEMV, heavy on MFMA tiles
   GemvArgs a{};
   a.x = x;
+  a.x_bf16 = xt == W4A16_BF16 ? 1 : 0;
   a.gather = sorted;
   a.top_k = top_k;
   a.G = H / kGroup;
   a.K = H;
-  a.R = R;
   a.qw0 = reinterpret_cast<const u32x4*>(gate->qw);
   a.sc0 = gate->scales;
   a.qw1 = reinterpret_cast<const u32x4*>(up->qw);
   a.sc1 = up->scales;
   a.expert_stride = static_cast<size_t>(H / kGroup) * I;
   a.N = I;
-  const GemvShape gu = gemv_shape(p.max_items, I, 1, H / kGroup, 0);
-  a.tiles = gu.tiles;
+  a.tiles = gemv_shape(p.max_items, I, 1, H / kGroup, 0).tiles;
   a.S = 1;
   a.gps = a.G;
   a.dense_rows = 0;
   a.items = items;
   a.n_items = n_items;
   a.mode = 1;
-  a.hq = hq;
-  a.hf = hf;
+  a.h = hraw;
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(a, p.D, gu.sub, xt == W4A16_F32 ? kInF32 : kInBF16, p.max_items * a.tiles, stream);
+  st = launch_gemv(a, p.max_items * a.tiles, stream);
   if (st != W4A16_OK) return st;
 
   _Float16* apx = reinterpret_cast<_Float16*>(b + p.apx_off);
   float* rsx = reinterpret_cast<float*>(b + p.rsx_off);
-  float* hraw = reinterpret_cast<float*>(b + p.h_off);
   _Float16* aph = reinterpret_cast<_Float16*>(b + p.aph_off);
   float* rsh = reinterpret_cast<float*>(b + p.rsh_off);
   MfmaArgs ma{};
@@ -363,17 +356,15 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
 
   // 3. down projection into per-pair outputs
   GemvArgs d{};
-  d.xq = hq;
-  d.xf = hf;
+  d.x = hraw;
+  d.x_bf16 = 0;
   d.G = I / kGroup;
   d.K = I;
-  d.R = R;
   d.qw0 = reinterpret_cast<const u32x4*>(down->qw);
   d.sc0 = down->scales;
   d.expert_stride = static_cast<size_t>(I / kGroup) * H;
   d.N = H;
-  const GemvShape dn = gemv_shape(p.max_items, H, 0, I / kGroup, 0);
-  d.tiles = dn.tiles;
+  d.tiles = gemv_shape(p.max_items, H, 0, I / kGroup, 0).tiles;
   d.S = 1;
   d.gps = d.G;
   d.dense_rows = 0;
@@ -382,7 +373,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   d.mode = 0;
   d.out = o;
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(d, p.D, dn.sub, kInDigits, p.max_items * d.tiles, stream);
+  st = launch_gemv(d, p.max_items * d.tiles, stream);
   if (st != W4A16_OK) return st;
   if (p.mfma) {
     if ((st = ev.mark(stream)) != W4A16_OK) return st;

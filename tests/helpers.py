@@ -53,3 +53,22 @@ def x_values(x: torch.Tensor) -> np.ndarray:
 
 def rel_err(y_gpu: torch.Tensor, y_ref: np.ndarray) -> float:
     return O.rel_frobenius(y_gpu.detach().cpu().numpy().astype(np.float64), y_ref)
+
+
+def grouped_words(qw_canon: np.ndarray) -> np.ndarray:
+    """The GROUPED layout of canonical codes qw[E][K/8][N], as the header
+    describes it: for group g and 64-column block j, 16-byte slot 16b + l holds
+    canonical word 4g + b of columns 64j + 4l .. 64j + 4l + 3.  Returns
+    [E][K/32][N/64][64][4] int32."""
+    E, W, N = qw_canon.shape
+    G = W // 4
+    v = qw_canon.reshape(E, G, 4, N // 64, 16, 4)          # e, g, b, j, l, c
+    return np.ascontiguousarray(v.transpose(0, 1, 3, 2, 4, 5)).reshape(E, G, N // 64, 64, 4)
+
+
+def canonical_words(qw_grouped: np.ndarray, K: int, N: int) -> np.ndarray:
+    """Inverse of grouped_words: canonical qw[E][K/8][N] from GROUPED words."""
+    E = qw_grouped.size // (K * N // 8)
+    v = qw_grouped.reshape(E, K // 32, N // 64, 4, 16, 4)  # e, g, j, b, l, c
+    return np.ascontiguousarray(v.transpose(0, 1, 3, 2, 4, 5)).reshape(E, K // 8, N)
+

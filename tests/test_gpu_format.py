@@ -7,7 +7,7 @@ import torch
 import int4_w4a16_group_g32_amd as L
 import oracle as O
 import workloads as W
-from helpers import to_dev, weight_from_codes
+from helpers import canonical_words, grouped_words, to_dev, weight_from_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -49,15 +49,16 @@ def test_quantize_half_way_ties_and_stack():
         assert np.array_equal(qw[e], qo) and np.array_equal(sc[e], so)
 
 
-def test_prepack_is_group_chunk_permutation():
+def test_prepack_is_the_grouped_slot_permutation():
     rng = np.random.default_rng(9)
-    E, K, N = 3, 256, 128
+    E, K, N = 3, 256, 192
     qw = rng.integers(-(2 ** 31), 2 ** 31, size=(E, K // 8, N), dtype=np.int64).astype(np.int32)
     sc = rng.random((E, K // 32, N)).astype(np.float32)
     w = weight_from_codes(qw, sc)
-    got = w.qw.cpu().numpy().reshape(E, K // 32, N, 4)
-    want = qw.reshape(E, K // 32, 4, N).transpose(0, 1, 3, 2)
-    assert w.layout == L.LAYOUT_GROUPED and np.array_equal(got, want)
+    got = w.qw.cpu().numpy()
+    assert w.layout == L.LAYOUT_GROUPED and got.size == qw.size
+    assert np.array_equal(got.reshape(E, K // 32, N // 64, 64, 4), grouped_words(qw))
+    assert np.array_equal(canonical_words(got, K, N), qw)
 
 
 @pytest.mark.parametrize("grouped", [False, True])

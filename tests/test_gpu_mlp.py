@@ -9,7 +9,7 @@ import torch
 import int4_w4a16_group_g32_amd as L
 import oracle as O
 import workloads as W
-from helpers import rel_err, tol_for, weight_from_codes, x_for_dtype, x_values
+from helpers import canonical_words, rel_err, tol_for, weight_from_codes, x_for_dtype, x_values
 
 pytestmark = pytest.mark.gpu
 
@@ -78,6 +78,5 @@ def test_mlp_full_size(dense_mlp, name, dtype):
     print(f"{name} relF={err:.3e} (512 sampled columns)", flush=True)
     assert err <= tol_for(dtype)
     # the library's quantization of the same weights agrees with the oracle's
-    qd = d.qw.cpu().numpy().reshape(I // 32, H, 4)[:, cols, :]
-    qo = _sampled_down(w_down, cols)[0].reshape(I // 32, 4, len(cols)).transpose(0, 2, 1)
-    assert np.array_equal(qd, qo)
+    qd = canonical_words(d.qw.cpu().numpy(), I, H)[0][:, cols]
+    assert np.array_equal(qd, _sampled_down(w_down, cols)[0])
