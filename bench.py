@@ -8,9 +8,10 @@ library, and several copies are rotated across steps so the 256 MB Infinity
 Cache cannot serve them.  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line with the step throughput (algorithmic HBM bytes per
-second), the roofline of the dominant kernel (fused gate/up GEMV, timed live
-with HIP events recorded by the library between its kernels) and the CPU
-oracle timed on a bounded sample of the same workload.
+second over a timed region of plain calls), the roofline of the dominant
+kernel (fused gate/up GEMV, timed live in a second pass with HIP events the
+library records between its kernels) and the CPU oracle timed on a bounded
+sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20]
 """
@@ -146,19 +147,8 @@ def run_mlp(args, cfg):
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    evs = [_events(nev) for _ in range(args.steps)]
-    handles = [_handles(e) for e in evs]
-    t0, t1 = _events(2)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        step(i, handles[i])
-    t1.record()
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms_step = total_ms / args.steps
-    kern = {n: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    ms_step = timed_steps_ms(args, lambda i: step(i))
+    kern, ms_marked = per_kernel_ms(args, names, lambda i, h: step(i, h))
     k_gu = kern["gate_up"]
     step_bytes = mlp_bytes(M, H, I, xbytes)
     gu_bytes = gate_up_bytes(M, H, I, xbytes)
@@ -186,6 +176,7 @@ def run_mlp(args, cfg):
                      "traffic": stored_traffic(cfg.name, "gate_up") if M <= 8 else None,
                      "bytes_per_launch": gu_bytes, "avg_launch_us": round(k_gu * 1e3, 2)},
         "kernels_us": {n: round(v * 1e3, 2) for n, v in kern.items()},
+        "ms_per_step_marked": round(ms_marked, 5),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
     }
     if not args.no_cpu_baseline:
@@ -239,18 +230,8 @@ def run_moe(args, cfg):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [_events(nev) for _ in range(args.steps)]
-    handles = [_handles(e) for e in evs]
-    t0, t1 = _events(2)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        step(handles[i])
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    kern = {n: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    ms_step = timed_steps_ms(args, lambda i: step())
+    kern, ms_marked = per_kernel_ms(args, names, lambda i, h: step(h))
     active = int((np.bincount(ids_np.ravel(), minlength=E) > 0).sum())
     step_bytes = active * 3 * H * I * 5 // 8 + M * H * xbytes + M * H * 4
     flops = 2 * 3 * H * I * M * k
@@ -263,8 +244,43 @@ def run_moe(args, cfg):
                    "routing": cfg.routing, "active_experts": active, "bytes_per_step": step_bytes},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "kernels_us": {n: round(v * 1e3, 2) for n, v in kern.items()},
+        "ms_per_step_marked": round(ms_marked, 5),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
     }
+
+
+def timed_steps_ms(args, step):
+    """The timed region: exactly args.steps plain steps between two events,
+    with a device synchronization on both sides."""
+    import torch
+    t0, t1 = _events(2)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / args.steps
+
+
+def per_kernel_ms(args, names, step):
+    """A second pass of args.steps steps through the *_timed entry point: the
+    library records an event before each of its kernels and one after the
+    last, on the stream the kernels run on.  Returns the mean milliseconds per
+    kernel (each interval also holds that kernel's dispatch gap) and the step
+    time of this pass (the marks themselves cost a few microseconds)."""
+    import torch
+    evs = [_events(len(names) + 1) for _ in range(args.steps)]
+    handles = [_handles(e) for e in evs]
+    t0, t1 = _events(2)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i, handles[i])
+    t1.record()
+    torch.cuda.synchronize()
+    kern = {n: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    return kern, t0.elapsed_time(t1) / args.steps
 
 
 def cpu_baseline_mlp(cfg, base, repeats=7):

@@ -24,12 +24,14 @@ MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt) {
   m.tiles = (N + per_tile - 1) / per_tile;
   m.tasks = m.items * m.tiles;
   const int G = K / kGroup;
-  // split K while the grid is below about two workgroups per CU, keeping the
-  // partial tiles' write + read traffic under a quarter of the weight bytes
-  int S = static_cast<int>(512 / m.tasks);
+  // split K until the grid fills the resident workgroups (two per CU with two
+  // activation pieces, four with one), keeping the partial tiles' write +
+  // read traffic under half the weight bytes
+  const int target = m.P == 2 ? 512 : 1024;
+  int S = static_cast<int>(target / m.tasks);
   const double wbytes_per_col = K * 0.625;
   const double part_per_col_per_split = 8.0 * static_cast<double>(m.items) * kMfmaRows;
-  const int s_traffic = static_cast<int>(0.25 * wbytes_per_col / part_per_col_per_split);
+  const int s_traffic = static_cast<int>(0.5 * wbytes_per_col / part_per_col_per_split);
   if (S > s_traffic) S = s_traffic;
   if (S > G / 4) S = G / 4;
   if (S > kMaxSplits) S = kMaxSplits;

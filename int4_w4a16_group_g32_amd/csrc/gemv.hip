@@ -271,10 +271,11 @@ void gemv_kernel(const GemvArgs a) {
   GroupCodes ring[kRing];
   float xv[kRowsPerWave][16];
   load_window(a, g_lo, min(kWin, g_hi - g_lo), pos0, nrows, wv, lane, xv);  // ahead of the weights
-  if (wave_ok) {
+  // A wave past the matrix's last column streams column block 0 and stores
+  // nothing: the ring loads stay unconditional, so the compiler's waits can
+  // count them.
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) load_group(wp, sp, gstride, g_lo + j, g_last, ring[j]);
-  }
+  for (int j = 0; j < kRing; ++j) load_group(wp, sp, gstride, g_lo + j, g_last, ring[j]);
 
   for (int gw = g_lo; gw < g_hi; gw += kWin) {
     const int nw = min(kWin, g_hi - gw);
@@ -284,7 +285,7 @@ void gemv_kernel(const GemvArgs a) {
     }
     convert_window(lds, nw, nrows, wv, lane, xv);
     __syncthreads();
-    if (wave_ok) {
+    {
       f32x4 wacc[4];
       f32x4* acc = kMulti ? wacc : tot;
       if (kMulti) {

@@ -18,20 +18,42 @@
 namespace w4 {
 namespace {
 
-constexpr int kGw = 4;       // groups per staged activation window
-constexpr int kRowPad = 40;  // halves per staged row of 32 (80-byte stride)
+constexpr int kGw = 4;           // groups per staged activation window (double-buffered)
+constexpr int kTileRing = 2 * kGw;  // groups of codes in flight per wave
+constexpr int kPrepThreads = 1024;
 
 // ------------------------------------------------------------ activation pieces
 
+template <typename XT>
+__device__ __forceinline__ void load8(const XT* xr, int b, float v[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float* xr, int b, float v[8]) {
+  const float4 u0 = reinterpret_cast<const float4*>(xr)[2 * b];
+  const float4 u1 = reinterpret_cast<const float4*>(xr)[2 * b + 1];
+  v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+  v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+}
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* xr, int b, float v[8]) {
+  const uint4 u = reinterpret_cast<const uint4*>(xr)[b];
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+
 // One workgroup per row.  Pass 1: the row's largest magnitude; pass 2: pieces
-// of x * 2^e, each block of 8 in the order 0,4,1,5,2,6,3,7.
+// of x * 2^e, each block of 8 in the order 0,4,1,5,2,6,3,7.  A thread takes
+// blocks of 8 consecutive activations (one or two 16-byte loads).
 template <typename XT, int P>
-__global__ __launch_bounds__(256) void mfma_prep_kernel(const XT* __restrict__ x, int R, int Mp,
-                                                        int K, const int* __restrict__ gather,
-                                                        int top_k, const int* __restrict__ need,
-                                                        _Float16* __restrict__ ap,
-                                                        float* __restrict__ rs) {
-  __shared__ float red[256];
+__global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const XT* __restrict__ x, int R, int Mp,
+                                                                 int K, const int* __restrict__ gather,
+                                                                 int top_k, const int* __restrict__ need,
+                                                                 _Float16* __restrict__ ap,
+                                                                 float* __restrict__ rs) {
+  __shared__ float red[kPrepThreads / kWave];
   const int row = blockIdx.x;
   if (need != nullptr && (row >= R || need[row] == 0)) return;
   long src = row < R ? row : -1;
@@ -40,31 +62,46 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const XT* __restrict__ x
     src = pr < 0 ? -1 : pr / top_k;
   }
   const XT* xr = x + (src < 0 ? 0 : src) * static_cast<size_t>(K);
+  const int nb = K / 8;
   float amax = 0.0f;
-  if (src >= 0)
-    for (int k = threadIdx.x; k < K; k += 256) amax = fmaxf(amax, fabsf(load_act(xr, k)));
-  red[threadIdx.x] = amax;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (static_cast<int>(threadIdx.x) < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
-    __syncthreads();
+  if (src >= 0) {
+    for (int b = threadIdx.x; b < nb; b += kPrepThreads) {
+      float v[8];
+      load8<XT>(xr, b, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
   }
-  amax = red[0];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if (lane_id() == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kPrepThreads / kWave; ++w) amax = fmaxf(amax, red[w]);
   int e = 0;
   if (amax > 0.0f) {
-    e = 14 - ilogbf(amax);
-    e = e > 100 ? 100 : (e < -100 ? -100 : e);
+    int lg = ilogbf(amax);
+    lg = lg > 120 ? 120 : (lg < -120 ? -120 : lg);
+    e = 14 - lg;
   }
   const float scale = (src >= 0 && amax > 0.0f) ? ldexpf(1.0f, e) : 0.0f;
   if (threadIdx.x == 0) rs[row] = scale > 0.0f ? ldexpf(1.0f, -e) : 0.0f;
-  for (int b = threadIdx.x; b < K / 8; b += 256) {
+  for (int b = threadIdx.x; b < nb; b += kPrepThreads) {
+    float v[8];
+    if (scale != 0.0f) {
+      load8<XT>(xr, b, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
     half8 h0, h1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float v = scale == 0.0f ? 0.0f : load_act(xr, 8 * b + kCodeOrder[i]) * scale;
-      const _Float16 hi = static_cast<_Float16>(v);
+      const float t = v[kCodeOrder[i]] * scale;
+      const _Float16 hi = static_cast<_Float16>(t);
       h0[i] = hi;
-      if (P == 2) h1[i] = static_cast<_Float16>(v - static_cast<float>(hi));
+      if (P == 2) h1[i] = static_cast<_Float16>(t - static_cast<float>(hi));
     }
     *reinterpret_cast<half8*>(ap + static_cast<size_t>(row) * K + 8 * b) = h0;
     if (P == 2) *reinterpret_cast<half8*>(ap + (static_cast<size_t>(Mp) + row) * K + 8 * b) = h1;
@@ -73,13 +110,87 @@ __global__ __launch_bounds__(256) void mfma_prep_kernel(const XT* __restrict__ x
 
 // ------------------------------------------------------------ the MFMA kernel
 
+// Activation window: 16-byte unit (p, gl, row, kb) at a_off(); k blocks are
+// XOR-swizzled by row so the 16 rows one ds_read_b128 touches fall in
+// distinct banks.
 template <int P>
-struct MfmaLds {
-  _Float16 a[P][kGw][kMfmaRows][kRowPad];
-};
+constexpr int kWinUnits = P * kGw * kMfmaRows * 4;
+
+__device__ __forceinline__ int a_off(int p, int gl, int row, int kb) {
+  return ((p * kGw + gl) * kMfmaRows + row) * 4 + (kb ^ ((row >> 2) & 3));
+}
 
 template <int P>
-__global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(const MfmaArgs a) {
+struct MfmaLds {
+  uint4 a[2][kWinUnits<P>];  // double buffer
+};
+
+// Thread t loads units t, t + 256, ...: unit u = ((p * 64 + row) * kGw + gl) * 4 + kb,
+// so 16 consecutive threads read one row's four groups (256 contiguous bytes).
+// Groups past the split's end are zero, so the tail needs no masking.  The
+// loads themselves are unconditional (clamped addresses): a load under a
+// branch makes the compiler's wait before the LDS store cover the code ring.
+template <int P>
+__device__ __forceinline__ void load_a_window(const MfmaArgs& a, int pos0, int gw, int g_hi,
+                                              uint4 r[kWinUnits<P> / kMfmaThreads]) {
+#pragma unroll
+  for (int i = 0; i < kWinUnits<P> / kMfmaThreads; ++i) {
+    const int u = static_cast<int>(threadIdx.x) + kMfmaThreads * i;
+    const int kb = u & 3, gl = (u >> 2) % kGw, row = (u >> 2) / kGw % kMfmaRows, p = (u >> 2) / kGw / kMfmaRows;
+    const int g = gw + gl;
+    const uint4 v = *reinterpret_cast<const uint4*>(a.ap + (static_cast<size_t>(p) * a.Mp + pos0 + row) * a.K +
+                                                    static_cast<size_t>(min(g, g_hi - 1)) * kGroup + 8 * kb);
+    r[i] = g < g_hi ? v : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void store_a_window(uint4* buf, const uint4 r[kWinUnits<P> / kMfmaThreads]) {
+#pragma unroll
+  for (int i = 0; i < kWinUnits<P> / kMfmaThreads; ++i) {
+    const int u = static_cast<int>(threadIdx.x) + kMfmaThreads * i;
+    const int kb = u & 3, gl = (u >> 2) % kGw, row = (u >> 2) / kGw % kMfmaRows, p = (u >> 2) / kGw / kMfmaRows;
+    buf[a_off(p, gl, row, kb)] = r[i];
+  }
+}
+
+struct TileCodes {
+  u32x4 w;  // word kb of the lane's four columns
+  f32x4 s;  // their scales
+};
+
+__device__ __forceinline__ void load_tile_codes(const u32x4* wp, const float* sp, size_t gstride, int g,
+                                                int g_last, TileCodes& c) {
+  const size_t gg = static_cast<size_t>(min(g, g_last));
+  c.w = __builtin_nontemporal_load(wp + gg * gstride);
+  c.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + gg * gstride));
+}
+
+// One group of the tile: 4 row blocks x 4 column blocks, both pieces.
+template <int P>
+__device__ __forceinline__ void mma_tile_group(const uint4* buf, int gl, int lc, int kb, uint32_t magic,
+                                               const TileCodes& c, f32x4 acc[4][4]) {
+  half8 bq[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) bq[cb] = codes_f16(c.w[cb], magic);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    half8 af[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) af[p] = __builtin_bit_cast(half8, buf[a_off(p, gl, rb * 16 + lc, kb)]);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[0], bq[cb], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      if (P == 2) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[1], bq[cb], d, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(c.s[cb], d[i], acc[rb][cb][i]);
+    }
+  }
+}
+
+template <int P>
+__global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void mfma_kernel(const MfmaArgs a) {
   __shared__ MfmaLds<P> lds;
   __shared__ int last;
   const int task = blockIdx.x;
@@ -137,71 +248,55 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(const MfmaArgs a) {
 
   const int g_lo = split * a.gps;
   const int g_hi = min(a.G, g_lo + a.gps);
-  for (int gw = g_lo; gw < g_hi; gw += kGw) {
-    const int nw = min(kGw, g_hi - gw);
-    // stage the pieces of rows pos0..pos0+63, groups gw..gw+nw-1: 16-byte units
-    const int units = P * nw * kMfmaRows * 4;
-    for (int u = threadIdx.x; u < units; u += kMfmaThreads) {
-      const int q4 = u & 3;
-      const int r = (u >> 2) % kMfmaRows;
-      const int gl = (u >> 2) / kMfmaRows % nw;
-      const int p = (u >> 2) / kMfmaRows / nw;
-      const half8 v = *reinterpret_cast<const half8*>(
-          a.ap + (static_cast<size_t>(p) * a.Mp + pos0 + r) * a.K + static_cast<size_t>(gw + gl) * kGroup + 8 * q4);
-      *reinterpret_cast<half8*>(&lds.a[p][gl][r][8 * q4]) = v;
-    }
-    __syncthreads();
-    if (wave_ok) {
-      u32x4 wn = __builtin_nontemporal_load(wp + static_cast<size_t>(gw) * gstride);
-      f32x4 sn = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + static_cast<size_t>(gw) * gstride));
-      for (int gl = 0; gl < nw; ++gl) {
-        const u32x4 wc = wn;
-        const f32x4 sc = sn;
-        if (gl + 1 < nw) {
-          wn = __builtin_nontemporal_load(wp + static_cast<size_t>(gw + gl + 1) * gstride);
-          sn = __builtin_nontemporal_load(
-              reinterpret_cast<const f32x4*>(sp + static_cast<size_t>(gw + gl + 1) * gstride));
+  const int g_last = g_hi - 1;
+  const int nwin = (g_hi - g_lo + kGw - 1) / kGw;
+  uint4 ra[kWinUnits<P> / kMfmaThreads];
+  // ring of kTileRing groups of codes in flight: group g_lo + i sits in slot
+  // i % kTileRing, two windows' worth, so a window always uses the same half
+  TileCodes ring[kTileRing];
+  // A wave past the matrix's last column streams column block 0 and stores
+  // nothing, so every load below is unconditional.
+  load_a_window<P>(a, pos0, g_lo, g_hi, ra);
+#pragma unroll
+  for (int j = 0; j < kTileRing; ++j) load_tile_codes(wp, sp, gstride, g_lo + j, g_last, ring[j]);
+  store_a_window<P>(lds.a[0], ra);
+  __syncthreads();
+  for (int w = 0; w < nwin; w += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // window w + h, LDS buffer h, ring slots kGw*h ..
+      if (w + h < nwin) {
+        const int gw = g_lo + (w + h) * kGw;
+        load_a_window<P>(a, pos0, gw + kGw, g_hi, ra);  // the next window, in flight (zeros past the end)
+#pragma unroll
+        for (int j = 0; j < kGw; ++j) {
+          mma_tile_group<P>(lds.a[h], j, lc, kb, magic, ring[kGw * h + j], acc);
+          load_tile_codes(wp, sp, gstride, gw + j + kTileRing, g_last, ring[kGw * h + j]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        half8 bq[4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) bq[cb] = codes_f16(wc[cb], magic);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          half8 af[P];
-#pragma unroll
-          for (int p = 0; p < P; ++p)
-            af[p] = *reinterpret_cast<const half8*>(&lds.a[p][gl][rb * 16 + lc][8 * kb]);
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[0], bq[cb], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            if (P == 2) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[1], bq[cb], d, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(sc[cb], d[i], acc[rb][cb][i]);
-          }
-        }
+        store_a_window<P>(lds.a[1 - h], ra);
+        __syncthreads();
       }
     }
-    __syncthreads();
   }
 
-  // split-K: write-through partials, agent-scope arrival counter, the last
-  // workgroup sums the partials in split order (see the GEMV kernel)
+  // Split-K: write-through partials, an agent-scope arrival counter, and the
+  // last workgroup sums the partials in split order (the GEMV kernel's
+  // scheme).  A partial tile is stored element-major, [j][thread] with
+  // j = (rb * 4 + cb) * 4 + i, so every store and load instruction covers 256
+  // contiguous bytes, and the readback keeps two splits' worth (128 loads per
+  // thread) in flight at a time.
   if (a.S > 1) {
     const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
     const size_t tf = static_cast<size_t>(kMfmaRows) * kMfmaCols;
-    float* base = a.partials + ct * a.S * tf;
-    if (wave_ok) {
+    float* base = a.partials + ct * a.S * tf + threadIdx.x;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = rb * 16 + 4 * kb + i;
-            __hip_atomic_store(base + split * tf + r * kMfmaCols + wv * 64 + cb * 16 + lc, acc[rb][cb][i],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-    }
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kMfmaThreads, acc[rb][cb][i],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0)
@@ -209,20 +304,30 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_kernel(const MfmaArgs a) {
               a.S - 1);
     __syncthreads();
     if (!last) return;
-    if (wave_ok) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < a.S; s0 += 2) {
+      float p[2][64];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = rb * 16 + 4 * kb + i;
-            const float* pp = base + r * kMfmaCols + wv * 64 + cb * 16 + lc;
-            float t = 0.0f;
-            for (int s2 = 0; s2 < a.S; ++s2)
-              t += __hip_atomic_load(pp + s2 * tf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            acc[rb][cb][i] = t;
-          }
+      for (int b = 0; b < 2; ++b) {
+        const float* ps = base + static_cast<size_t>(min(s0 + b, a.S - 1)) * tf;
+#pragma unroll
+        for (int e = 0; e < 64; ++e)
+          p[b][e] = __hip_atomic_load(ps + e * kMfmaThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        if (s0 + b < a.S) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[rb][cb][i] += p[b][(rb * 4 + cb) * 4 + i];
+        }
+      }
     }
     if (threadIdx.x == 0)
       __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -266,16 +371,16 @@ w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, 
                                 float* rs, hipStream_t stream) {
   if (Mp == 0) return W4A16_OK;
   if (xt == W4A16_F32 && P == 2)
-    mfma_prep_kernel<float, 2><<<Mp, 256, 0, stream>>>(static_cast<const float*>(x), R, Mp, K, gather,
+    mfma_prep_kernel<float, 2><<<Mp, kPrepThreads, 0, stream>>>(static_cast<const float*>(x), R, Mp, K, gather,
                                                        top_k, need, ap, rs);
   else if (xt == W4A16_F32)
-    mfma_prep_kernel<float, 1><<<Mp, 256, 0, stream>>>(static_cast<const float*>(x), R, Mp, K, gather,
+    mfma_prep_kernel<float, 1><<<Mp, kPrepThreads, 0, stream>>>(static_cast<const float*>(x), R, Mp, K, gather,
                                                        top_k, need, ap, rs);
   else if (P == 2)
-    mfma_prep_kernel<uint16_t, 2><<<Mp, 256, 0, stream>>>(static_cast<const uint16_t*>(x), R, Mp, K,
+    mfma_prep_kernel<uint16_t, 2><<<Mp, kPrepThreads, 0, stream>>>(static_cast<const uint16_t*>(x), R, Mp, K,
                                                           gather, top_k, need, ap, rs);
   else
-    mfma_prep_kernel<uint16_t, 1><<<Mp, 256, 0, stream>>>(static_cast<const uint16_t*>(x), R, Mp, K,
+    mfma_prep_kernel<uint16_t, 1><<<Mp, kPrepThreads, 0, stream>>>(static_cast<const uint16_t*>(x), R, Mp, K,
                                                           gather, top_k, need, ap, rs);
   return launch_status();
 }
