@@ -31,7 +31,10 @@ namespace w4 {
 namespace {
 
 constexpr int kWin = 32;                 // groups per staging window
-constexpr int kRing = 4;                 // groups of codes in flight per wave
+#ifndef W4_GEMV_RING
+#define W4_GEMV_RING 4
+#endif
+constexpr int kRing = W4_GEMV_RING;       // groups of codes in flight per wave
 constexpr int kUnitsPerGroup = 16 * 4;   // 16-byte units of one group's A (16 rows x 4 k blocks)
 
 struct GemvLds {
@@ -409,6 +412,11 @@ GemvShape gemv_shape(size_t items, int N, int mode, int G, size_t max_split_task
   sh.tiles = (N + per_tile - 1) / per_tile;
   const size_t tasks = items * static_cast<size_t>(sh.tiles);
   int S = tasks > 0 ? static_cast<int>(W4_GEMV_TARGET_WGS / tasks) : 1;
+  // no more splits than it takes to give each one a full staging window:
+  // shorter splits add fixed per-workgroup cost (staging, split-K tail)
+  // without adding bandwidth
+  const int s_window = (G + kWin - 1) / kWin;
+  if (S > s_window) S = s_window;
   int max_s = G / W4_GEMV_MIN_GROUPS_PER_SPLIT;
   if (max_s > kMaxSplits) max_s = kMaxSplits;
   if (S > max_s) S = max_s;
