@@ -1,5 +1,8 @@
 // Host entry points: argument checks, workspace layout and kernel dispatch for
 // the dense GEMM and the dense SwiGLU MLP.
+#include <algorithm>
+#include <cmath>
+
 #include "dispatch.h"
 
 namespace w4 {
@@ -24,19 +27,28 @@ MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt) {
   m.tiles = (N + per_tile - 1) / per_tile;
   m.tasks = m.items * m.tiles;
   const int G = K / kGroup;
-  // split K until the grid fills the resident workgroups (two per CU with two
-  // activation pieces, four with one), keeping the partial tiles' write +
-  // read traffic under half the weight bytes
-  const int target = m.P == 2 ? 512 : 1024;
-  int S = static_cast<int>(target / m.tasks);
+  // Split K to balance the grid over the resident workgroups: the kernel holds
+  // two workgroups per CU (its registers allow two waves per SIMD), 512 on
+  // the chip, and every workgroup of a launch streams the same number of
+  // groups, so a launch takes about ceil(tasks * S / 512) rounds of
+  // (G / S + a fixed per-workgroup cost) group steps.  The partial tiles'
+  // write + read traffic stays under half the weight bytes.
   const double wbytes_per_col = K * 0.625;
   const double part_per_col_per_split = 8.0 * static_cast<double>(m.items) * kMfmaRows;
-  const int s_traffic = static_cast<int>(0.5 * wbytes_per_col / part_per_col_per_split);
-  if (S > s_traffic) S = s_traffic;
-  if (S > G / 4) S = G / 4;
-  if (S > kMaxSplits) S = kMaxSplits;
-  if (m.tasks * S * sizeof(int) > kCounterBytes) S = 1;
-  if (S < 1) S = 1;
+  int s_max = static_cast<int>(W4_MFMA_PARTIAL_CAP * wbytes_per_col / part_per_col_per_split);
+  if (s_max > G / 4) s_max = G / 4;
+  if (s_max > kMaxSplits) s_max = kMaxSplits;
+  while (s_max > 1 && m.tasks * s_max * sizeof(int) > kCounterBytes) --s_max;
+  int S = 1;
+  double best = 0.0;
+  for (int s = 1; s <= std::max(s_max, 1); ++s) {
+    const double rounds = std::ceil(static_cast<double>(m.tasks) * s / kMfmaResidentWgs);
+    const double cost = rounds * ((G + s - 1) / s + kMfmaWgOverheadGroups);
+    if (s == 1 || cost < best) {
+      best = cost;
+      S = s;
+    }
+  }
   m.S = S;
   m.gps = (G + S - 1) / S;
   return m;

@@ -17,6 +17,17 @@ inline int mfma_pieces(w4a16_dtype_t xt) { return xt == W4A16_F32 ? 2 : 1; }
 constexpr int kMfmaRows = 64;     // rows per tile
 constexpr int kMfmaCols = 256;    // weight columns per tile (4 waves x 4 blocks of 16)
 constexpr int kMfmaThreads = 256;
+// Workgroups of the tile kernel resident at once (two per CU on 256 CUs) and
+// the fixed cost of one workgroup (staging, split-K tail, epilogue) in units
+// of one group step; the split planner balances launches with them.
+#ifndef W4_MFMA_WG_OVERHEAD_GROUPS
+#define W4_MFMA_WG_OVERHEAD_GROUPS 4
+#endif
+#ifndef W4_MFMA_PARTIAL_CAP
+#define W4_MFMA_PARTIAL_CAP 0.5  // partial-tile traffic cap, a fraction of the weight bytes
+#endif
+constexpr int kMfmaResidentWgs = 512;
+constexpr int kMfmaWgOverheadGroups = W4_MFMA_WG_OVERHEAD_GROUPS;
 
 struct MfmaArgs {
   const _Float16* ap;  // [P][Mp][K]

@@ -12,6 +12,8 @@
 // waves, each of which streams its own 64 columns of codes: one 16-byte
 // GROUPED slot per lane and group (a contiguous kilobyte per wave load), whose
 // four words are column lc of the four MFMA blocks.
+#include <type_traits>
+
 #include "mfma.h"
 #include "mfma_ops.h"
 
@@ -127,9 +129,10 @@ struct MfmaLds {
 
 // Thread t loads units t, t + 256, ...: unit u = ((p * 64 + row) * kGw + gl) * 4 + kb,
 // so 16 consecutive threads read one row's four groups (256 contiguous bytes).
-// Groups past the split's end are zero, so the tail needs no masking.  The
-// loads themselves are unconditional (clamped addresses): a load under a
-// branch makes the compiler's wait before the LDS store cover the code ring.
+// The loads are unconditional (clamped addresses); groups past the split's
+// end are zeroed when the window is stored, so the tail needs no masking.  A
+// load under a branch, or a use of its value before the window's groups are
+// done, would make the compiler's wait cover the code ring as well.
 template <int P>
 __device__ __forceinline__ void load_a_window(const MfmaArgs& a, int pos0, int gw, int g_hi,
                                               uint4 r[kWinUnits<P> / kMfmaThreads]) {
@@ -137,20 +140,19 @@ __device__ __forceinline__ void load_a_window(const MfmaArgs& a, int pos0, int g
   for (int i = 0; i < kWinUnits<P> / kMfmaThreads; ++i) {
     const int u = static_cast<int>(threadIdx.x) + kMfmaThreads * i;
     const int kb = u & 3, gl = (u >> 2) % kGw, row = (u >> 2) / kGw % kMfmaRows, p = (u >> 2) / kGw / kMfmaRows;
-    const int g = gw + gl;
-    const uint4 v = *reinterpret_cast<const uint4*>(a.ap + (static_cast<size_t>(p) * a.Mp + pos0 + row) * a.K +
-                                                    static_cast<size_t>(min(g, g_hi - 1)) * kGroup + 8 * kb);
-    r[i] = g < g_hi ? v : make_uint4(0, 0, 0, 0);
+    r[i] = *reinterpret_cast<const uint4*>(a.ap + (static_cast<size_t>(p) * a.Mp + pos0 + row) * a.K +
+                                           static_cast<size_t>(min(gw + gl, g_hi - 1)) * kGroup + 8 * kb);
   }
 }
 
 template <int P>
-__device__ __forceinline__ void store_a_window(uint4* buf, const uint4 r[kWinUnits<P> / kMfmaThreads]) {
+__device__ __forceinline__ void store_a_window(uint4* buf, int gw, int g_hi,
+                                               const uint4 r[kWinUnits<P> / kMfmaThreads]) {
 #pragma unroll
   for (int i = 0; i < kWinUnits<P> / kMfmaThreads; ++i) {
     const int u = static_cast<int>(threadIdx.x) + kMfmaThreads * i;
     const int kb = u & 3, gl = (u >> 2) % kGw, row = (u >> 2) / kGw % kMfmaRows, p = (u >> 2) / kGw / kMfmaRows;
-    buf[a_off(p, gl, row, kb)] = r[i];
+    buf[a_off(p, gl, row, kb)] = gw + gl < g_hi ? r[i] : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -166,24 +168,81 @@ __device__ __forceinline__ void load_tile_codes(const u32x4* wp, const float* sp
   c.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + gg * gstride));
 }
 
-// One group of the tile: 4 row blocks x 4 column blocks, both pieces.
+// One group of the tile: the live row blocks (nrb of 4, wave-uniform) x 4
+// column blocks.
+//
+// Two pieces (float32 activations): B holds the exact codes and each group's
+// 16x16 result is scaled by s[g][n] on the float32 accumulators, so the scale
+// is applied exactly once, in float32.
+//
+// One piece (bf16 activations): the scale is folded into B, which holds
+// f16(q * f16(s * 2^c)) for a per-lane, per-column-block power of two 2^c
+// (the lanes that share a column see the same scales and so keep the same
+// c), and the MFMA accumulates straight into the accumulators; the epilogue
+// multiplies by 2^-c.  c starts so that the largest scale of the split's first
+// kTileRing groups lands in [1/2, 1) (2^138 if they are all zero); a later
+// group whose scaled value would reach 2^12 (where q * s could leave the f16
+// range) moves c to bring it to [1/2, 1) and rescales that column block's
+// accumulators by the same power of two, so no product overflows.  Each
+// weight is then rounded twice in f16 (about 2^-11 relative each); a group
+// whose scale lies more than 2^14 below the anchor keeps an absolute precision
+// of about 2^-25 of the anchor instead, and float32 scales below the normal
+// range (2^-126) are carried with reduced precision.
 template <int P>
 __device__ __forceinline__ void mma_tile_group(const uint4* buf, int gl, int lc, int kb, uint32_t magic,
-                                               const TileCodes& c, f32x4 acc[4][4]) {
+                                               const TileCodes& c, int nrb, int cexp[4], f32x4 acc[4][4]) {
   half8 bq[4];
+  if (P == 1) {
+    f32x4 sp;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) bq[cb] = codes_f16(c.w[cb], magic);
+    for (int cb = 0; cb < 4; ++cb) sp[cb] = ldexpf(c.s[cb], cexp[cb]);
+    const float m = fmaxf(fmaxf(fabsf(sp[0]), fabsf(sp[1])), fmaxf(fabsf(sp[2]), fabsf(sp[3])));
+    if (__builtin_amdgcn_ballot_w64(m >= 4096.0f) != 0) {  // rare: re-anchor
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    half8 af[P];
+      for (int cb = 0; cb < 4; ++cb) {
+        // from the raw scale, so a scaled value that overflowed to inf still
+        // gets its anchor
+        const bool move = fabsf(sp[cb]) >= 4096.0f;
+        const int cn = move ? -__builtin_amdgcn_frexp_expf(c.s[cb]) : cexp[cb];
+        const int d = cexp[cb] - cn;
+        cexp[cb] = cn;
+        sp[cb] = ldexpf(c.s[cb], cn);
 #pragma unroll
-    for (int p = 0; p < P; ++p) af[p] = __builtin_bit_cast(half8, buf[a_off(p, gl, rb * 16 + lc, kb)]);
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = ldexpf(acc[rb][cb][i], -d);
+      }
+    }
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[0], bq[cb], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-      if (P == 2) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[1], bq[cb], d, 0, 0, 0);
+      const _Float16 h = static_cast<_Float16>(sp[cb]);
+      bq[cb] = codes_f16(c.w[cb], magic) * half8{h, h, h, h, h, h, h, h};
+    }
+  } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(c.s[cb], d[i], acc[rb][cb][i]);
+    for (int cb = 0; cb < 4; ++cb) bq[cb] = codes_f16(c.w[cb], magic);
+  }
+  // all row blocks' fragments are read (the window holds 64 rows), so one
+  // wait covers them; only the MFMAs of dead row blocks are skipped
+  half8 af[4][P];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int p = 0; p < P; ++p) af[rb][p] = __builtin_bit_cast(half8, buf[a_off(p, gl, rb * 16 + lc, kb)]);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    if (rb < nrb) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        if (P == 1) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[rb][0], bq[cb], acc[rb][cb], 0, 0, 0);
+        } else {
+          f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[rb][0], bq[cb], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[rb][P - 1], bq[cb], d, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(c.s[cb], d[i], acc[rb][cb][i]);
+        }
+      }
     }
   }
 }
@@ -258,25 +317,58 @@ void mfma_kernel(const MfmaArgs a) {
   // nothing, so every load below is unconditional.
   load_a_window<P>(a, pos0, g_lo, g_hi, ra);
 #pragma unroll
-  for (int j = 0; j < kTileRing; ++j) load_tile_codes(wp, sp, gstride, g_lo + j, g_last, ring[j]);
-  store_a_window<P>(lds.a[0], ra);
+  for (int j = 0; j < kTileRing; ++j) {
+    load_tile_codes(wp, sp, gstride, g_lo + j, g_last, ring[j]);
+    __builtin_amdgcn_sched_barrier(0);  // issue order = use order
+  }
+  // live 16-row blocks of the tile (items hold 1 .. 64 rows)
+  const int nrb = (nrows + 15) >> 4;
+  // one piece: the per-column-block anchors (see mma_tile_group)
+  int cexp[4] = {0, 0, 0, 0};
+  if (P == 1) {
+    f32x4 mx = ring[0].s;
+#pragma unroll
+    for (int j = 1; j < kTileRing; ++j)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) mx[cb] = fmaxf(fabsf(mx[cb]), fabsf(ring[j].s[cb]));
+    // an all-zero start takes the first nonzero group's anchor on arrival:
+    // 2^138 lifts every normal float32 scale to 2^12 or more
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) cexp[cb] = mx[cb] != 0.0f ? -__builtin_amdgcn_frexp_expf(fabsf(mx[cb])) : 138;
+  }
+  store_a_window<P>(lds.a[0], g_lo, g_hi, ra);
   __syncthreads();
-  for (int w = 0; w < nwin; w += 2) {
+  // Window wi uses LDS buffer and ring half h = wi % 2.  The loop body is two
+  // whole windows and an odd last window runs after it, so every path into
+  // the loop header has the same loads outstanding (with a conditional second
+  // window the compiler's waits would drain half the ring at every header).
+  auto window = [&](int wi, auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const int gw = g_lo + wi * kGw;
+    load_a_window<P>(a, pos0, gw + kGw, g_hi, ra);  // the next window, in flight
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {  // window w + h, LDS buffer h, ring slots kGw*h ..
-      if (w + h < nwin) {
-        const int gw = g_lo + (w + h) * kGw;
-        load_a_window<P>(a, pos0, gw + kGw, g_hi, ra);  // the next window, in flight (zeros past the end)
-#pragma unroll
-        for (int j = 0; j < kGw; ++j) {
-          mma_tile_group<P>(lds.a[h], j, lc, kb, magic, ring[kGw * h + j], acc);
-          load_tile_codes(wp, sp, gstride, gw + j + kTileRing, g_last, ring[kGw * h + j]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        store_a_window<P>(lds.a[1 - h], ra);
-        __syncthreads();
-      }
+    for (int j = 0; j < kGw; ++j) {
+      mma_tile_group<P>(lds.a[h], j, lc, kb, magic, ring[kGw * h + j], nrb, cexp, acc);
+      load_tile_codes(wp, sp, gstride, gw + j + kTileRing, g_last, ring[kGw * h + j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    store_a_window<P>(lds.a[1 - h], gw + kGw, g_hi, ra);
+    __syncthreads();
+  };
+  int w = 0;
+  for (; w + 1 < nwin; w += 2) {
+    window(w, std::integral_constant<int, 0>{});
+    window(w + 1, std::integral_constant<int, 1>{});
+  }
+  if (w < nwin) window(w, std::integral_constant<int, 0>{});
+
+  if (P == 1) {  // back to the scales' own units
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rb][cb][i] = ldexpf(acc[rb][cb][i], -cexp[cb]);
   }
 
   // Split-K: write-through partials, an agent-scope arrival counter, and the

@@ -95,3 +95,33 @@ def test_gemm_config_single_m1():
     err = rel_err(y, O.gemm64(x_values(x), qw, sc))
     print(f"gemm_m1 relF={err:.3e}", flush=True)
     assert err <= 1e-5
+
+
+def _wide_scales(K, N, seed, spread, base):
+    """Random codes and scales base * 2^u, u uniform in [-spread, spread] per
+    (group, column); a few whole groups are zero, and in one 16-column block
+    the first twelve groups are zero for every column."""
+    rng = np.random.default_rng(seed)
+    qw = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    sc = (base * np.exp2(rng.integers(-spread, spread + 1, size=(K // 32, N)))).astype(np.float32)
+    sc[rng.random(size=sc.shape) < 0.05] = 0.0
+    sc[:12, 16:32] = 0.0
+    return qw, sc
+
+
+@pytest.mark.parametrize("spread,base", [(0, 1e-30), (0, 1e30), (6, 1e-3), (20, 1.0), (40, 1.0)])
+@pytest.mark.parametrize("M", [17, 64, 130])
+def test_gemm_bf16_tiles_hold_any_scale_range(M, spread, base):
+    """bf16 activations on the MFMA tile path fold each group's scale into the
+    f16 weight operand relative to a per-column power-of-two anchor; scales
+    far outside the f16 range and columns whose scales span up to 2^80 still
+    meet the bf16 bound, and K splits combine partials of different anchors."""
+    K, N = 7168, 512
+    qw, sc = _wide_scales(K, N, 400 + M + spread, spread, base)
+    w = weight_from_codes(qw, sc)
+    x = x_for_dtype(W.activations(M, K, 401 + M).cuda(), "bf16")
+    y, _ = _run_gemm(x, w, N)
+    assert torch.isfinite(y).all()
+    err = rel_err(y, O.gemm64(x_values(x), qw, sc))
+    print(f"gemm bf16 M={M} spread={spread} base={base:g} relF={err:.3e}", flush=True)
+    assert err <= 1e-2
