@@ -196,7 +196,8 @@ W4A16_API w4a16_status_t w4a16_swiglu_mlp_timed(const void* x, w4a16_dtype_t xt,
  * the position of each pair in sorted_pairs.  topk_ids are int32 in [0, E),
  * distinct per token; ids outside [0, E) are skipped on the device (they
  * appear in no list and their inv entry is -1) rather than read out of bounds.
- * Errors: INVALID_ARG (null/misaligned, M < 0, top_k < 1, top_k > E, E < 1).
+ * Errors: INVALID_ARG (null/misaligned, M < 0, top_k < 1, top_k > E, E < 1),
+ * UNSUPPORTED (E > 6144).
  */
 W4A16_API w4a16_status_t w4a16_moe_route(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_t E,
                                int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
@@ -218,7 +219,8 @@ W4A16_API size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype
  * live in the workspace; per-expert row counts never leave the device.
  * Experts with at most 8 rows run on the GEMV kernels, heavier experts on MFMA
  * tiles of 64 rows.
- * Errors as w4a16_swiglu_mlp plus INVALID_ARG for top_k < 1 or top_k > E.
+ * Errors as w4a16_swiglu_mlp plus INVALID_ARG for top_k < 1 or top_k > E and
+ * UNSUPPORTED for more than 6144 experts.
  */
 W4A16_API w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int32_t M,
                                  const int32_t* topk_ids, const float* topk_w, int32_t top_k,

@@ -12,55 +12,89 @@ namespace w4 {
 namespace {
 
 constexpr int kRouteThreads = 1024;
-constexpr int kRouteLdsInts = 12288;  // 48 KiB of per-chunk histograms
+constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kRouteLdsInts = 12288;  // 48 KiB: per-wave expert counts and totals
+
+// Waves that place pairs for E experts: each keeps E counters in LDS, next to
+// one row of per-expert totals.
+__host__ __device__ inline int route_waves(int E) {
+  const int w = kRouteLdsInts / E - 1;
+  return w < 1 ? 1 : (w > kRouteWaves ? kRouteWaves : w);
+}
+
+// Lanes of this wave whose key equals this lane's key (keys < 2^bits): one
+// ballot per key bit, intersected.
+__device__ __forceinline__ uint64_t same_key_lanes(int key, int bits) {
+  uint64_t m = ~0ull;
+  for (int b = 0; b < bits; ++b) {
+    const bool on = (key >> b) & 1;
+    const uint64_t v = __ballot(on);
+    m &= on ? v : ~v;
+  }
+  return m;
+}
 
 // Stable counting sort of pairs p = t * top_k + slot by expert id, in one
-// workgroup.  Tokens are cut into C chunks; a per-(chunk, expert) histogram is
-// scanned along chunks per expert, then each chunk places its pairs in token
-// order.  Ids outside [0, E) are skipped (inv = -1).  Optionally also emits the
-// work items of the grouped layer: an expert with at most kMaxGemvRows rows is
-// one GEMV item, a heavier one is cut into MFMA items of kMfmaRows rows, and
-// heavy[p] marks the positions that belong to MFMA items.
+// workgroup.  Wave w of the W placing waves owns the pairs [w L, (w + 1) L);
+// pass A counts each wave's pairs per expert, a scan along waves per expert
+// (after the scan over experts) gives every wave its first position per
+// expert, and pass B places the pairs: a lane's position is its wave's
+// running position for its expert plus the number of lower lanes in the same
+// 64-pair step with the same expert, so the order within an expert is pair
+// order.  Ids outside [0, E) are skipped (inv = -1).  Optionally also emits
+// the work items of the grouped layer: an expert with at most kMaxGemvRows
+// rows is one GEMV item, a heavier one is cut into MFMA items of kMfmaRows
+// rows, and heavy[pos] marks the positions that belong to MFMA items.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int32_t* __restrict__ ids, int M, int top_k, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv,
     int4* __restrict__ items_g, int4* __restrict__ items_m, int32_t* __restrict__ n_items,
     int32_t* __restrict__ heavy) {
-  extern __shared__ int hist[];  // [C][E]
+  extern __shared__ int lds[];  // wc[W][E], then tot[E]
   __shared__ int carry;
+  __shared__ int scan[kRouteThreads];
   const int tid = threadIdx.x;
-  int C = kRouteLdsInts / E;
-  if (C > 64) C = 64;
-  if (C < 1) C = 1;
-  const int tok_per_chunk = (M + C - 1) / C;
-
-  for (int i = tid; i < C * E; i += kRouteThreads) hist[i] = 0;
-  __syncthreads();
-  // 1. per-chunk histograms
+  const int W = route_waves(E);
+  int* wc = lds;
+  int* tot = lds + W * E;
   const int pairs = M * top_k;
-  for (int p = tid; p < pairs; p += kRouteThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) atomicAdd(&hist[(p / top_k / tok_per_chunk) * E + e], 1);
+  const int L = (pairs + W - 1) / W;
+  int bits = 1;
+  while ((1 << bits) <= E) ++bits;  // keys 0 .. E (E = skipped)
+  const int wv = tid / kWave, lane = tid % kWave;
+  const uint64_t below = (1ull << lane) - 1;
+
+  for (int i = tid; i < (W + 1) * E; i += kRouteThreads) lds[i] = 0;
+  __syncthreads();
+  // A. per-wave counts
+  if (wv < W) {
+    const int p0 = wv * L, p1 = min(pairs, p0 + L);
+    for (int q = p0; q < p1; q += kWave) {
+      const int p = q + lane;
+      int key = E;
+      if (p < p1) {
+        const int e = ids[p];
+        if (e >= 0 && e < E) key = e;
+      }
+      const uint64_t m = same_key_lanes(key, bits);
+      if ((m & below) == 0 && key < E) wc[wv * E + key] += __popcll(m);
+    }
   }
   __syncthreads();
-  // 2. exclusive scan along chunks per expert; counts
+  // totals per expert
   for (int e = tid; e < E; e += kRouteThreads) {
     int run = 0;
-    for (int c = 0; c < C; ++c) {
-      const int v = hist[c * E + e];
-      hist[c * E + e] = run;
-      run += v;
-    }
+    for (int w = 0; w < W; ++w) run += wc[w * E + e];
+    tot[e] = run;
     counts[e] = run;
   }
   __syncthreads();
-  // 3. offsets = exclusive scan of counts (blocks of kRouteThreads, serial carry)
+  // offsets = exclusive scan of the totals (blocks of kRouteThreads, serial carry)
   if (tid == 0) carry = 0;
   __syncthreads();
-  __shared__ int scan[kRouteThreads];
   for (int base = 0; base < E; base += kRouteThreads) {
     const int e = base + tid;
-    const int v = e < E ? counts[e] : 0;
+    const int v = e < E ? tot[e] : 0;
     scan[tid] = v;
     __syncthreads();
     for (int off = 1; off < kRouteThreads; off <<= 1) {
@@ -69,33 +103,52 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       scan[tid] += t;
       __syncthreads();
     }
-    if (e < E) offsets[e] = carry + scan[tid] - v;
+    if (e < E) {
+      offsets[e] = carry + scan[tid] - v;
+      tot[e] = carry + scan[tid] - v;
+    }
     __syncthreads();
     if (tid == kRouteThreads - 1) carry += scan[tid];
     __syncthreads();
   }
   if (tid == 0) offsets[E] = carry;
+  // first position of every wave per expert
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int run = tot[e];
+    for (int w = 0; w < W; ++w) {
+      const int t = wc[w * E + e];
+      wc[w * E + e] = run;
+      run += t;
+    }
+  }
   __syncthreads();
-  // 4. placement: chunk c walks its tokens in order
-  for (int c = tid; c < C; c += kRouteThreads) {
-    const int t0 = c * tok_per_chunk, t1 = min(M, t0 + tok_per_chunk);
-    for (int t = t0; t < t1; ++t) {
-      for (int s = 0; s < top_k; ++s) {
-        const int p = t * top_k + s;
+  // B. placement
+  if (wv < W) {
+    const int p0 = wv * L, p1 = min(pairs, p0 + L);
+    for (int q = p0; q < p1; q += kWave) {
+      const int p = q + lane;
+      int key = E;
+      if (p < p1) {
         const int e = ids[p];
-        if (e >= 0 && e < E) {
-          const int pos = offsets[e] + hist[c * E + e]++;
-          sorted_pairs[pos] = p;
-          inv[p] = pos;
-        } else {
-          inv[p] = -1;
-        }
+        if (e >= 0 && e < E) key = e;
       }
+      const uint64_t m = same_key_lanes(key, bits);
+      if (key < E) {
+        const int pos = wc[wv * E + key] + __popcll(m & below);
+        sorted_pairs[pos] = p;
+        inv[p] = pos;
+        if (heavy != nullptr) heavy[pos] = counts[key] > kMaxGemvRows ? 1 : 0;
+      } else if (p < p1) {
+        inv[p] = -1;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if ((m & below) == 0 && key < E) wc[wv * E + key] += __popcll(m);
+      __builtin_amdgcn_wave_barrier();
     }
   }
   if (items_g == nullptr) return;
   __syncthreads();
-  // 5. work items: exclusive scans over experts of the GEMV and MFMA item counts
+  // C. work items: exclusive scans over experts of the GEMV and MFMA item counts
   for (int kind = 0; kind < 2; ++kind) {
     if (tid == 0) carry = 0;
     __syncthreads();
@@ -123,11 +176,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
             items_m[it] = make_int4(e, o0 + r, min(kMfmaRows, c0 - r), 0);
         }
       }
-      if (kind == 1 && e < E) {
-        const int o0 = offsets[e];
-        const int hv = c0 > kMaxGemvRows ? 1 : 0;
-        for (int r = 0; r < c0; ++r) heavy[o0 + r] = hv;
-      }
       __syncthreads();
       if (tid == kRouteThreads - 1) carry += scan[tid];
       __syncthreads();
@@ -138,32 +186,37 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 }
 
 // y[t][n] = sum over slots, in slot order, of w[t][s] * o[inv[t*top_k+s]][n].
+// A thread produces four consecutive columns (16-byte loads and stores; H is
+// a multiple of 32).
 __global__ void combine_kernel(const float* __restrict__ o, const int32_t* __restrict__ inv,
                                const float* __restrict__ topk_w, int M, int top_k, int H,
                                float* __restrict__ y) {
+  const int H4 = H / 4;
   const size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
-  if (idx >= static_cast<size_t>(M) * H) return;
-  const int t = static_cast<int>(idx / H);
-  const int n = static_cast<int>(idx % H);
-  float acc = 0.0f;
+  if (idx >= static_cast<size_t>(M) * H4) return;
+  const int t = static_cast<int>(idx / H4);
+  const int n4 = static_cast<int>(idx % H4);
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int s = 0; s < top_k; ++s) {
     const int pos = inv[t * top_k + s];
-    if (pos >= 0) acc = fmaf(topk_w[t * top_k + s], o[static_cast<size_t>(pos) * H + n], acc);
+    if (pos >= 0) {
+      const float w = topk_w[t * top_k + s];
+      const float4 v = reinterpret_cast<const float4*>(o + static_cast<size_t>(pos) * H)[n4];
+      acc.x = fmaf(w, v.x, acc.x);
+      acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z);
+      acc.w = fmaf(w, v.w, acc.w);
+    }
   }
-  y[idx] = acc;
+  reinterpret_cast<float4*>(y + static_cast<size_t>(t) * H)[n4] = acc;
 }
 
-size_t route_lds_bytes(int E) {
-  int C = kRouteLdsInts / E;
-  if (C > 64) C = 64;
-  if (C < 1) C = 1;
-  return static_cast<size_t>(C) * E * sizeof(int);
-}
+size_t route_lds_bytes(int E) { return static_cast<size_t>(route_waves(E) + 1) * E * sizeof(int); }
 
 w4a16_status_t launch_route(const int32_t* ids, int M, int top_k, int E, int32_t* counts,
                             int32_t* offsets, int32_t* sorted_pairs, int32_t* inv, int4* items_g,
                             int4* items_m, int32_t* n_items, int32_t* heavy, hipStream_t stream) {
-  if (E > kRouteLdsInts) return W4A16_ERR_UNSUPPORTED;
+  if (2 * E > kRouteLdsInts) return W4A16_ERR_UNSUPPORTED;
   const size_t lds = route_lds_bytes(E);
   route_kernel<<<1, kRouteThreads, lds, stream>>>(ids, M, top_k, E, counts, offsets, sorted_pairs,
                                                    inv, items_g, items_m, n_items, heavy);
@@ -402,7 +455,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
 
   // 4. weighted combine in slot order
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  const size_t total = static_cast<size_t>(M) * H;
+  const size_t total = static_cast<size_t>(M) * (H / 4);
   combine_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(o, inv, topk_w, M,
                                                                                   top_k, H, y);
   if ((st = launch_status()) != W4A16_OK) return st;
