@@ -16,6 +16,7 @@ from .w4a16 import (  # noqa: F401
     silu64,
     swiglu_mlp64,
     route,
+    moe_topk,
     moe64,
     rel_frobenius,
 )

@@ -166,6 +166,33 @@ def route(topk_ids: np.ndarray, num_experts: int):
     return counts, offsets, sorted_pairs, inv
 
 
+def moe_topk(logits: np.ndarray, top_k: int):
+    """Router: the top-k experts of every token and their gate weights.
+
+    [FW] "What the Edit Actually Changes": for each token the router selects
+    top-k experts.  The pages give no gating rule; the reading taken is the
+    plainest one the configurations support (softmax-normalised gate weights
+    over the chosen experts): the k largest logits of the token, in descending
+    order with equal logits taken in ascending expert index, and weights
+    softmax over those k logits, exp(l_i - l_max) / sum_j exp(l_j - l_max).
+    Logits must be finite.  Returns topk_ids [M][k] int32 and topk_w [M][k]
+    float64.
+    """
+    lg = np.asarray(logits, dtype=np.float64)
+    assert lg.ndim == 2
+    M, E = lg.shape
+    assert 1 <= top_k <= E
+    ids = np.empty((M, top_k), dtype=np.int32)
+    w = np.empty((M, top_k), dtype=np.float64)
+    for t in range(M):
+        order = sorted(range(E), key=lambda e: (-lg[t, e], e))
+        sel = order[:top_k]
+        ids[t] = sel
+        z = np.exp(lg[t, sel] - lg[t, sel[0]])
+        w[t] = z / z.sum()
+    return ids, w
+
+
 def moe64(x, topk_ids, topk_w, expert, num_experts, tokens=None) -> np.ndarray:
     """Routed-expert SwiGLU MoE layer in float64.
 

@@ -309,3 +309,73 @@ def test_moe_special_cases():
     assert np.allclose(y1, y0[perm], rtol=1e-14, atol=1e-15)
     sub = O.moe64(x, ids, wr, ex, E, tokens=[5, 2])
     assert np.allclose(sub, y0[[5, 2]], rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- router (top-k gating)
+
+def _topk_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "topk_hand.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key == "case":
+                cur = {"k": int(vals[0])}
+                cases.append(cur)
+            else:
+                cur[key] = vals
+    return cases
+
+
+def _closed_form(expr):
+    """Evaluate a fixture weight written in e = exp(1): only 1, 2, e and / + ( )."""
+    assert set(expr) <= set("0123456789e/+() ")
+    return eval(expr, {"__builtins__": {}}, {"e": math.e})
+
+
+def test_topk_hand_worked_fixture():
+    for c in _topk_cases():
+        logits = np.array([[float(v) for v in c["logits"]]])
+        ids, w = O.moe_topk(logits, c["k"])
+        assert ids[0].tolist() == [int(v) for v in c["ids"]]
+        np.testing.assert_allclose(w[0], [_closed_form(v) for v in c["weights"]], rtol=1e-14, atol=0)
+
+
+def test_topk_all_experts_is_a_full_softmax_in_descending_order():
+    rng = np.random.default_rng(7)
+    lg = rng.standard_normal((5, 37))
+    ids, w = O.moe_topk(lg, 37)
+    for t in range(5):
+        assert sorted(ids[t].tolist()) == list(range(37))
+        assert np.all(np.diff(lg[t, ids[t]]) <= 0)
+        full = np.exp(lg[t] - lg[t].max())
+        full /= full.sum()
+        np.testing.assert_allclose(w[t], full[ids[t]], rtol=1e-13, atol=0)
+
+
+def test_topk_brute_force_selection_and_ties():
+    """Integer logits with many ties: every chosen logit is >= every unchosen
+    one, equal logits are taken in ascending index, and the weights are a
+    softmax over the chosen logits (sum 1, shift invariant)."""
+    rng = np.random.default_rng(8)
+    lg = rng.integers(-3, 4, size=(40, 16)).astype(np.float64)
+    for k in (1, 3, 8, 16):
+        ids, w = O.moe_topk(lg, k)
+        shifted_ids, shifted_w = O.moe_topk(lg + 123.0, k)
+        assert np.array_equal(ids, shifted_ids)
+        np.testing.assert_allclose(w, shifted_w, rtol=1e-12)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-13)
+        for t in range(lg.shape[0]):
+            chosen = set(ids[t].tolist())
+            rest = [e for e in range(16) if e not in chosen]
+            if rest:
+                assert lg[t, ids[t]].min() >= lg[t, rest].max()
+            for a, b in zip(ids[t][:-1], ids[t][1:]):
+                assert lg[t, a] > lg[t, b] or (lg[t, a] == lg[t, b] and a < b)
+            # the boundary: an unchosen expert tied with the last chosen one has a larger index
+            last = ids[t][-1]
+            for e in rest:
+                if lg[t, e] == lg[t, last]:
+                    assert e > last
