@@ -254,6 +254,35 @@ def run_moe(args, cfg):
     }
 
 
+def run_router(args, cfg):
+    """One router call per step: float32 logits [M][E] -> top-k ids and
+    softmax gate weights.  A few MB at most, so the figure is latency."""
+    import torch
+    import int4_w4a16_group_g32_amd as L
+    import workloads as W
+
+    M, E, k = cfg.M, cfg.experts, cfg.top_k
+    logits = W.router_logits(M, E, cfg.index, device="cuda")
+    ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((M, k), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        L.moe_topk(logits, k, ids, wts)
+
+    for i in range(args.warmup):
+        step(i)
+    ms_step = timed_steps_ms(args, step)
+    step_bytes = M * E * 4 + M * k * 8
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "M": M, "experts": E, "top_k": k, "bytes_per_step": step_bytes},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+    }
+
+
 def timed_steps_ms(args, step):
     """The timed region: exactly args.steps plain steps between two events,
     with a device synchronization on both sides."""
@@ -355,6 +384,8 @@ def main():
         result = run_mlp(args, cfg)
     elif cfg.kind == "moe":
         result = run_moe(args, cfg)
+    elif cfg.kind == "router":
+        result = run_router(args, cfg)
     else:
         print(f"workload {cfg.name} has no bench line", file=sys.stderr)
         sys.exit(2)

@@ -187,6 +187,22 @@ W4A16_API w4a16_status_t w4a16_swiglu_mlp_timed(const void* x, w4a16_dtype_t xt,
                                                 int32_t* recorded);
 
 /*
+ * Router: the top_k experts of every token and their gate weights (page "The
+ * Final Wire", section "What the Edit Actually Changes": for each token the
+ * router selects top-k experts).  The pages give no gating rule; this library
+ * takes, per token row of logits[M][E] (float32, finite), the top_k largest
+ * logits in descending order, equal logits in ascending expert index, and
+ * writes their expert ids to topk_ids[M][top_k] (int32, distinct per token)
+ * and softmax weights over those top_k logits, exp(l - l_max) / sum, to
+ * topk_w[M][top_k] (float32).  The outputs feed w4a16_moe_route and
+ * w4a16_moe_grouped directly.  Deterministic.
+ * Errors: INVALID_ARG (null/misaligned, M < 0, E < 1, top_k < 1, top_k > E),
+ * UNSUPPORTED (E > 1024 or top_k > 32).  M == 0 enqueues nothing.
+ */
+W4A16_API w4a16_status_t w4a16_moe_topk(const float* logits, int32_t M, int32_t E, int32_t top_k,
+                              int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/*
  * Group (token, slot) pairs by expert (page "The Final Wire", section "What
  * the Edit Actually Changes": the router picks top-k experts per token and
  * each expert runs its own projections).  Pair p = t * top_k + slot.  Outputs,

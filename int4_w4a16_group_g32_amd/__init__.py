@@ -33,6 +33,7 @@ EXPORTS = (
     "w4a16_swiglu_mlp_workspace_bytes",
     "w4a16_swiglu_mlp",
     "w4a16_swiglu_mlp_timed",
+    "w4a16_moe_topk",
     "w4a16_moe_route",
     "w4a16_moe_workspace_bytes",
     "w4a16_moe_grouped",
@@ -82,6 +83,7 @@ def load_library() -> ctypes.CDLL:
             "w4a16_swiglu_mlp": (i32, [vp, i32, i32, dp, dp, dp, vp, vp, sz, vp]),
             "w4a16_swiglu_mlp_timed": (i32, [vp, i32, i32, dp, dp, dp, vp, vp, sz, vp, vp, i32,
                                              ctypes.POINTER(i32)]),
+            "w4a16_moe_topk": (i32, [vp, i32, i32, i32, vp, vp, vp]),
             "w4a16_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
             "w4a16_moe_workspace_bytes": (sz, [i32, i32, i32, dp, dp, dp]),
             "w4a16_moe_grouped": (i32, [vp, i32, i32, vp, vp, i32, dp, dp, dp, vp, vp, sz, vp]),
@@ -188,6 +190,13 @@ def swiglu_mlp(x: torch.Tensor, gate: Weight, up: Weight, down: Weight, y: torch
     _check(load_library().w4a16_swiglu_mlp(_ptr(x), _dtype_code(x), x.shape[0], _dref(gate), _dref(up),
                                            _dref(down), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                            _stream(stream)), "w4a16_swiglu_mlp")
+
+
+def moe_topk(logits: torch.Tensor, top_k: int, topk_ids: torch.Tensor, topk_w: torch.Tensor, stream=None):
+    """Top-k experts per token row of float32 logits [M][E] and their softmax gate weights."""
+    M, E = logits.shape
+    _check(load_library().w4a16_moe_topk(_ptr(logits), M, E, top_k, _ptr(topk_ids), _ptr(topk_w),
+                                         _stream(stream)), "w4a16_moe_topk")
 
 
 def moe_route(topk_ids: torch.Tensor, num_experts: int, counts, offsets, sorted_pairs, inv, stream=None):

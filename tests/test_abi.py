@@ -118,6 +118,21 @@ def test_moe_argument_checks(lib):
                                None) == L.ERR_INVALID_ARG
 
 
+def test_topk_argument_checks(lib):
+    """Every rejection happens on the host, before anything is launched."""
+    call = lambda M, E, k, logits=0x1000, ids=0x2000, w=0x3000: lib.w4a16_moe_topk(
+        ctypes.c_void_p(logits), M, E, k, ctypes.c_void_p(ids), ctypes.c_void_p(w), None)
+    assert call(-1, 8, 2) == L.ERR_INVALID_ARG
+    assert call(4, 0, 1) == L.ERR_INVALID_ARG
+    assert call(4, 8, 0) == L.ERR_INVALID_ARG
+    assert call(4, 8, 9) == L.ERR_INVALID_ARG      # top_k > E
+    assert call(4, 1025, 8) == L.ERR_UNSUPPORTED   # more experts than one wave holds
+    assert call(4, 64, 33) == L.ERR_UNSUPPORTED
+    assert call(4, 64, 8, logits=0) == L.ERR_INVALID_ARG
+    assert call(4, 64, 8, ids=0x2004) == L.ERR_INVALID_ARG  # misaligned
+    assert call(0, 64, 8, logits=0, ids=0, w=0) == L.OK     # M == 0: nothing to do
+
+
 def test_quantize_and_prepack_checks(lib):
     assert lib.w4a16_quantize(ctypes.c_void_p(0x1000), 48, 64, 1, ctypes.c_void_p(0x2000),
                               ctypes.c_void_p(0x3000), None) == L.ERR_UNSUPPORTED

@@ -25,14 +25,14 @@ import torch
 WEIGHT_STD = 0.02
 
 # tensor tags, so that every (config, tensor) pair has its own stream
-TAG_X, TAG_GATE, TAG_UP, TAG_DOWN, TAG_TOPK, TAG_GATEW, TAG_ZIPF = range(7)
+TAG_X, TAG_GATE, TAG_UP, TAG_DOWN, TAG_TOPK, TAG_GATEW, TAG_ZIPF, TAG_LOGITS = range(8)
 
 
 @dataclass(frozen=True)
 class Config:
     name: str
     index: int
-    kind: str            # "gemm" | "mlp" | "moe"
+    kind: str            # "gemm" | "mlp" | "moe" | "router"
     M: int
     K: int               # hidden size (input dim of gate/up, output dim of down)
     N: int               # output dim of a plain gemm, else the intermediate size
@@ -51,6 +51,9 @@ CONFIGS = {
     "moe_decode_m64": Config("moe_decode_m64", 3, "moe", 64, 7168, 2048, "bf16", 384, 8, "uniform"),
     "moe_prefill_m2048": Config("moe_prefill_m2048", 4, "moe", 2048, 7168, 2048, "bf16", 384, 8, "zipf", 1.1),
     "gemm_m2048_hot_expert": Config("gemm_m2048_hot_expert", 5, "gemm", 2048, 7168, 4096, "bf16"),
+    # router (top-k gating) ahead of the two MoE layers: float32 logits [M][384]
+    "router_m64": Config("router_m64", 3, "router", 64, 0, 0, "f32", 384, 8),
+    "router_m2048": Config("router_m2048", 4, "router", 2048, 0, 0, "f32", 384, 8),
 }
 
 
@@ -84,6 +87,11 @@ def activations(M, K, config, dtype="f32", index=0, device="cpu") -> torch.Tenso
 def weights(K, N, config, tag, index=0, device="cpu") -> torch.Tensor:
     """Unquantized weights W[K][N] ~ N(0, 0.02^2) in float32."""
     return normal((K, N), WEIGHT_STD, config, tag, index, device)
+
+
+def router_logits(M, E, config, index=0, device="cpu") -> torch.Tensor:
+    """Router logits[M][E] ~ N(0,1) in float32."""
+    return normal((M, E), 1.0, config, TAG_LOGITS, index, device)
 
 
 def topk_uniform(M, E, k, config, index=0) -> np.ndarray:
