@@ -18,5 +18,6 @@ from .w4a16 import (  # noqa: F401
     route,
     moe_topk,
     moe64,
+    moe_shared64,
     rel_frobenius,
 )

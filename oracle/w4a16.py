@@ -233,6 +233,24 @@ def moe64(x, topk_ids, topk_w, expert, num_experts, tokens=None) -> np.ndarray:
     return y
 
 
+def moe_shared64(x, topk_ids, topk_w, expert, num_experts, shared, tokens=None) -> np.ndarray:
+    """Routed experts plus one shared expert, float64.
+
+    [WP] section "The Engine Dispatch: Model::linear" puts the shared expert
+    on the INT4 path beside the routed experts, and [FL] section "Assumptions
+    and Knowledge Boundaries" names an MoE with a shared expert.  The pages
+    do not say how it joins the layer; the reading taken is the plain sum
+    y[t] = (routed
+    experts' weighted sum, as in moe64) + shared(x[t]) with weight 1, the
+    shared term added last.  ``shared`` is ((qw_g, sc_g), (qw_u, sc_u),
+    (qw_d, sc_d)) for one SwiGLU MLP of the experts' shape.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rows = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    routed = moe64(x, topk_ids, topk_w, expert, num_experts, tokens)
+    return routed + swiglu_mlp64(x[rows], *shared)
+
+
 def rel_frobenius(y, ref) -> float:
     """||y - ref||_F / ||ref||_F, computed in float64."""
     y = np.asarray(y, dtype=np.float64)

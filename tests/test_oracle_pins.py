@@ -379,3 +379,31 @@ def test_topk_brute_force_selection_and_ties():
             for e in rest:
                 if lg[t, e] == lg[t, last]:
                     assert e > last
+
+
+# ---------------------------------------------------------------- shared expert
+
+def test_moe_shared_special_cases():
+    """The shared expert adds one SwiGLU MLP with weight 1: zero routed gate
+    weights leave exactly the shared MLP; an all-zero shared expert (zero
+    scales) leaves exactly the routed sum; a per-token loop agrees."""
+    rng = np.random.default_rng(41)
+    M, E, k, H, I = 6, 5, 2, 32, 64
+    x = rng.standard_normal((M, H)).astype(np.float32)
+    ex = _experts(rng, E, H, I)
+    sh = _experts(rng, 1, H, I)(0)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(M)])
+    w = rng.random((M, k))
+    y0 = O.moe_shared64(x, ids, np.zeros((M, k)), ex, E, sh)
+    assert np.array_equal(y0, O.swiglu_mlp64(x, *sh))
+    zero = tuple((qw, np.zeros_like(sc)) for qw, sc in sh)
+    assert np.array_equal(O.moe_shared64(x, ids, w, ex, E, zero), O.moe64(x, ids, w, ex, E))
+    y = O.moe_shared64(x, ids, w, ex, E, sh)
+    for t in range(M):
+        want = np.zeros(H)
+        for s in range(k):
+            want += w[t, s] * O.swiglu_mlp64(x[t:t + 1], *ex(int(ids[t, s])))[0]
+        want += O.swiglu_mlp64(x[t:t + 1], *sh)[0]
+        assert np.allclose(y[t], want, rtol=0, atol=1e-13 * np.abs(want).max())
+    sub = O.moe_shared64(x, ids, w, ex, E, sh, tokens=[4, 1])
+    assert np.allclose(sub, y[[4, 1]], rtol=1e-14, atol=1e-15)
