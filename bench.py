@@ -217,6 +217,8 @@ def run_moe(args, cfg):
     wts = torch.as_tensor(W.gate_weights(M, k, cfg.index)).cuda()
     x = W.activations(M, H, cfg.index, cfg.x_dtype, device="cuda")
     y = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    if cfg.shared:
+        return run_moe_shared(args, cfg, stacks, ids, ids_np, wts, x, y)
     ws = L.new_workspace(L.moe_workspace_bytes(M, k, xt, *stacks))
     lib = L.load_library()
     sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -250,6 +252,63 @@ def run_moe(args, cfg):
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "kernels_us": {n: round(v * 1e3, 2) for n, v in kern.items()},
         "ms_per_step_marked": round(ms_marked, 5),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+    }
+
+
+def run_moe_shared(args, cfg, stacks, ids, ids_np, wts, x, y):
+    """One MoE layer with a shared expert per step, the shared expert running
+    inside the routed experts' grouped launches.  Also times the same work as
+    two calls (routed layer, then the shared expert as a dense MLP) to show
+    what the overlap saves."""
+    import numpy as np
+    import torch
+    import int4_w4a16_group_g32_amd as L
+    import workloads as W
+
+    E, H, I, M, k = cfg.experts, cfg.K, cfg.N, cfg.M, cfg.top_k
+    xt = L.F32 if cfg.x_dtype == "f32" else L.BF16
+    xbytes = 4 if cfg.x_dtype == "f32" else 2
+    shared = []
+    for tag, (K, N) in ((W.TAG_GATE, (H, I)), (W.TAG_UP, (H, I)), (W.TAG_DOWN, (I, H))):
+        qw = torch.empty((1, K // 8, N), dtype=torch.int32, device="cuda")
+        sc = torch.empty((1, K // 32, N), dtype=torch.float32, device="cuda")
+        L.quantize(W.weights(K, N, cfg.index, tag, W.SHARED_EXPERT_INDEX, device="cuda"), qw[0], sc[0])
+        shared.append(L.prepack(L.Weight(qw, sc, K, N, 1, L.LAYOUT_CANONICAL), torch.empty_like(qw)))
+    ws = L.new_workspace(L.moe_shared_workspace_bytes(M, k, xt, *stacks, *shared))
+
+    def step(i):
+        L.moe_grouped_shared(x, ids, wts, *stacks, *shared, y, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    ms_step = timed_steps_ms(args, step)
+    # the same work in two calls: routed layer, then the shared MLP (dense entry point)
+    ws_r = L.new_workspace(L.moe_workspace_bytes(M, k, xt, *stacks))
+    dense = [L.Weight(w.qw[0], w.scales[0], w.K, w.N, 1, w.layout) for w in shared]
+    ws_d = L.new_workspace(L.swiglu_mlp_workspace_bytes(M, xt, *dense))
+    y2 = torch.empty_like(y)
+
+    def step2(i):
+        L.moe_grouped(x, ids, wts, *stacks, y, ws_r)
+        L.swiglu_mlp(x, *dense, y2, ws_d)
+
+    for i in range(args.warmup):
+        step2(i)
+    ms_two = timed_steps_ms(args, step2)
+    active = int((np.bincount(ids_np.ravel(), minlength=E) > 0).sum()) + 1
+    step_bytes = active * 3 * H * I * 5 // 8 + M * H * xbytes + M * H * 4
+    flops = 2 * 3 * H * I * M * (k + 1)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.x_dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "M": M, "experts": E, "top_k": k, "hidden": H, "intermediate": I,
+                   "routing": cfg.routing, "shared_experts": 1, "active_experts_with_shared": active,
+                   "bytes_per_step": step_bytes},
+        "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "ms_routed_then_shared_mlp": round(ms_two, 5),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
     }
 

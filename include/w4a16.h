@@ -244,6 +244,35 @@ W4A16_API w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int3
                                  const w4a16_weight_t* down, float* y, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* Bytes of workspace w4a16_moe_grouped_shared needs (0 for invalid arguments). */
+W4A16_API size_t w4a16_moe_shared_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype_t xt,
+                                        const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                        const w4a16_weight_t* down, const w4a16_weight_t* shared_gate,
+                                        const w4a16_weight_t* shared_up,
+                                        const w4a16_weight_t* shared_down);
+
+/*
+ * MoE layer with a shared expert (page "The Weight of Precision", section "The
+ * Engine Dispatch: Model::linear": the shared expert runs on the INT4 path
+ * beside the routed experts; the pages do not say how it joins the layer):
+ *   y[t] = w4a16_moe_grouped's routed sum + MLP_shared(x[t]),
+ * the shared term added last with weight 1.  shared_gate/up/down are one
+ * GROUPED SwiGLU MLP (num_experts == 1) of the routed experts' shapes.  The
+ * shared expert runs as one more expert inside the same grouped launches
+ * (GEMV items of up to 8 rows while M <= 64, MFMA tiles beyond), so it
+ * overlaps the routed experts instead of following them.  Arguments,
+ * workspace and errors as
+ * w4a16_moe_grouped, plus INVALID_ARG for a null shared descriptor and
+ * UNSUPPORTED for a shared expert of another shape or with num_experts != 1.
+ */
+W4A16_API w4a16_status_t w4a16_moe_grouped_shared(const void* x, w4a16_dtype_t xt, int32_t M,
+                                        const int32_t* topk_ids, const float* topk_w, int32_t top_k,
+                                        const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                        const w4a16_weight_t* down, const w4a16_weight_t* shared_gate,
+                                        const w4a16_weight_t* shared_up,
+                                        const w4a16_weight_t* shared_down, float* y, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+
 /*
  * Measurement variant of w4a16_moe_grouped, with the event convention of
  * w4a16_swiglu_mlp_timed.  Kernels in launch order: expert grouping; gate/up

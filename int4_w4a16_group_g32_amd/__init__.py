@@ -37,6 +37,8 @@ EXPORTS = (
     "w4a16_moe_route",
     "w4a16_moe_workspace_bytes",
     "w4a16_moe_grouped",
+    "w4a16_moe_shared_workspace_bytes",
+    "w4a16_moe_grouped_shared",
     "w4a16_moe_grouped_timed",
 )
 
@@ -87,6 +89,9 @@ def load_library() -> ctypes.CDLL:
             "w4a16_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
             "w4a16_moe_workspace_bytes": (sz, [i32, i32, i32, dp, dp, dp]),
             "w4a16_moe_grouped": (i32, [vp, i32, i32, vp, vp, i32, dp, dp, dp, vp, vp, sz, vp]),
+            "w4a16_moe_shared_workspace_bytes": (sz, [i32, i32, i32, dp, dp, dp, dp, dp, dp]),
+            "w4a16_moe_grouped_shared": (i32, [vp, i32, i32, vp, vp, i32, dp, dp, dp, dp, dp, dp, vp, vp, sz,
+                                               vp]),
             "w4a16_moe_grouped_timed": (i32, [vp, i32, i32, vp, vp, i32, dp, dp, dp, vp, vp, sz, vp, vp,
                                               i32, ctypes.POINTER(i32)]),
         }
@@ -207,6 +212,24 @@ def moe_route(topk_ids: torch.Tensor, num_experts: int, counts, offsets, sorted_
 
 def moe_workspace_bytes(M: int, top_k: int, xt: int, gate: Weight, up: Weight, down: Weight) -> int:
     return load_library().w4a16_moe_workspace_bytes(M, top_k, xt, _dref(gate), _dref(up), _dref(down))
+
+
+def moe_shared_workspace_bytes(M: int, top_k: int, xt: int, gate: Weight, up: Weight, down: Weight,
+                               shared_gate: Weight, shared_up: Weight, shared_down: Weight) -> int:
+    return load_library().w4a16_moe_shared_workspace_bytes(M, top_k, xt, _dref(gate), _dref(up), _dref(down),
+                                                           _dref(shared_gate), _dref(shared_up),
+                                                           _dref(shared_down))
+
+
+def moe_grouped_shared(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate: Weight, up: Weight,
+                       down: Weight, shared_gate: Weight, shared_up: Weight, shared_down: Weight, y: torch.Tensor,
+                       ws: torch.Tensor, stream=None):
+    M, k = topk_ids.shape
+    _check(load_library().w4a16_moe_grouped_shared(_ptr(x), _dtype_code(x), M, _ptr(topk_ids), _ptr(topk_w), k,
+                                                   _dref(gate), _dref(up), _dref(down), _dref(shared_gate),
+                                                   _dref(shared_up), _dref(shared_down), _ptr(y), _ptr(ws),
+                                                   ws.numel() * ws.element_size(), _stream(stream)),
+           "w4a16_moe_grouped_shared")
 
 
 def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate: Weight, up: Weight,

@@ -259,8 +259,11 @@ void gemv_kernel(const GemvArgs a) {
   // the lane reads GROUPED slot 16kb + lc of the wave's 64-column block: word
   // kb of columns c0 + 4lc + cb, cb = 0..3 (MFMA block cb, column lc)
   const int cbase = wave_ok ? c0 : 0;
-  const u32x4* wp = (mat ? a.qw1 : a.qw0) + ebase + cbase + 16 * kb + lc;
-  const f32x4* sp = reinterpret_cast<const f32x4*>((mat ? a.sc1 : a.sc0) + ebase + cbase + 4 * lc);
+  const bool xe = expert + 1 == a.extra_plus1;
+  const u32x4* qb = xe ? (mat ? a.qw1x : a.qw0x) : (mat ? a.qw1 : a.qw0) + ebase;
+  const float* sb = xe ? (mat ? a.sc1x : a.sc0x) : (mat ? a.sc1 : a.sc0) + ebase;
+  const u32x4* wp = qb + cbase + 16 * kb + lc;
+  const f32x4* sp = reinterpret_cast<const f32x4*>(sb + cbase + 4 * lc);
   const size_t gstride = static_cast<size_t>(a.N);  // chunks (and scales) per group row
   const int g_last = g_hi - 1;
   const uint32_t magic = magic_vgpr();

@@ -39,6 +39,13 @@ struct MfmaArgs {
   const u32x4* qw1;    // up (SwiGLU mode)
   const float* sc1;
   size_t expert_stride;  // chunks (and scales) per expert
+  // One more expert with weights of its own (the shared expert of an MoE
+  // layer): id extra_plus1 - 1 reads these instead of the stacks (0: none).
+  int extra_plus1;
+  const u32x4* qw0x;
+  const float* sc0x;
+  const u32x4* qw1x;
+  const float* sc1x;
   int N;                 // columns per matrix
   int tiles;             // column tiles per row item
   int S, gps;            // K splits, groups per split

@@ -295,8 +295,11 @@ void mfma_kernel(const MfmaArgs a) {
     chunk = c0 + 16 * kb + lc;
   }
   const size_t ebase = static_cast<size_t>(expert) * a.expert_stride;
-  const u32x4* wp = (mat ? a.qw1 : a.qw0) + ebase + (wave_ok ? chunk : 0);
-  const float* sp = (mat ? a.sc1 : a.sc0) + ebase + (wave_ok ? col0 : 0);
+  const bool xe = expert + 1 == a.extra_plus1;
+  const u32x4* qb = xe ? (mat ? a.qw1x : a.qw0x) : (mat ? a.qw1 : a.qw0) + ebase;
+  const float* sb = xe ? (mat ? a.sc1x : a.sc0x) : (mat ? a.sc1 : a.sc0) + ebase;
+  const u32x4* wp = qb + (wave_ok ? chunk : 0);
+  const float* sp = sb + (wave_ok ? col0 : 0);
   const size_t gstride = static_cast<size_t>(a.N);  // chunks (and scales) per group row
 
   f32x4 acc[4][4];

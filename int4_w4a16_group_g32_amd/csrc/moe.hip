@@ -12,6 +12,7 @@ namespace w4 {
 namespace {
 
 constexpr int kRouteThreads = 1024;
+constexpr int kSharedGemvRows = 64;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kRouteLdsInts = 12288;  // 48 KiB: per-wave expert counts and totals
 
@@ -44,12 +45,17 @@ __device__ __forceinline__ uint64_t same_key_lanes(int key, int bits) {
 // order.  Ids outside [0, E) are skipped (inv = -1).  Optionally also emits
 // the work items of the grouped layer: an expert with at most kMaxGemvRows
 // rows is one GEMV item, a heavier one is cut into MFMA items of kMfmaRows
-// rows, and heavy[pos] marks the positions that belong to MFMA items.
+// rows, and heavy[pos] marks the positions that belong to MFMA items.  With
+// shared_rows = M a shared expert (id E) takes the positions M * top_k + t,
+// t = 0 .. M-1, one per token in token order (gather entry t * top_k): up to
+// kSharedGemvRows rows as GEMV items of kMaxGemvRows rows, which join the
+// routed experts' GEMV launches (the MFMA items have no K split, so a lone
+// heavy expert would be a long serial tail), more as MFMA items.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int32_t* __restrict__ ids, int M, int top_k, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv,
     int4* __restrict__ items_g, int4* __restrict__ items_m, int32_t* __restrict__ n_items,
-    int32_t* __restrict__ heavy) {
+    int32_t* __restrict__ heavy, int shared_rows) {
   extern __shared__ int lds[];  // wc[W][E], then tot[E]
   __shared__ int carry;
   __shared__ int scan[kRouteThreads];
@@ -146,6 +152,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       __builtin_amdgcn_wave_barrier();
     }
   }
+  // the shared expert's positions follow the routed pairs
+  for (int t = tid; t < shared_rows; t += kRouteThreads) {
+    sorted_pairs[pairs + t] = t * top_k;
+    if (heavy != nullptr) heavy[pairs + t] = shared_rows > kSharedGemvRows ? 1 : 0;
+  }
   if (items_g == nullptr) return;
   __syncthreads();
   // C. work items: exclusive scans over experts of the GEMV and MFMA item counts
@@ -183,13 +194,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     if (tid == 0) n_items[kind] = carry;
     __syncthreads();
   }
+  if (shared_rows > 0 && tid == 0) {  // the shared expert's items go last
+    if (shared_rows <= kSharedGemvRows) {
+      int it = n_items[0];
+      for (int r = 0; r < shared_rows; r += kMaxGemvRows, ++it)
+        items_g[it] = make_int4(E, pairs + r, min(kMaxGemvRows, shared_rows - r), 0);
+      n_items[0] = it;
+    } else {
+      int it = n_items[1];
+      for (int r = 0; r < shared_rows; r += kMfmaRows, ++it)
+        items_m[it] = make_int4(E, pairs + r, min(kMfmaRows, shared_rows - r), 0);
+      n_items[1] = it;
+    }
+  }
 }
 
 // y[t][n] = sum over slots, in slot order, of w[t][s] * o[inv[t*top_k+s]][n].
 // A thread produces four consecutive columns (16-byte loads and stores; H is
 // a multiple of 32).
+// With shared0 >= 0 the shared expert's output row o[shared0 + t] is added
+// last, with weight 1.
 __global__ void combine_kernel(const float* __restrict__ o, const int32_t* __restrict__ inv,
-                               const float* __restrict__ topk_w, int M, int top_k, int H,
+                               const float* __restrict__ topk_w, int M, int top_k, int H, int shared0,
                                float* __restrict__ y) {
   const int H4 = H / 4;
   const size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
@@ -208,6 +234,13 @@ __global__ void combine_kernel(const float* __restrict__ o, const int32_t* __res
       acc.w = fmaf(w, v.w, acc.w);
     }
   }
+  if (shared0 >= 0) {
+    const float4 v = reinterpret_cast<const float4*>(o + static_cast<size_t>(shared0 + t) * H)[n4];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
   reinterpret_cast<float4*>(y + static_cast<size_t>(t) * H)[n4] = acc;
 }
 
@@ -215,17 +248,19 @@ size_t route_lds_bytes(int E) { return static_cast<size_t>(route_waves(E) + 1) *
 
 w4a16_status_t launch_route(const int32_t* ids, int M, int top_k, int E, int32_t* counts,
                             int32_t* offsets, int32_t* sorted_pairs, int32_t* inv, int4* items_g,
-                            int4* items_m, int32_t* n_items, int32_t* heavy, hipStream_t stream) {
+                            int4* items_m, int32_t* n_items, int32_t* heavy, int shared_rows,
+                            hipStream_t stream) {
   if (2 * E > kRouteLdsInts) return W4A16_ERR_UNSUPPORTED;
   const size_t lds = route_lds_bytes(E);
   route_kernel<<<1, kRouteThreads, lds, stream>>>(ids, M, top_k, E, counts, offsets, sorted_pairs,
-                                                   inv, items_g, items_m, n_items, heavy);
+                                                   inv, items_g, items_m, n_items, heavy, shared_rows);
   return launch_status();
 }
 
 struct MoePlan {
   int P = 0, Mp = 0;
   size_t pairs = 0, max_items = 0, max_mitems = 0;
+  size_t positions = 0;  // pairs, then one per token for a shared expert
   size_t counts_off, offsets_off, sorted_off, inv_off, items_off, mitems_off, nitems_off, heavy_off;
   size_t h_off, o_off;
   size_t apx_off, rsx_off, aph_off, rsh_off;
@@ -233,28 +268,35 @@ struct MoePlan {
   size_t bytes = 0;
 };
 
-MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate) {
+MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate, bool shared) {
   MoePlan p;
   p.P = mfma_pieces(xt);
   const int E = gate->num_experts, H = gate->K, I = gate->N;
   p.pairs = static_cast<size_t>(M) * top_k;
+  p.positions = p.pairs + (shared ? static_cast<size_t>(M) : 0);
   p.max_items = std::min<size_t>(E, p.pairs) + 1;  // one GEMV item per light expert
   p.mfma = M > kMaxGemvRows;                       // an expert gets at most M rows
   p.max_mitems = p.mfma ? p.pairs / kMfmaRows + std::min<size_t>(E, p.pairs / (kMaxGemvRows + 1)) + 1 : 0;
-  p.Mp = p.mfma ? mfma_rows_padded(static_cast<int>(p.pairs)) : 0;
+  if (shared) {  // the shared expert is one more expert with M rows
+    if (M <= kSharedGemvRows)
+      p.max_items += (static_cast<size_t>(M) + kMaxGemvRows - 1) / kMaxGemvRows;
+    else
+      p.max_mitems += (static_cast<size_t>(M) + kMfmaRows - 1) / kMfmaRows;
+  }
+  p.Mp = p.mfma ? mfma_rows_padded(static_cast<int>(p.positions)) : 0;
   Carve c;
   size_t dummy;
   c.take(dummy, kCounterBytes);
   c.take(p.counts_off, static_cast<size_t>(E) * 4);
   c.take(p.offsets_off, static_cast<size_t>(E + 1) * 4);
-  c.take(p.sorted_off, p.pairs * 4);
+  c.take(p.sorted_off, p.positions * 4);
   c.take(p.inv_off, p.pairs * 4);
   c.take(p.items_off, p.max_items * 16);
   c.take(p.mitems_off, std::max<size_t>(p.max_mitems, 1) * 16);
   c.take(p.nitems_off, 16);
-  c.take(p.heavy_off, p.pairs * 4);
-  c.take(p.h_off, std::max<size_t>(p.pairs, p.Mp) * I * 4);
-  c.take(p.o_off, p.pairs * H * 4);
+  c.take(p.heavy_off, p.positions * 4);
+  c.take(p.h_off, std::max<size_t>(p.positions, p.Mp) * I * 4);
+  c.take(p.o_off, p.positions * H * 4);
   c.take(p.apx_off, static_cast<size_t>(p.P) * p.Mp * H * 2);
   c.take(p.rsx_off, static_cast<size_t>(p.Mp) * 4);
   c.take(p.aph_off, static_cast<size_t>(p.P) * p.Mp * I * 2);
@@ -278,6 +320,16 @@ w4a16_status_t check_moe(const w4a16_weight_t* gate, const w4a16_weight_t* up,
   return W4A16_OK;
 }
 
+// A shared expert: one SwiGLU MLP of the routed experts' shapes, GROUPED.
+w4a16_status_t check_shared(const w4a16_weight_t* gate, const w4a16_weight_t* sg, const w4a16_weight_t* su,
+                            const w4a16_weight_t* sd) {
+  const w4a16_status_t st = check_moe(sg, su, sd);
+  if (st != W4A16_OK) return st;
+  if (sg->num_experts != 1) return W4A16_ERR_UNSUPPORTED;
+  if (sg->K != gate->K || sg->N != gate->N) return W4A16_ERR_UNSUPPORTED;
+  return W4A16_OK;
+}
+
 }  // namespace
 }  // namespace w4
 
@@ -296,7 +348,7 @@ extern "C" w4a16_status_t w4a16_moe_route(const int32_t* topk_ids, int32_t M, in
       return W4A16_ERR_INVALID_ARG;
   }
   return launch_route(topk_ids, M, top_k, E, counts, offsets, sorted_pairs, inv, nullptr, nullptr,
-                      nullptr, nullptr, stream);
+                      nullptr, nullptr, 0, stream);
 }
 
 extern "C" size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype_t xt,
@@ -304,16 +356,32 @@ extern "C" size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtyp
                                             const w4a16_weight_t* down) {
   if (M <= 0 || top_k < 1 || check_moe(gate, up, down) != W4A16_OK) return 0;
   if (xt != W4A16_F32 && xt != W4A16_BF16) return 0;
-  return plan_moe(M, top_k, xt, gate).bytes;
+  return plan_moe(M, top_k, xt, gate, false).bytes;
+}
+
+extern "C" size_t w4a16_moe_shared_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype_t xt,
+                                                   const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                                   const w4a16_weight_t* down,
+                                                   const w4a16_weight_t* shared_gate,
+                                                   const w4a16_weight_t* shared_up,
+                                                   const w4a16_weight_t* shared_down) {
+  if (M <= 0 || top_k < 1 || check_moe(gate, up, down) != W4A16_OK) return 0;
+  if (check_shared(gate, shared_gate, shared_up, shared_down) != W4A16_OK) return 0;
+  if (xt != W4A16_F32 && xt != W4A16_BF16) return 0;
+  return plan_moe(M, top_k, xt, gate, true).bytes;
 }
 
 namespace w4 {
+// sg, su, sd: the shared expert's gate, up and down (all null: none).
 static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const int32_t* topk_ids,
                                const float* topk_w, int32_t top_k, const w4a16_weight_t* gate,
-                               const w4a16_weight_t* up, const w4a16_weight_t* down, float* y,
-                               void* ws, size_t ws_bytes, hipStream_t stream, EventMarks& ev) {
+                               const w4a16_weight_t* up, const w4a16_weight_t* down,
+                               const w4a16_weight_t* sg, const w4a16_weight_t* su, const w4a16_weight_t* sd,
+                               float* y, void* ws, size_t ws_bytes, hipStream_t stream, EventMarks& ev) {
   w4a16_status_t st = check_moe(gate, up, down);
   if (st != W4A16_OK) return st;
+  const bool shared = sg != nullptr;
+  if (shared && (st = check_shared(gate, sg, su, sd)) != W4A16_OK) return st;
   const int E = gate->num_experts, H = gate->K, I = gate->N;
   if (M < 0 || top_k < 1 || top_k > E || (xt != W4A16_F32 && xt != W4A16_BF16))
     return W4A16_ERR_INVALID_ARG;
@@ -326,7 +394,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   if (ranges_overlap(x, static_cast<size_t>(M) * H * dtype_bytes(xt), y,
                      static_cast<size_t>(M) * H * 4))
     return W4A16_ERR_INVALID_ARG;
-  const MoePlan p = plan_moe(M, top_k, xt, gate);
+  const MoePlan p = plan_moe(M, top_k, xt, gate, shared);
   if (ws_bytes < p.bytes) return W4A16_ERR_WORKSPACE;
   char* b = static_cast<char*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(b + p.counts_off);
@@ -340,11 +408,12 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   float* hraw = reinterpret_cast<float*>(b + p.h_off);
   float* o = reinterpret_cast<float*>(b + p.o_off);
   const int R = static_cast<int>(p.pairs);
+  const int T = static_cast<int>(p.positions);  // routed pairs, then the shared expert's rows
 
   // 1. expert grouping and work items
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
   st = launch_route(topk_ids, M, top_k, E, counts, offsets, sorted, inv, items, mitems, n_items,
-                    heavy, stream);
+                    heavy, shared ? M : 0, stream);
   if (st != W4A16_OK) return st;
 
   // 2. gate/up with the SwiGLU epilogue: light experts on the GEMV, heavy on MFMA tiles
@@ -369,6 +438,13 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   a.n_items = n_items;
   a.mode = 1;
   a.h = hraw;
+  if (shared) {
+    a.extra_plus1 = E + 1;
+    a.qw0x = reinterpret_cast<const u32x4*>(sg->qw);
+    a.sc0x = sg->scales;
+    a.qw1x = reinterpret_cast<const u32x4*>(su->qw);
+    a.sc1x = su->scales;
+  }
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
   st = launch_gemv(a, p.max_items * a.tiles, stream);
   if (st != W4A16_OK) return st;
@@ -380,7 +456,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   MfmaArgs ma{};
   if (p.mfma) {
     if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma_prep(x, xt, R, p.Mp, H, p.P, sorted, top_k, heavy, apx, rsx, stream);
+    st = launch_mfma_prep(x, xt, T, p.Mp, H, p.P, sorted, top_k, heavy, apx, rsx, stream);
     if (st != W4A16_OK) return st;
     ma.ap = apx;
     ma.rs = rsx;
@@ -402,6 +478,11 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     ma.mode = 1;
     ma.h = hraw;
     ma.h_bf16 = 0;
+    ma.extra_plus1 = a.extra_plus1;
+    ma.qw0x = a.qw0x;
+    ma.sc0x = a.sc0x;
+    ma.qw1x = a.qw1x;
+    ma.sc1x = a.sc1x;
     if ((st = ev.mark(stream)) != W4A16_OK) return st;
     st = launch_mfma(ma, p.P, p.max_mitems * ma.tiles, stream);
     if (st != W4A16_OK) return st;
@@ -425,12 +506,17 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   d.n_items = n_items;
   d.mode = 0;
   d.out = o;
+  if (shared) {
+    d.extra_plus1 = E + 1;
+    d.qw0x = reinterpret_cast<const u32x4*>(sd->qw);
+    d.sc0x = sd->scales;
+  }
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
   st = launch_gemv(d, p.max_items * d.tiles, stream);
   if (st != W4A16_OK) return st;
   if (p.mfma) {
     if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma_prep(hraw, W4A16_F32, R, p.Mp, I, p.P, nullptr, 0, heavy, aph, rsh, stream);
+    st = launch_mfma_prep(hraw, W4A16_F32, T, p.Mp, I, p.P, nullptr, 0, heavy, aph, rsh, stream);
     if (st != W4A16_OK) return st;
     MfmaArgs md = ma;
     md.ap = aph;
@@ -448,6 +534,11 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     md.mode = 0;
     md.out = o;
     md.h = nullptr;
+    md.extra_plus1 = d.extra_plus1;
+    md.qw0x = d.qw0x;
+    md.sc0x = d.sc0x;
+    md.qw1x = nullptr;
+    md.sc1x = nullptr;
     if ((st = ev.mark(stream)) != W4A16_OK) return st;
     st = launch_mfma(md, p.P, p.max_mitems * md.tiles, stream);
     if (st != W4A16_OK) return st;
@@ -457,7 +548,8 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
   const size_t total = static_cast<size_t>(M) * (H / 4);
   combine_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(o, inv, topk_w, M,
-                                                                                  top_k, H, y);
+                                                                                  top_k, H, shared ? R : -1,
+                                                                                  y);
   if ((st = launch_status()) != W4A16_OK) return st;
   return ev.mark(stream);
 }
@@ -470,7 +562,19 @@ extern "C" w4a16_status_t w4a16_moe_grouped(const void* x, w4a16_dtype_t xt, int
                                             float* y, void* ws, size_t ws_bytes,
                                             hipStream_t stream) {
   EventMarks none;
-  return moe_impl(x, xt, M, topk_ids, topk_w, top_k, gate, up, down, y, ws, ws_bytes, stream, none);
+  return moe_impl(x, xt, M, topk_ids, topk_w, top_k, gate, up, down, nullptr, nullptr, nullptr, y, ws,
+                  ws_bytes, stream, none);
+}
+
+extern "C" w4a16_status_t w4a16_moe_grouped_shared(
+    const void* x, w4a16_dtype_t xt, int32_t M, const int32_t* topk_ids, const float* topk_w,
+    int32_t top_k, const w4a16_weight_t* gate, const w4a16_weight_t* up, const w4a16_weight_t* down,
+    const w4a16_weight_t* shared_gate, const w4a16_weight_t* shared_up, const w4a16_weight_t* shared_down,
+    float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (shared_gate == nullptr || shared_up == nullptr || shared_down == nullptr) return W4A16_ERR_INVALID_ARG;
+  EventMarks none;
+  return moe_impl(x, xt, M, topk_ids, topk_w, top_k, gate, up, down, shared_gate, shared_up, shared_down, y,
+                  ws, ws_bytes, stream, none);
 }
 
 extern "C" w4a16_status_t w4a16_moe_grouped_timed(
@@ -482,8 +586,8 @@ extern "C" w4a16_status_t w4a16_moe_grouped_timed(
   EventMarks ev;
   ev.events = events;
   ev.capacity = capacity;
-  w4a16_status_t st =
-      moe_impl(x, xt, M, topk_ids, topk_w, top_k, gate, up, down, y, ws, ws_bytes, stream, ev);
+  w4a16_status_t st = moe_impl(x, xt, M, topk_ids, topk_w, top_k, gate, up, down, nullptr, nullptr, nullptr,
+                                y, ws, ws_bytes, stream, ev);
   if (recorded != nullptr) *recorded = ev.recorded;
   return st;
 }

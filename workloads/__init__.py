@@ -41,6 +41,7 @@ class Config:
     top_k: int = 0
     routing: str = ""    # "uniform" | "zipf"
     zipf_alpha: float = 0.0
+    shared: bool = False  # MoE layer with one shared expert of the experts' shape
 
 
 CONFIGS = {
@@ -50,11 +51,19 @@ CONFIGS = {
     "mlp_verify_m64_bf16": Config("mlp_verify_m64_bf16", 2, "mlp", 64, 7168, 18432, "bf16"),
     "moe_decode_m64": Config("moe_decode_m64", 3, "moe", 64, 7168, 2048, "bf16", 384, 8, "uniform"),
     "moe_prefill_m2048": Config("moe_prefill_m2048", 4, "moe", 2048, 7168, 2048, "bf16", 384, 8, "zipf", 1.1),
+    "moe_decode_m64_shared": Config("moe_decode_m64_shared", 3, "moe", 64, 7168, 2048, "bf16", 384, 8, "uniform",
+                                    shared=True),
+    "moe_prefill_m2048_shared": Config("moe_prefill_m2048_shared", 4, "moe", 2048, 7168, 2048, "bf16", 384, 8,
+                                       "zipf", 1.1, shared=True),
     "gemm_m2048_hot_expert": Config("gemm_m2048_hot_expert", 5, "gemm", 2048, 7168, 4096, "bf16"),
     # router (top-k gating) ahead of the two MoE layers: float32 logits [M][384]
     "router_m64": Config("router_m64", 3, "router", 64, 0, 0, "f32", 384, 8),
     "router_m2048": Config("router_m2048", 4, "router", 2048, 0, 0, "f32", 384, 8),
 }
+
+
+# expert index of a shared expert's weight streams (the routed experts use 0 .. E-1)
+SHARED_EXPERT_INDEX = 10_000
 
 
 def seed_of(config: int, tag: int, index: int = 0) -> int:
