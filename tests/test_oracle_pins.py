@@ -407,3 +407,53 @@ def test_moe_shared_special_cases():
         assert np.allclose(y[t], want, rtol=0, atol=1e-13 * np.abs(want).max())
     sub = O.moe_shared64(x, ids, w, ex, E, sh, tokens=[4, 1])
     assert np.allclose(sub, y[[4, 1]], rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- other group sizes (64, 128)
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_quantizer_invariants_other_group_sizes(group):
+    """One scale per `group` rows: every nonzero group reaches |q| = 7, the
+    scale is the group's max|w| / 7 in float32, and |w - q*s| <= s/2."""
+    rng = np.random.default_rng(group)
+    K, N = 1024, 48
+    w = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    qw, sc = O.quantize_w4a16(w, group)
+    assert sc.shape == (K // group, N)
+    q = O.unpack(qw).astype(np.int64)
+    assert (np.abs(q).reshape(K // group, group, N).max(axis=1) == 7).all()
+    m = np.abs(w).reshape(K // group, group, N).max(axis=1)
+    assert np.array_equal(sc, (m / np.float32(7.0)).astype(np.float32))
+    s = np.repeat(sc, group, axis=0).astype(np.float64)
+    err = np.abs(w.astype(np.float64) - q * s)
+    assert (err <= 0.5 * s * (1 + 1e-12)).all()
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_quantizer_power_of_two_groups_are_exact_other_sizes(group):
+    rng = np.random.default_rng(group + 1)
+    K, N = 512, 8
+    q = rng.integers(-7, 8, size=(K, N))
+    q[::group, :] = 7
+    s = np.ldexp(1.0, rng.integers(-12, 0, size=(K // group, N)))
+    w = (q * np.repeat(s, group, axis=0)).astype(np.float32)
+    qw, sc = O.quantize_w4a16(w, group)
+    assert np.array_equal(O.unpack(qw), q)
+    assert np.array_equal(sc.astype(np.float64), s)
+
+
+@pytest.mark.parametrize("M,K,N,group", [(2, 128, 3, 64), (1, 256, 2, 128), (2, 256, 3, 64)])
+def test_gemm64_brute_force_other_group_sizes(M, K, N, group):
+    """The scale of row k is sc[k // group]: a Fraction loop with that index."""
+    rng = np.random.default_rng(M * 7 + K + group)
+    x = _dyadic(rng, (M, K), 6, -3, 3)
+    q = rng.integers(-8, 8, size=(K, N))
+    qw = O.pack_nibbles(q + 8)
+    sc = np.abs(_dyadic(rng, (K // group, N), 6, -8, -2)) + np.float32(2.0 ** -8)
+    y = O.gemm64(x, qw, sc)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(x[m, k])) * int(q[k, n]) * Fraction(float(sc[k // group, n]))
+            assert Fraction(float(y[m, n])) == acc, (m, n)
