@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
   W4A16_OK = 0,
   W4A16_ERR_INVALID_ARG = 1, /* null/misaligned pointer, negative size, bad id range */
-  W4A16_ERR_UNSUPPORTED = 2, /* group size != 32, K % 32 != 0, N % 64 != 0, wrong layout */
+  W4A16_ERR_UNSUPPORTED = 2, /* group size not 32/64/128, K % group != 0, N % 64 != 0, wrong layout */
   W4A16_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace_bytes query */
   W4A16_ERR_HIP = 4          /* a HIP launch or runtime call failed */
 } w4a16_status_t;
@@ -64,23 +64,27 @@ typedef enum { W4A16_F32 = 0, W4A16_BF16 = 1 } w4a16_dtype_t;
  *  CANONICAL: qw[E][K/8][N]; nibble j (bits 4j..4j+3) of word (i, n) holds row
  *             k = 8i + j.  This is the interchange format written by a
  *             quantizer (w4a16_quantize).
- *  GROUPED:   qw[E][K/32][N/64][64][4]; for scale group g and 64-column
+ *  GROUPED:   qw[E][K/32][N/64][64][4]; for 32-row block g and 64-column
  *             block j, the 16-byte slot 16b + l (b = 0..3, l = 0..15) holds
  *             canonical word 4g + b (rows 32g + 8b .. 32g + 8b + 7) of the
  *             columns 64j + 4l .. 64j + 4l + 3, in column order.  One matrix
- *             core lane reads one slot per group: its four columns' codes for
- *             one 8-row block.  Compute entry points read this layout only;
+ *             core lane reads one slot per block: its four columns' codes for
+ *             one 8-row block.  The code layout does not depend on the group
+ *             size.  Compute entry points read this layout only;
  *             w4a16_prepack converts.
- * Scales are sc[E][K/32][N] float32 in both layouts.
+ * Scales are sc[E][K/group_size][N] float32 in both layouts: row k of
+ * column n uses sc[e][k / group_size][n].  Group sizes 32, 64 and 128 are
+ * supported (the pages target 32; page "The First Line of Code", section
+ * "What the Edit Actually Does", calls the group size configurable).
  */
 typedef enum { W4A16_LAYOUT_CANONICAL = 0, W4A16_LAYOUT_GROUPED = 1 } w4a16_layout_t;
 
 typedef struct {
   const int32_t* qw;       /* device: packed codes, layout per `layout` */
-  const float* scales;     /* device: sc[E][K/32][N] */
-  int32_t K;               /* input dim, multiple of 32 */
+  const float* scales;     /* device: sc[E][K/group_size][N] */
+  int32_t K;               /* input dim, multiple of group_size */
   int32_t N;               /* output dim, multiple of 64 */
-  int32_t group_size;      /* must be 32 */
+  int32_t group_size;      /* rows per scale: 32, 64 or 128 */
   int32_t num_experts;     /* 1 for a dense weight; E for an expert stack */
   w4a16_layout_t layout;
 } w4a16_weight_t;
@@ -110,13 +114,22 @@ W4A16_API w4a16_status_t w4a16_quantize(const float* w, int32_t K, int32_t N, in
                               int32_t* qw, float* scales, hipStream_t stream);
 
 /*
+ * w4a16_quantize with group_size rows per scale (32, 64 or 128): scales are
+ * sc[E][K/group_size][N], scale = max|w| / 7 over each group, codes as above.
+ * Errors as w4a16_quantize, plus UNSUPPORTED for another group size or
+ * K % group_size != 0.
+ */
+W4A16_API w4a16_status_t w4a16_quantize_group(const float* w, int32_t K, int32_t N, int32_t num_experts,
+                                    int32_t group_size, int32_t* qw, float* scales, hipStream_t stream);
+
+/*
  * Permute CANONICAL codes into the GROUPED layout the compute kernels stream
  * (one-time load step; the weight and scale maps of page "The Final Wire",
  * section "The Multi-Step Integration Chain").  Scales are not moved: `out`
  * receives a GROUPED descriptor that points at `dst_qw` and at src->scales.
  * dst_qw must hold src->num_experts * K * N / 8 int32 and must not overlap
  * src->qw.  Errors: INVALID_ARG (null/misaligned, out == NULL, overlap),
- * UNSUPPORTED (src not CANONICAL, group size, K % 32, N % 64).
+ * UNSUPPORTED (src not CANONICAL, group size, K % group size, N % 64).
  */
 W4A16_API w4a16_status_t w4a16_prepack(const w4a16_weight_t* src, int32_t* dst_qw, w4a16_weight_t* out,
                              hipStream_t stream);
@@ -141,7 +154,7 @@ W4A16_API size_t w4a16_gemm_workspace_bytes(int32_t M, const w4a16_weight_t* w, 
  * matrix cores (all rows in one MFMA tile); larger M runs 64-row MFMA tiles.
  * Deterministic: the same inputs give bitwise the same y.
  * Errors: INVALID_ARG (null/misaligned, M < 0, bad dtype, y aliasing x),
- * UNSUPPORTED (layout, group size, K % 32, N % 64, num_experts != 1),
+ * UNSUPPORTED (layout, group size, K % group size, N % 64, num_experts != 1),
  * WORKSPACE (ws_bytes too small), HIP (launch failure).
  */
 W4A16_API w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M, const w4a16_weight_t* w,

@@ -26,6 +26,7 @@ EXPORTS = (
     "w4a16_status_string",
     "w4a16_workspace_init",
     "w4a16_quantize",
+    "w4a16_quantize_group",
     "w4a16_prepack",
     "w4a16_dequantize",
     "w4a16_gemm_workspace_bytes",
@@ -77,6 +78,7 @@ def load_library() -> ctypes.CDLL:
             "w4a16_status_string": (ctypes.c_char_p, [i32]),
             "w4a16_workspace_init": (i32, [vp, sz, vp]),
             "w4a16_quantize": (i32, [vp, i32, i32, i32, vp, vp, vp]),
+            "w4a16_quantize_group": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
             "w4a16_prepack": (i32, [dp, vp, dp, vp]),
             "w4a16_dequantize": (i32, [dp, vp, vp]),
             "w4a16_gemm_workspace_bytes": (sz, [i32, dp, i32]),
@@ -134,14 +136,15 @@ def _dtype_code(x: torch.Tensor) -> int:
 class Weight:
     """A W4A16 weight (or expert stack): codes, scales and their shape."""
     qw: torch.Tensor          # int32, CANONICAL [E][K/8][N] or GROUPED [E][K/32][N][4]
-    scales: torch.Tensor      # float32 [E][K/32][N]
+    scales: torch.Tensor      # float32 [E][K/group_size][N]
     K: int
     N: int
     num_experts: int = 1
     layout: int = LAYOUT_GROUPED
+    group_size: int = GROUP   # rows per scale: 32, 64 or 128
 
     def desc(self) -> WeightDesc:
-        return WeightDesc(self.qw.data_ptr(), self.scales.data_ptr(), self.K, self.N, GROUP,
+        return WeightDesc(self.qw.data_ptr(), self.scales.data_ptr(), self.K, self.N, self.group_size,
                           self.num_experts, self.layout)
 
 
@@ -156,19 +159,23 @@ def workspace_init(ws: torch.Tensor, stream=None):
                                                 _stream(stream)), "w4a16_workspace_init")
 
 
-def quantize(w: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor, stream=None):
-    """w float32 [E][K][N] (or [K][N]) -> CANONICAL qw, scales (caller-allocated)."""
+def quantize(w: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor, stream=None, group_size: int = GROUP):
+    """w float32 [E][K][N] (or [K][N]) -> CANONICAL qw, scales [E][K/group_size][N] (caller-allocated)."""
     E = 1 if w.dim() == 2 else w.shape[0]
     K, N = w.shape[-2], w.shape[-1]
-    _check(load_library().w4a16_quantize(_ptr(w), K, N, E, _ptr(qw), _ptr(scales), _stream(stream)),
-           "w4a16_quantize")
+    if group_size == GROUP:
+        st = load_library().w4a16_quantize(_ptr(w), K, N, E, _ptr(qw), _ptr(scales), _stream(stream))
+    else:
+        st = load_library().w4a16_quantize_group(_ptr(w), K, N, E, group_size, _ptr(qw), _ptr(scales),
+                                                 _stream(stream))
+    _check(st, "w4a16_quantize")
 
 
 def prepack(src: Weight, dst_qw: torch.Tensor, stream=None) -> Weight:
     out = WeightDesc()
     _check(load_library().w4a16_prepack(_dref(src), _ptr(dst_qw), ctypes.byref(out), _stream(stream)),
            "w4a16_prepack")
-    return Weight(dst_qw, src.scales, out.K, out.N, out.num_experts, out.layout)
+    return Weight(dst_qw, src.scales, out.K, out.N, out.num_experts, out.layout, out.group_size)
 
 
 def dequantize(w: Weight, out: torch.Tensor, stream=None):

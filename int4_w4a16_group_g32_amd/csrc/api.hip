@@ -77,6 +77,7 @@ MfmaArgs mfma_dense_args(const MfmaPlan& m, int rows, const w4a16_weight_t* w0,
   a.tiles = m.tiles;
   a.S = m.S;
   a.gps = m.gps;
+  a.gshift = group_shift(w0);
   a.dense_rows = rows;
   a.mode = mode;
   a.partials = reinterpret_cast<float*>(ws + partials_off);
@@ -188,6 +189,7 @@ GemvArgs gemv_dense_args(int M, const w4a16_weight_t* w0, const w4a16_weight_t* 
   a.tiles = tiles;
   a.S = S;
   a.gps = gps;
+  a.gshift = group_shift(w0);
   a.dense_rows = M;
   a.mode = mode;
   a.partials = reinterpret_cast<float*>(ws + partials_off);
@@ -253,6 +255,7 @@ w4a16_status_t check_mlp(const w4a16_weight_t* gate, const w4a16_weight_t* up,
   if ((st = check_dense_grouped(up)) != W4A16_OK) return st;
   if ((st = check_dense_grouped(down)) != W4A16_OK) return st;
   if (gate->K != up->K || gate->N != up->N) return W4A16_ERR_UNSUPPORTED;
+  if (gate->group_size != up->group_size) return W4A16_ERR_UNSUPPORTED;  // one launch streams both
   if (down->K != gate->N || down->N != gate->K) return W4A16_ERR_UNSUPPORTED;
   return W4A16_OK;
 }

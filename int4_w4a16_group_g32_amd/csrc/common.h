@@ -10,7 +10,8 @@
 
 namespace w4 {
 
-constexpr int kGroup = 32;       // rows of K that share one scale
+constexpr int kGroup = 32;       // rows of K in one code block (one MFMA k step); scale groups are
+                                 // kGroup << gshift rows, gshift = 0, 1, 2 (group size 32, 64, 128)
 constexpr int kWave = 64;        // CDNA wavefront width
 constexpr int kMaxGemvRows = 8;  // largest row count the GEMV kernels take per task
 
@@ -29,12 +30,15 @@ inline w4a16_status_t check_weight(const w4a16_weight_t* w) {
   if (w == nullptr || w->qw == nullptr || w->scales == nullptr) return W4A16_ERR_INVALID_ARG;
   if (!aligned16(w->qw) || !aligned16(w->scales)) return W4A16_ERR_INVALID_ARG;
   if (w->K < 0 || w->N < 0 || w->num_experts < 1) return W4A16_ERR_INVALID_ARG;
-  if (w->group_size != kGroup) return W4A16_ERR_UNSUPPORTED;
-  if (w->K % kGroup != 0 || w->N % 64 != 0) return W4A16_ERR_UNSUPPORTED;
+  if (w->group_size != 32 && w->group_size != 64 && w->group_size != 128) return W4A16_ERR_UNSUPPORTED;
+  if (w->K % w->group_size != 0 || w->N % 64 != 0) return W4A16_ERR_UNSUPPORTED;
   if (w->layout != W4A16_LAYOUT_CANONICAL && w->layout != W4A16_LAYOUT_GROUPED)
     return W4A16_ERR_UNSUPPORTED;
   return W4A16_OK;
 }
+
+// log2(group size / 32) of a weight that passed check_weight.
+inline int group_shift(const w4a16_weight_t* w) { return w->group_size == 128 ? 2 : (w->group_size == 64 ? 1 : 0); }
 
 // ---------------------------------------------------------------- device helpers
 

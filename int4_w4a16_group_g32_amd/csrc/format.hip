@@ -4,7 +4,8 @@
 // Format (web page "The Weight of Precision: Building Native INT4 Quantization
 // for a Custom Speculative Decoding Engine", section "The Kernel: w4a16_gemm"):
 // symmetric INT4 codes, value = nibble - 8, eight nibbles per int32 along K,
-// one float32 scale per 32-row group per output column.
+// one float32 scale per 32-row group per output column (64- and 128-row
+// groups are supported as well).
 #include "common.h"
 
 namespace w4 {
@@ -18,11 +19,12 @@ __global__ void fill_zero_kernel(uint4* __restrict__ p, size_t n16, uint8_t* __r
   if (i < ntail) tail[i] = 0;
 }
 
-// One thread per (expert, group, column).  Scale = max|w| / 7 rounded once in
-// float32; code = round-half-even of the float64 quotient, clamped to [-8, 7].
-__global__ void quantize_kernel(const float* __restrict__ w, int K, int N, int E,
+// One thread per (expert, scale group, column) of `group` rows (32, 64 or
+// 128).  Scale = max|w| / 7 rounded once in float32; code = round-half-even of
+// the float64 quotient, clamped to [-8, 7].
+__global__ void quantize_kernel(const float* __restrict__ w, int K, int N, int E, int group,
                                 int32_t* __restrict__ qw, float* __restrict__ sc) {
-  const int G = K / kGroup;
+  const int G = K / group;
   size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
   size_t total = static_cast<size_t>(E) * G * N;
   if (idx >= total) return;
@@ -30,23 +32,25 @@ __global__ void quantize_kernel(const float* __restrict__ w, int K, int N, int E
   const size_t eg = idx / N;  // e * G + g
   const size_t e = eg / G;
   const int g = static_cast<int>(eg % G);
-  const float* col = w + (e * K + static_cast<size_t>(g) * kGroup) * N + n;
+  const float* col = w + (e * K + static_cast<size_t>(g) * group) * N + n;
   float m = 0.0f;
-  for (int r = 0; r < kGroup; ++r) m = fmaxf(m, fabsf(col[static_cast<size_t>(r) * N]));
+  for (int r = 0; r < group; ++r) m = fmaxf(m, fabsf(col[static_cast<size_t>(r) * N]));
   const float s = __fdiv_rn(m, 7.0f);
   const double sd = static_cast<double>(s);
-  uint32_t words[4] = {0, 0, 0, 0};
-  for (int r = 0; r < kGroup; ++r) {
-    int q = 0;
-    if (s != 0.0f) {
-      double t = rint(static_cast<double>(col[static_cast<size_t>(r) * N]) / sd);
-      t = fmin(fmax(t, -8.0), 7.0);
-      q = static_cast<int>(t);
+  int32_t* out = qw + (e * (K / 8) + static_cast<size_t>(g) * (group / 8)) * N + n;
+  for (int b = 0; b < group / 8; ++b) {  // one code word per 8 rows
+    uint32_t word = 0;
+    for (int j = 0; j < 8; ++j) {
+      int q = 0;
+      if (s != 0.0f) {
+        double t = rint(static_cast<double>(col[static_cast<size_t>(8 * b + j) * N]) / sd);
+        t = fmin(fmax(t, -8.0), 7.0);
+        q = static_cast<int>(t);
+      }
+      word |= static_cast<uint32_t>(q + 8) << (4 * j);
     }
-    words[r >> 3] |= static_cast<uint32_t>(q + 8) << (4 * (r & 7));
+    out[static_cast<size_t>(b) * N] = static_cast<int32_t>(word);
   }
-  int32_t* out = qw + (e * (K / 8) + static_cast<size_t>(g) * 4) * N + n;
-  for (int j = 0; j < 4; ++j) out[static_cast<size_t>(j) * N] = static_cast<int32_t>(words[j]);
   sc[eg * N + n] = s;
 }
 
@@ -78,7 +82,7 @@ __global__ void prepack_kernel(const int32_t* __restrict__ src, int K, int N, in
 // One thread per (expert, word row, column): writes float32(q * s) for the
 // word's eight rows.  q * s is one IEEE float32 multiply of exact operands.
 __global__ void dequantize_kernel(const int32_t* __restrict__ qw, const float* __restrict__ sc,
-                                  int K, int N, int E, int grouped, float* __restrict__ out) {
+                                  int K, int N, int E, int group, int grouped, float* __restrict__ out) {
   const int W = K / 8;
   size_t idx = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
   size_t total = static_cast<size_t>(E) * W * N;
@@ -94,7 +98,7 @@ __global__ void dequantize_kernel(const int32_t* __restrict__ qw, const float* _
   } else {
     word = static_cast<uint32_t>(qw[ei * N + n]);
   }
-  const float s = sc[(e * (K / kGroup) + g) * N + n];
+  const float s = sc[(e * (K / group) + (8 * i) / group) * N + n];
   float* o = out + (e * K + static_cast<size_t>(i) * 8) * N + n;
   for (int j = 0; j < 8; ++j) {
     const float q = static_cast<float>(static_cast<int>((word >> (4 * j)) & 0xFu) - 8);
@@ -135,16 +139,23 @@ extern "C" w4a16_status_t w4a16_workspace_init(void* ws, size_t bytes, hipStream
   return launch_status();
 }
 
-extern "C" w4a16_status_t w4a16_quantize(const float* w, int32_t K, int32_t N, int32_t E,
-                                         int32_t* qw, float* scales, hipStream_t stream) {
+extern "C" w4a16_status_t w4a16_quantize_group(const float* w, int32_t K, int32_t N, int32_t E,
+                                               int32_t group_size, int32_t* qw, float* scales,
+                                               hipStream_t stream) {
   if (w == nullptr || qw == nullptr || scales == nullptr) return W4A16_ERR_INVALID_ARG;
   if (!aligned16(w) || !aligned16(qw) || !aligned16(scales)) return W4A16_ERR_INVALID_ARG;
   if (K < 0 || N < 0 || E < 0) return W4A16_ERR_INVALID_ARG;
-  if (K % kGroup != 0) return W4A16_ERR_UNSUPPORTED;
-  const size_t total = static_cast<size_t>(E) * (K / kGroup) * N;
+  if (group_size != 32 && group_size != 64 && group_size != 128) return W4A16_ERR_UNSUPPORTED;
+  if (K % group_size != 0) return W4A16_ERR_UNSUPPORTED;
+  const size_t total = static_cast<size_t>(E) * (K / group_size) * N;
   if (total == 0) return W4A16_OK;
-  quantize_kernel<<<grid_for(total, 256), 256, 0, stream>>>(w, K, N, E, qw, scales);
+  quantize_kernel<<<grid_for(total, 256), 256, 0, stream>>>(w, K, N, E, group_size, qw, scales);
   return launch_status();
+}
+
+extern "C" w4a16_status_t w4a16_quantize(const float* w, int32_t K, int32_t N, int32_t E,
+                                         int32_t* qw, float* scales, hipStream_t stream) {
+  return w4a16_quantize_group(w, K, N, E, 32, qw, scales, stream);
 }
 
 extern "C" w4a16_status_t w4a16_prepack(const w4a16_weight_t* src, int32_t* dst_qw,
@@ -175,6 +186,6 @@ extern "C" w4a16_status_t w4a16_dequantize(const w4a16_weight_t* w, float* out,
   const size_t total = static_cast<size_t>(w->num_experts) * (w->K / 8) * w->N;
   if (total == 0) return W4A16_OK;
   dequantize_kernel<<<grid_for(total, 256), 256, 0, stream>>>(
-      w->qw, w->scales, w->K, w->N, w->num_experts, w->layout == W4A16_LAYOUT_GROUPED, out);
+      w->qw, w->scales, w->K, w->N, w->num_experts, w->group_size, w->layout == W4A16_LAYOUT_GROUPED, out);
   return launch_status();
 }

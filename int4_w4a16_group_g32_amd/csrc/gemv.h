@@ -18,7 +18,8 @@ struct GemvArgs {
   const float* sc0;
   const u32x4* qw1;     // matrix 1 (up) for the SwiGLU mode, else null
   const float* sc1;
-  size_t expert_stride;  // chunks (and scales) per expert: G * N
+  size_t expert_stride;  // chunks per expert: G * N (scales per expert: expert_stride >> gshift)
+  int gshift;            // scale group = 32 << gshift rows: scale row of code block g is g >> gshift
   // One more expert with weights of its own (the shared expert of an MoE
   // layer): id extra_plus1 - 1 reads these instead of the stacks (0: none).
   int extra_plus1;

@@ -156,10 +156,10 @@ struct GroupCodes {
 // prefetch past the end re-reads a group that is still in cache instead of
 // branching): the lane's 16-byte GROUPED slot and its four scales.
 __device__ __forceinline__ void load_group(const u32x4* __restrict__ wp, const f32x4* __restrict__ sp,
-                                           size_t gstride, int g, int g_last, GroupCodes& c) {
+                                           size_t gstride, int g, int g_last, int gshift, GroupCodes& c) {
   const size_t gg = static_cast<size_t>(min(g, g_last));
   const u32x4 w = __builtin_nontemporal_load(wp + gg * gstride);
-  const f32x4 v = __builtin_nontemporal_load(sp + gg * (gstride / 4));
+  const f32x4 v = __builtin_nontemporal_load(sp + (gg >> gshift) * (gstride / 4));
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     c.w[cb] = w[cb];
@@ -261,7 +261,7 @@ void gemv_kernel(const GemvArgs a) {
   const int cbase = wave_ok ? c0 : 0;
   const bool xe = expert + 1 == a.extra_plus1;
   const u32x4* qb = xe ? (mat ? a.qw1x : a.qw0x) : (mat ? a.qw1 : a.qw0) + ebase;
-  const float* sb = xe ? (mat ? a.sc1x : a.sc0x) : (mat ? a.sc1 : a.sc0) + ebase;
+  const float* sb = xe ? (mat ? a.sc1x : a.sc0x) : (mat ? a.sc1 : a.sc0) + (ebase >> a.gshift);
   const u32x4* wp = qb + cbase + 16 * kb + lc;
   const f32x4* sp = reinterpret_cast<const f32x4*>(sb + cbase + 4 * lc);
   const size_t gstride = static_cast<size_t>(a.N);  // chunks (and scales) per group row
@@ -281,7 +281,7 @@ void gemv_kernel(const GemvArgs a) {
   // nothing: the ring loads stay unconditional, so the compiler's waits can
   // count them.
 #pragma unroll
-  for (int j = 0; j < kRing; ++j) load_group(wp, sp, gstride, g_lo + j, g_last, ring[j]);
+  for (int j = 0; j < kRing; ++j) load_group(wp, sp, gstride, g_lo + j, g_last, a.gshift, ring[j]);
 
   for (int gw = g_lo; gw < g_hi; gw += kWin) {
     const int nw = min(kWin, g_hi - gw);
@@ -305,7 +305,7 @@ void gemv_kernel(const GemvArgs a) {
         for (int j = 0; j < kRing; ++j) {
           const bool on = gl + j < nw;
           mma_group(lds, on ? gl + j : gl, lc, kb, arow && on, magic, ring[j], acc);
-          load_group(wp, sp, gstride, gw + gl + j + kRing, g_last, ring[j]);
+          load_group(wp, sp, gstride, gw + gl + j + kRing, g_last, a.gshift, ring[j]);
           // keep each refill right behind its consumer: the scheduler would
           // otherwise sink all refills to the end and drain the ring
           __builtin_amdgcn_sched_barrier(0);

@@ -162,10 +162,10 @@ struct TileCodes {
 };
 
 __device__ __forceinline__ void load_tile_codes(const u32x4* wp, const float* sp, size_t gstride, int g,
-                                                int g_last, TileCodes& c) {
+                                                int g_last, int gshift, TileCodes& c) {
   const size_t gg = static_cast<size_t>(min(g, g_last));
   c.w = __builtin_nontemporal_load(wp + gg * gstride);
-  c.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + gg * gstride));
+  c.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (gg >> gshift) * gstride));
 }
 
 // One group of the tile: the live row blocks (nrb of 4, wave-uniform) x 4
@@ -297,7 +297,7 @@ void mfma_kernel(const MfmaArgs a) {
   const size_t ebase = static_cast<size_t>(expert) * a.expert_stride;
   const bool xe = expert + 1 == a.extra_plus1;
   const u32x4* qb = xe ? (mat ? a.qw1x : a.qw0x) : (mat ? a.qw1 : a.qw0) + ebase;
-  const float* sb = xe ? (mat ? a.sc1x : a.sc0x) : (mat ? a.sc1 : a.sc0) + ebase;
+  const float* sb = xe ? (mat ? a.sc1x : a.sc0x) : (mat ? a.sc1 : a.sc0) + (ebase >> a.gshift);
   const u32x4* wp = qb + (wave_ok ? chunk : 0);
   const float* sp = sb + (wave_ok ? col0 : 0);
   const size_t gstride = static_cast<size_t>(a.N);  // chunks (and scales) per group row
@@ -321,7 +321,7 @@ void mfma_kernel(const MfmaArgs a) {
   load_a_window<P>(a, pos0, g_lo, g_hi, ra);
 #pragma unroll
   for (int j = 0; j < kTileRing; ++j) {
-    load_tile_codes(wp, sp, gstride, g_lo + j, g_last, ring[j]);
+    load_tile_codes(wp, sp, gstride, g_lo + j, g_last, a.gshift, ring[j]);
     __builtin_amdgcn_sched_barrier(0);  // issue order = use order
   }
   // live 16-row blocks of the tile (items hold 1 .. 64 rows)
@@ -352,7 +352,7 @@ void mfma_kernel(const MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < kGw; ++j) {
       mma_tile_group<P>(lds.a[h], j, lc, kb, magic, ring[kGw * h + j], nrb, cexp, acc);
-      load_tile_codes(wp, sp, gstride, gw + j + kTileRing, g_last, ring[kGw * h + j]);
+      load_tile_codes(wp, sp, gstride, gw + j + kTileRing, g_last, a.gshift, ring[kGw * h + j]);
       __builtin_amdgcn_sched_barrier(0);
     }
     store_a_window<P>(lds.a[1 - h], gw + kGw, g_hi, ra);

@@ -316,17 +316,19 @@ w4a16_status_t check_moe(const w4a16_weight_t* gate, const w4a16_weight_t* up,
   if (gate->num_experts != up->num_experts || gate->num_experts != down->num_experts)
     return W4A16_ERR_UNSUPPORTED;
   if (gate->K != up->K || gate->N != up->N) return W4A16_ERR_UNSUPPORTED;
+  if (gate->group_size != up->group_size) return W4A16_ERR_UNSUPPORTED;  // one launch streams both
   if (down->K != gate->N || down->N != gate->K) return W4A16_ERR_UNSUPPORTED;
   return W4A16_OK;
 }
 
-// A shared expert: one SwiGLU MLP of the routed experts' shapes, GROUPED.
-w4a16_status_t check_shared(const w4a16_weight_t* gate, const w4a16_weight_t* sg, const w4a16_weight_t* su,
-                            const w4a16_weight_t* sd) {
+// A shared expert: one SwiGLU MLP of the routed experts' shapes and group sizes, GROUPED.
+w4a16_status_t check_shared(const w4a16_weight_t* gate, const w4a16_weight_t* down, const w4a16_weight_t* sg,
+                            const w4a16_weight_t* su, const w4a16_weight_t* sd) {
   const w4a16_status_t st = check_moe(sg, su, sd);
   if (st != W4A16_OK) return st;
   if (sg->num_experts != 1) return W4A16_ERR_UNSUPPORTED;
   if (sg->K != gate->K || sg->N != gate->N) return W4A16_ERR_UNSUPPORTED;
+  if (sg->group_size != gate->group_size || sd->group_size != down->group_size) return W4A16_ERR_UNSUPPORTED;
   return W4A16_OK;
 }
 
@@ -366,7 +368,7 @@ extern "C" size_t w4a16_moe_shared_workspace_bytes(int32_t M, int32_t top_k, w4a
                                                    const w4a16_weight_t* shared_up,
                                                    const w4a16_weight_t* shared_down) {
   if (M <= 0 || top_k < 1 || check_moe(gate, up, down) != W4A16_OK) return 0;
-  if (check_shared(gate, shared_gate, shared_up, shared_down) != W4A16_OK) return 0;
+  if (check_shared(gate, down, shared_gate, shared_up, shared_down) != W4A16_OK) return 0;
   if (xt != W4A16_F32 && xt != W4A16_BF16) return 0;
   return plan_moe(M, top_k, xt, gate, true).bytes;
 }
@@ -381,7 +383,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   w4a16_status_t st = check_moe(gate, up, down);
   if (st != W4A16_OK) return st;
   const bool shared = sg != nullptr;
-  if (shared && (st = check_shared(gate, sg, su, sd)) != W4A16_OK) return st;
+  if (shared && (st = check_shared(gate, down, sg, su, sd)) != W4A16_OK) return st;
   const int E = gate->num_experts, H = gate->K, I = gate->N;
   if (M < 0 || top_k < 1 || top_k > E || (xt != W4A16_F32 && xt != W4A16_BF16))
     return W4A16_ERR_INVALID_ARG;
@@ -429,6 +431,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   a.qw1 = reinterpret_cast<const u32x4*>(up->qw);
   a.sc1 = up->scales;
   a.expert_stride = static_cast<size_t>(H / kGroup) * I;
+  a.gshift = group_shift(gate);
   a.N = I;
   a.tiles = gemv_shape(p.max_items, I, 1, H / kGroup, 0).tiles;
   a.S = 1;
@@ -468,6 +471,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     ma.qw1 = a.qw1;
     ma.sc1 = a.sc1;
     ma.expert_stride = a.expert_stride;
+    ma.gshift = a.gshift;
     ma.N = I;
     ma.tiles = (I + kMfmaCols / 2 - 1) / (kMfmaCols / 2);
     ma.S = 1;
@@ -497,6 +501,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   d.qw0 = reinterpret_cast<const u32x4*>(down->qw);
   d.sc0 = down->scales;
   d.expert_stride = static_cast<size_t>(I / kGroup) * H;
+  d.gshift = group_shift(down);
   d.N = H;
   d.tiles = gemv_shape(p.max_items, H, 0, I / kGroup, 0).tiles;
   d.S = 1;
@@ -528,6 +533,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     md.qw1 = nullptr;
     md.sc1 = nullptr;
     md.expert_stride = d.expert_stride;
+    md.gshift = d.gshift;
     md.N = H;
     md.tiles = (H + kMfmaCols - 1) / kMfmaCols;
     md.gps = md.G;

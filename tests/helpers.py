@@ -32,13 +32,14 @@ def weight_from_codes(qw_np: np.ndarray, sc_np: np.ndarray) -> L.Weight:
     if qw_np.ndim == 2:
         qw_np, sc_np = qw_np[None], sc_np[None]
     E, Kw, N = qw_np.shape
-    canon = L.Weight(to_dev(qw_np), to_dev(sc_np), Kw * 8, N, E, L.LAYOUT_CANONICAL)
+    group = Kw * 8 // sc_np.shape[1]  # rows per scale, from the scales' shape
+    canon = L.Weight(to_dev(qw_np), to_dev(sc_np), Kw * 8, N, E, L.LAYOUT_CANONICAL, group)
     return L.prepack(canon, torch.empty_like(canon.qw))
 
 
-def oracle_quantize_stack(ws):
+def oracle_quantize_stack(ws, group=32):
     """Oracle-quantize a list of float32 [K][N] matrices into stacked codes and scales."""
-    qs, ss = zip(*(O.quantize_w4a16(w) for w in ws))
+    qs, ss = zip(*(O.quantize_w4a16(w, group) for w in ws))
     return np.stack(qs), np.stack(ss)
 
 

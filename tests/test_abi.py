@@ -55,8 +55,10 @@ def test_workspace_queries_are_host_only(lib):
     n = lib.w4a16_gemm_workspace_bytes(4, ctypes.byref(d), L.F32)
     assert n > 0 and n % 256 == 0
     assert lib.w4a16_gemm_workspace_bytes(0, ctypes.byref(d), L.F32) == 0
-    bad = _desc(group=64)
-    assert lib.w4a16_gemm_workspace_bytes(4, ctypes.byref(bad), L.F32) == 0
+    for g in (16, 96, 256):  # 32, 64 and 128 are the supported group sizes
+        bad = _desc(group=g)
+        assert lib.w4a16_gemm_workspace_bytes(4, ctypes.byref(bad), L.F32) == 0
+    assert lib.w4a16_gemm_workspace_bytes(4, ctypes.byref(_desc(K=7168, N=18432, group=128)), L.F32) > 0
     g, u, dn = _desc(7168, 18432), _desc(7168, 18432), _desc(18432, 7168)
     assert lib.w4a16_swiglu_mlp_workspace_bytes(4, L.F32, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn)) > 0
     mismatched = _desc(18432, 4096)
@@ -67,7 +69,8 @@ def test_workspace_queries_are_host_only(lib):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("group_size", 64, L.ERR_UNSUPPORTED),
+    ("group_size", 96, L.ERR_UNSUPPORTED),
+    ("group_size", 16, L.ERR_UNSUPPORTED),
     ("K", 48, L.ERR_UNSUPPORTED),
     ("N", 96, L.ERR_UNSUPPORTED),
     ("layout", L.LAYOUT_CANONICAL, L.ERR_UNSUPPORTED),
