@@ -313,6 +313,43 @@ def run_moe_shared(args, cfg, stacks, ids, ids_np, wts, x, y):
     }
 
 
+def run_gemm(args, cfg):
+    """One w4a16_gemm call per step (dense weight, M x K x N).  Reported as
+    TFLOP/s against the bf16 dense MFMA peak when M >= 512, else as GB/s."""
+    import torch
+    import int4_w4a16_group_g32_amd as L
+    import workloads as W
+
+    M, K, N = cfg.M, cfg.K, cfg.N
+    xt = L.F32 if cfg.x_dtype == "f32" else L.BF16
+    xbytes = 4 if cfg.x_dtype == "f32" else 2
+    copies = []
+    for c in range(max(1, args.copies)):
+        copies.append(L.quantize_to_weight(W.weights(K, N, cfg.index, W.TAG_GATE, c, device="cuda")))
+    x = W.activations(M, K, cfg.index, cfg.x_dtype, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = L.new_workspace(L.gemm_workspace_bytes(M, copies[0], xt))
+
+    def step(i):
+        L.gemm(x, copies[i % len(copies)], y, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    ms_step = timed_steps_ms(args, step)
+    flops = 2.0 * M * K * N
+    step_bytes = K * N * 5 // 8 + M * K * xbytes + M * N * 4
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    big = M >= 512
+    return {
+        "metric": METRIC, "value": round(tflops if big else gbs, 2), "unit": "TFLOP/s" if big else "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.x_dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "M": M, "K": K, "N": N, "bytes_per_step": step_bytes, "flops_per_step": flops},
+        "pct_mfma_peak_bf16": round(100 * tflops / 2500.0, 1), "gbs": round(gbs, 1),
+    }
+
+
 def run_router(args, cfg):
     """One router call per step: float32 logits [M][E] -> top-k ids and
     softmax gate weights.  A few MB at most, so the figure is latency."""
@@ -445,6 +482,8 @@ def main():
         result = run_moe(args, cfg)
     elif cfg.kind == "router":
         result = run_router(args, cfg)
+    elif cfg.kind == "gemm":
+        result = run_gemm(args, cfg)
     else:
         print(f"workload {cfg.name} has no bench line", file=sys.stderr)
         sys.exit(2)
