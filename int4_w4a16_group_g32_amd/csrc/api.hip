@@ -18,7 +18,33 @@ size_t gemv_partial_bytes(size_t tasks, int S) {
   return S > 1 ? tasks * S * kPartialTileFloats * sizeof(float) : 0;
 }
 
-MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt) {
+MfmaPlan plan_wide(int rows, int N, int K) {
+  MfmaPlan m;
+  m.wide = true;
+  m.P = 1;
+  m.Mp = static_cast<int>(round_up(static_cast<size_t>(rows), kWideRows));
+  m.items = static_cast<size_t>(m.Mp / kWideRows);
+  m.tiles = (N + kWideCols - 1) / kWideCols;
+  m.tasks = m.items * m.tiles;
+  const int G = K / kGroup;
+  // split K until the grid holds about one workgroup per CU, keeping at least
+  // 16 groups per split
+  int S = 1;
+  while (m.tasks * (S + 1) <= static_cast<size_t>(kWideResidentWgs) && (S + 1) * 16 <= G && S + 1 <= kMaxSplits &&
+         m.tasks * (S + 1) * sizeof(int) <= kCounterBytes)
+    ++S;
+  if (m.tasks * sizeof(int) > kCounterBytes) S = 1;
+  // an even number of groups per split (G is even): whole two-group windows
+  m.gps = G > 0 ? ((G + S - 1) / S + 1) / 2 * 2 : 2;
+  m.S = G > 0 ? (G + m.gps - 1) / m.gps : 1;
+  return m;
+}
+
+MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt, bool allow_wide) {
+  // (the wide kernel's buffer offsets are 32-bit: codes under 2 GiB)
+  if (allow_wide && xt == W4A16_BF16 && mode == 0 && rows >= W4_WIDE_MIN_ROWS && K % 64 == 0 &&
+      static_cast<size_t>(K) * N / 2 < (size_t{1} << 31))
+    return plan_wide(rows, N, K);
   MfmaPlan m;
   m.P = mfma_pieces(xt);
   m.Mp = mfma_rows_padded(rows);
@@ -55,6 +81,7 @@ MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt) {
 }
 
 size_t mfma_partial_bytes(const MfmaPlan& m) {
+  if (m.wide) return m.S > 1 ? m.tasks * m.S * static_cast<size_t>(kWideRows) * kWideCols * sizeof(float) : 0;
   return m.S > 1 ? m.tasks * m.S * static_cast<size_t>(kMfmaRows) * kMfmaCols * sizeof(float) : 0;
 }
 
@@ -89,10 +116,11 @@ GemmPlan plan_gemm(int M, const w4a16_weight_t* w, w4a16_dtype_t xt) {
   GemmPlan p;
   if (M > kMaxGemvRows) {
     p.mfma = true;
-    p.mf = plan_mfma(M, w->N, 0, w->K, xt);
+    p.mf = plan_mfma(M, w->N, 0, w->K, xt, true);
     Carve c;
     c.take(p.counters_off, kCounterBytes);
-    c.take(p.ap_off, static_cast<size_t>(p.mf.P) * p.mf.Mp * w->K * 2);
+    // (wide tiles read up to 128 bytes past the piece plane: padded)
+    c.take(p.ap_off, static_cast<size_t>(p.mf.P) * p.mf.Mp * w->K * 2 + (p.mf.wide ? 256 : 0));
     c.take(p.rs_off, static_cast<size_t>(p.mf.Mp) * 4);
     c.take(p.partials_off, mfma_partial_bytes(p.mf));
     p.bytes = c.cursor;
@@ -117,8 +145,8 @@ MlpPlan plan_mlp(int M, w4a16_dtype_t xt, const w4a16_weight_t* gate, const w4a1
   if (M > kMaxGemvRows) {
     const int H = gate->K, I = gate->N;
     p.mfma = true;
-    p.gu = plan_mfma(M, I, 1, H, xt);
-    p.dn = plan_mfma(M, down->N, 0, I, xt);
+    p.gu = plan_mfma(M, I, 1, H, xt, false);
+    p.dn = plan_mfma(M, down->N, 0, I, xt, false);
     const int P = p.gu.P, Mp = p.gu.Mp;
     Carve c;
     c.take(p.counters_off, kCounterBytes);
@@ -229,6 +257,7 @@ extern "C" w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M,
     if (st != W4A16_OK) return st;
     MfmaArgs a = mfma_dense_args(p.mf, M, w, nullptr, 0, ap, rs, wsb, p.partials_off, p.counters_off);
     a.out = y;
+    if (p.mf.wide) return launch_wide(a, p.mf.tasks * p.mf.S, stream);
     return launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream);
   }
   if (!counters_fit(p.tasks, p.S)) return W4A16_ERR_UNSUPPORTED;

@@ -18,10 +18,12 @@ struct Carve {
 
 // MFMA path (rows above the GEMV range)
 struct MfmaPlan {
+  bool wide = false;  // wide tiles (256 x 128) instead of 64 x 256
   int P = 0, Mp = 0, tiles = 0, S = 1, gps = 0;
   size_t items = 0, tasks = 0;
 };
-MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt);
+// allow_wide: the caller launches wide tiles when the plan says so
+MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt, bool allow_wide);
 
 struct GemmPlan {
   int S = 1, gps = 1;

@@ -27,6 +27,16 @@ constexpr int kMfmaThreads = 256;
 #define W4_MFMA_PARTIAL_CAP 0.5  // partial-tile traffic cap, a fraction of the weight bytes
 #endif
 constexpr int kMfmaResidentWgs = 512;
+
+// Wide tiles (wide.hip): 256 rows x 128 columns per workgroup, bf16
+// activations, dense rows, plain output; taken from W4_WIDE_MIN_ROWS rows on.
+constexpr int kWideRows = 256;
+constexpr int kWideCols = 128;
+constexpr int kWideThreads = 256;
+#ifndef W4_WIDE_MIN_ROWS
+#define W4_WIDE_MIN_ROWS 256
+#endif
+constexpr int kWideResidentWgs = 256;  // one per CU
 constexpr int kMfmaWgOverheadGroups = W4_MFMA_WG_OVERHEAD_GROUPS;
 
 struct MfmaArgs {
@@ -68,6 +78,9 @@ w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, 
                                 const int* gather, int top_k, const int* need, _Float16* ap,
                                 float* rs, hipStream_t stream);
 w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream_t stream);
+// Wide-tile launch (mode 0, dense rows, Mp a multiple of kWideRows); a.tiles
+// counts 128-column tiles.
+w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stream);
 
 // Rows of the piece planes for R positions.
 inline int mfma_rows_padded(int R) { return (R + kMfmaRows - 1) / kMfmaRows * kMfmaRows + kMfmaRows; }

@@ -1,0 +1,411 @@
+// Wide MFMA tiles for large row counts with bf16 activations.
+//
+// y[m][n] = sum_g s[g][n] * sum_{k in g} x[m][k] * q[k][n]   (page "The Weight
+// of Precision: Building Native INT4 Quantization for a Custom Speculative
+// Decoding Engine", section "The Kernel: w4a16_gemm").
+//
+// The operands are those of the 64-row tile kernel's one-piece mode: A is the
+// f16 piece of x * 2^e per row (mfma.h), B the weights expanded to
+// f16(q * f16(s * 2^c)), accumulated by v_mfma_f32_16x16x32_f16 in float32 and
+// brought back by 2^-c per column and 2^-e per row at the end.  Here c is fixed
+// per column for the whole launch: the workgroup first reads the column's
+// scales over all of K and puts the largest in [1/2, 1), so no product can
+// leave the f16 range and no accumulator ever needs rescaling.
+//
+// A workgroup computes 256 rows x 128 columns.  Wave (wr, wc) = (wv >> 1,
+// wv & 1) owns rows 128wr .. +127 and columns 64wc .. +63: 8 x 4 MFMA blocks
+// of 16 x 16, so every expanded weight feeds 8 MFMAs, twice the 64-row tile's
+// reuse, and the vector work per matrix-core instruction halves.  The 256 x 64
+// activation window (two groups) is staged once in LDS and read by the two
+// waves of each row half; each wave streams its own 64 columns of codes, one
+// 16-byte GROUPED slot per lane and group.
+//
+// Workgroups are numbered so that each XCD (the hardware deals workgroup b to
+// XCD b mod 8) takes a contiguous run of tiles, row tile major: the column
+// tiles of one row tile then share that XCD's L2 for their activations.
+#include <type_traits>
+
+#include "mfma.h"
+#include "mfma_ops.h"
+
+namespace w4 {
+namespace {
+
+constexpr int kWw = 2;                                     // groups per staged activation window
+constexpr int kWideRing = 2 * kWw;                         // groups of codes in flight per wave
+constexpr int kWideWinUnits = kWw * kWideRows * 4;         // 16-byte units per window
+constexpr int kWideUnitsPerThread = kWideWinUnits / kWideThreads;
+constexpr int kAnchorBatch = 16;                           // scale loads in flight per thread
+constexpr int kXcds = 8;
+constexpr int kAhead = 3;                                  // A fragments read ahead of their MFMAs
+
+// Raw buffer resources: a wave-uniform base and size in scalar registers, so a
+// load takes one 32-bit lane offset and a scalar offset (no 64-bit address
+// arithmetic per load).  The size check covers the lane offset only, not the
+// scalar one, so every scalar offset below is kept inside its buffer.
+constexpr int kBufFlags = 0x00020000;  // dword 3 of a raw buffer resource on gfx9
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  const int n = bytes >= 0x7fffffffu ? 0x7fffffff : static_cast<int>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufFlags);
+}
+
+// Unit (gl, row, kb) of a window: the four 16-byte k blocks of a row are
+// permuted by a 2-bit function of the row so that the 8 (or 16) lanes one LDS
+// cycle serves, rows r .. r+7 (r .. r+15) of one k block for an A fragment
+// read, fall in distinct 16-byte bank groups whether the LDS has 32 or 64
+// banks; the staging stores (two rows x four k blocks per 8 lanes) are
+// conflict-free with any such permutation.
+__device__ __forceinline__ int a_swz(int row) { return (((row >> 1) ^ (row >> 3)) & 1) | ((row >> 1) & 2); }
+__device__ __forceinline__ int w_off(int gl, int row, int kb) {
+  return (gl * kWideRows + row) * 4 + (kb ^ a_swz(row));
+}
+
+struct WideLds {
+  uint4 a[2][kWideWinUnits];  // double buffer, 2 x 32 KiB
+  float red[8][kWideCols];    // anchor reduction
+  int cexp[kWideCols];
+  int last;
+};
+
+// Staging: thread t handles units u = t + 256 i, k block u & 3, row
+// 8 (u >> 6) + ((u >> 2) & 7), group (u >> 5) & 1: each 8 lanes two rows of
+// one group, each wave 8 rows x both groups.  The lane offset holds t's row,
+// group and k block; the scalar offset the window's first group and 32 i
+// rows.  The prefetch after a split's last window reads the next split's
+// activations, or past the end of the row (at most 128 bytes past the last
+// row of the plane, which the workspace pads), and is never used.
+__device__ __forceinline__ int stage_row(int u) { return 8 * (u >> 6) + ((u >> 2) & 7); }
+
+__device__ __forceinline__ void wide_load_a(__amdgpu_buffer_rsrc_t ra_src, int voff, int K, int gw,
+                                            uint4 r[kWideUnitsPerThread]) {
+#pragma unroll
+  for (int i = 0; i < kWideUnitsPerThread; ++i)
+    r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, voff, (gw * kGroup + 32 * i * K) * 2, 0));
+}
+
+// Every split holds an even number of groups (the launch checks it), so a
+// window is always whole.
+__device__ __forceinline__ void wide_store_a(uint4* buf, const uint4 r[kWideUnitsPerThread]) {
+#pragma unroll
+  for (int i = 0; i < kWideUnitsPerThread; ++i) {
+    const int u = static_cast<int>(threadIdx.x) + kWideThreads * i;
+    buf[w_off((u >> 5) & 1, stage_row(u), u & 3)] = r[i];
+  }
+}
+
+struct WideCodes {
+  u32x4 w;  // word kb of the lane's four columns
+  f32x4 s;  // their scales
+};
+
+// Codes and scales of group g (wave-uniform): the lane offsets are fixed, the
+// group moves the scalar offset.  Prefetches past the matrix's last group
+// re-read that group.
+__device__ __forceinline__ void wide_load_codes(__amdgpu_buffer_rsrc_t wsrc, __amdgpu_buffer_rsrc_t ssrc, int wvoff,
+                                                int svoff, int N, int g_req, int g_max, int gshift, WideCodes& c) {
+  const int g = min(g_req, g_max);
+  c.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wsrc, wvoff, g * N * 16, 0));
+  c.s = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ssrc, svoff, (g >> gshift) * N * 4, 0));
+}
+
+// The matrix-core step with the accumulator tied in place (the compiler's
+// own form writes a fresh register and copies it back every loop trip).
+// Being opaque to the compiler, it gets no hazard padding: every use below
+// keeps its operands' producers and consumers well apart, and the kernel
+// pads the accumulators' first write and last read itself.
+__device__ __forceinline__ void mfma_tied(f32x4& acc, const half8& a, const half8& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Expansion of one code word and its anchored scale into
+// f16(q * f16(s * 2^c)), k order 0,4,1,5,2,6,3,7 (the A pieces' order), cut
+// into eight steps of one or two vector instructions that the main loop
+// spreads between its MFMAs.  A nibble under an f16 exponent of 0x6400 reads
+// as 1024 + n (bits 0..3) or 1024 + 16 n (bits 4..7): one packed subtract of
+// 1032, or one packed fma (x / 16 - 72), leaves n - 8 exactly.
+struct WordExp {
+  half2v h, p0, p1, p2, p3;
+  uint32_t hi;
+};
+
+template <int kStep>
+__device__ __forceinline__ void expand_step(uint32_t w, float s, int ce, uint32_t magic, WordExp& e, half8& out) {
+  const half2v sub = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+  const half2v sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+  const half2v off = {static_cast<_Float16>(-72.0f), static_cast<_Float16>(-72.0f)};
+  if constexpr (kStep == 0) {
+    const _Float16 hh = static_cast<_Float16>(ldexpf(s, ce));
+    e.h = half2v{hh, hh};
+  } else if constexpr (kStep == 1) {
+    e.p0 = __builtin_bit_cast(half2v, (w & 0x000f000fu) | magic) + sub;
+  } else if constexpr (kStep == 2) {
+    e.p1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, (w & 0x00f000f0u) | magic), sixteenth, off);
+  } else if constexpr (kStep == 3) {
+    e.hi = w >> 8;
+    e.p2 = __builtin_bit_cast(half2v, (e.hi & 0x000f000fu) | magic) + sub;
+  } else if constexpr (kStep == 4) {
+    e.p3 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, (e.hi & 0x00f000f0u) | magic), sixteenth, off);
+  } else if constexpr (kStep == 5) {
+    e.p0 = e.p0 * e.h;
+    e.p1 = e.p1 * e.h;
+  } else if constexpr (kStep == 6) {
+    e.p2 = e.p2 * e.h;
+    e.p3 = e.p3 * e.h;
+  } else {
+    out = half8{e.p0[0], e.p0[1], e.p1[0], e.p1[1], e.p2[0], e.p2[1], e.p3[0], e.p3[1]};
+  }
+}
+
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void wide_kernel(const MfmaArgs a) {
+  __shared__ WideLds lds;
+  const int t = static_cast<int>(threadIdx.x);
+
+  // XCD-aware task order: XCD x = b mod 8 takes tasks x*q + min(x, r) + b / 8
+  // of T = 8q + r, a bijection onto 0 .. T-1 for b < T.
+  const int T = static_cast<int>(gridDim.x);
+  const int b = static_cast<int>(blockIdx.x);
+  const int xcd = b % kXcds, q = T / kXcds, rem = T % kXcds;
+  const int task = xcd * q + min(xcd, rem) + b / kXcds;
+  const int split = task % a.S;
+  const int rest = task / a.S;
+  const int tile = rest % a.tiles;
+  const int item = rest / a.tiles;
+  const int row0 = item * kWideRows;
+
+  const int wv = wave_id();
+  const int lane = lane_id();
+  const int lc = lane & 15, kb = lane >> 4;
+  const int wr = wv >> 1, wc = wv & 1;
+  const uint32_t magic = magic_vgpr();
+
+  const int c0 = tile * kWideCols + wc * 64;
+  const bool wave_ok = c0 < a.N;
+  const int col0 = c0 + 4 * lc;
+  const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(a.qw0, static_cast<size_t>(a.G) * a.N * 16);
+  const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(a.sc0, static_cast<size_t>(a.G >> a.gshift) * a.N * 4);
+  const int wvoff = ((wave_ok ? c0 : 0) + 16 * kb + lc) * 16;
+  const int svoff = (wave_ok ? col0 : 4 * lc) * 4;
+  const __amdgpu_buffer_rsrc_t asrc =
+      make_rsrc(a.ap + static_cast<size_t>(row0) * a.K, static_cast<size_t>(kWideRows) * a.K * 2);
+  const int avoff = (stage_row(t) * a.K + ((t >> 5) & 1) * kGroup + 8 * (t & 3)) * 2;  // unit t of the staging map
+
+  const int g_lo = split * a.gps;
+  const int g_hi = min(a.G, g_lo + a.gps);
+  const int nwin = (g_hi - g_lo + kWw - 1) / kWw;
+
+  uint4 ra[kWideUnitsPerThread];
+  WideCodes ring[kWideRing];
+  wide_load_a(asrc, avoff, a.K, g_lo, ra);
+#pragma unroll
+  for (int j = 0; j < kWideRing; ++j) {
+    wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, g_lo + j, a.G - 1, a.gshift, ring[j]);
+    __builtin_amdgcn_sched_barrier(0);  // issue order = use order
+  }
+
+  // Column anchors over every scale row of K: thread t reads columns
+  // 4(t & 31) .. +3 of the tile at scale rows t >> 5, + 8, ... (rows past the
+  // end are clamped to the last one; a repeated row leaves a maximum as it is).
+  {
+    const int cq = t & 31, r0 = t >> 5;
+    const int ccol = tile * kWideCols + 4 * cq;
+    const int ccl = ccol < a.N ? ccol : 0;
+    const int rows = a.G >> a.gshift;
+    f32x4 mx = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = r0; r < rows; r += 8 * kAnchorBatch) {
+      f32x4 v[kAnchorBatch];
+      // rows past the end are clamped to the last one, which leaves a maximum as it is
+#pragma unroll
+      for (int j = 0; j < kAnchorBatch; ++j)
+        v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             ssrc, (min(r + 8 * j, rows - 1) * a.N + ccl) * 4, 0, 0));
+#pragma unroll
+      for (int j = 0; j < kAnchorBatch; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx[e] = fmaxf(mx[e], fabsf(v[j][e]));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lds.red[r0][4 * cq + e] = mx[e];
+    __syncthreads();
+    if (t < kWideCols) {
+      float m = lds.red[0][t];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) m = fmaxf(m, lds.red[j][t]);
+      lds.cexp[t] = m > 0.0f ? -__builtin_amdgcn_frexp_expf(m) : 0;
+    }
+  }
+  wide_store_a(lds.a[0], ra);
+  __syncthreads();
+  int cexp[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) cexp[cb] = lds.cexp[wc * 64 + 4 * lc + cb];
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Window wi uses LDS buffer and ring half h = wi % 2; the loop body is two
+  // whole windows and an odd last window runs after it, so every path into
+  // the loop header has the same loads outstanding.  A window is a run of 16
+  // row-block steps (two groups x 8 row blocks), each one A fragment read
+  // (kAhead steps ahead) and 4 MFMAs; between the MFMAs run the steps of the
+  // next group's expansion (its codes are consumed one group early, and the
+  // slot is refilled with group g + kWideRing when the group ends).  The
+  // schedule is pinned with scheduling barriers.
+  half8 bq[2][4];  // expanded weights, by group parity (the loop body holds an even number of groups)
+  {
+    WordExp e;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      expand_step<0>(ring[0].w[cb], ring[0].s[cb], cexp[cb], magic, e, bq[0][cb]);
+      expand_step<1>(ring[0].w[cb], ring[0].s[cb], cexp[cb], magic, e, bq[0][cb]);
+      expand_step<2>(ring[0].w[cb], ring[0].s[cb], cexp[cb], magic, e, bq[0][cb]);
+      expand_step<3>(ring[0].w[cb], ring[0].s[cb], cexp[cb], magic, e, bq[0][cb]);
+      expand_step<4>(ring[0].w[cb], ring[0].s[cb], cexp[cb], magic, e, bq[0][cb]);
+      expand_step<5>(ring[0].w[cb], ring[0].s[cb], cexp[cb], magic, e, bq[0][cb]);
+      expand_step<6>(ring[0].w[cb], ring[0].s[cb], cexp[cb], magic, e, bq[0][cb]);
+      expand_step<7>(ring[0].w[cb], ring[0].s[cb], cexp[cb], magic, e, bq[0][cb]);
+    }
+  }
+  wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, g_lo + kWideRing, a.G - 1, a.gshift, ring[0]);
+  // the accumulators were just written by vector instructions: pad before
+  // the first (opaque) MFMA reads them
+  asm volatile("s_nop 7\n\ts_nop 7");
+  auto window = [&](int wi, auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const int gw = g_lo + wi * kWw;
+    wide_load_a(asrc, avoff, a.K, gw + kWw, ra);  // the next window, in flight
+    const uint4* buf = lds.a[h];
+    auto rd = [&](int st) {
+      return __builtin_bit_cast(half8, buf[w_off(st >> 3, wr * 128 + (st & 7) * 16 + lc, kb)]);
+    };
+    half8 af[4];
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st) af[st] = rd(st);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kWw; ++j) {
+      constexpr int kBody = 2 * kWw;  // groups per loop body
+      const int cur = (kWw * h + j) & 1;
+      const int nslot = (kWw * h + j + 1) % kWideRing;
+      static_assert(kBody % kWideRing == 0, "ring slots repeat with the loop body");
+      WordExp e;
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb) {
+        const int st = 8 * j + rb;
+        if (st + kAhead < 8 * kWw) af[(st + kAhead) & 3] = rd(st + kAhead);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          mfma_tied(acc[rb][cb], af[st & 3], bq[cur][cb]);
+          // expansion step (rb * 4 + cb) % 8 of word (rb * 4 + cb) / 8
+          const int x = rb * 4 + cb, word = x >> 3;
+          const uint32_t wd = ring[nslot].w[word];
+          const float sc = ring[nslot].s[word];
+          half8& o = bq[cur ^ 1][word];
+          switch (x & 7) {
+            case 0: expand_step<0>(wd, sc, cexp[word], magic, e, o); break;
+            case 1: expand_step<1>(wd, sc, cexp[word], magic, e, o); break;
+            case 2: expand_step<2>(wd, sc, cexp[word], magic, e, o); break;
+            case 3: expand_step<3>(wd, sc, cexp[word], magic, e, o); break;
+            case 4: expand_step<4>(wd, sc, cexp[word], magic, e, o); break;
+            case 5: expand_step<5>(wd, sc, cexp[word], magic, e, o); break;
+            case 6: expand_step<6>(wd, sc, cexp[word], magic, e, o); break;
+            default: expand_step<7>(wd, sc, cexp[word], magic, e, o); break;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, gw + j + 1 + kWideRing, a.G - 1, a.gshift, ring[nslot]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wide_store_a(lds.a[1 - h], ra);
+    __syncthreads();
+  };
+  int w = 0;
+  for (; w + 1 < nwin; w += 2) {
+    window(w, std::integral_constant<int, 0>{});
+    window(w + 1, std::integral_constant<int, 1>{});
+  }
+  if (w < nwin) window(w, std::integral_constant<int, 0>{});
+  // the last (opaque) MFMAs' results are read by vector instructions below
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+
+  // Split-K: write-through partials [j][thread], j = (rb * 4 + cb) * 4 + i, an
+  // agent-scope arrival counter, and the last workgroup sums the partials in
+  // split order, 64 loads per thread in flight.
+  if (a.S > 1) {
+    const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
+    const size_t tf = static_cast<size_t>(kWideRows) * kWideCols;
+    float* base = a.partials + ct * a.S * tf + t;
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kWideThreads, acc[rb][cb][i],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t == 0)
+      lds.last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  a.S - 1);
+    __syncthreads();
+    if (!lds.last) return;
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < a.S; ++s) {
+      const float* ps = base + static_cast<size_t>(s) * tf;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float p[64];
+#pragma unroll
+        for (int e = 0; e < 64; ++e)
+          p[e] = __hip_atomic_load(ps + (hh * 64 + e) * kWideThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int e = 0; e < 64; ++e) {
+          const int j = hh * 64 + e;
+          acc[j >> 4][(j >> 2) & 3][j & 3] += p[e];
+        }
+      }
+    }
+    if (t == 0) __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (!wave_ok) return;
+
+  // lane (lc, kb) holds rows rb*16 + 4kb + i of columns col0 .. col0 + 3 (the
+  // four column blocks): one 16-byte store per row
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + wr * 128 + rb * 16 + 4 * kb + i;
+      if (r < a.dense_rows) {
+        const float f = a.rs[r];
+        float4 o;
+        o.x = ldexpf(acc[rb][0][i], -cexp[0]) * f;
+        o.y = ldexpf(acc[rb][1][i], -cexp[1]) * f;
+        o.z = ldexpf(acc[rb][2][i], -cexp[2]) * f;
+        o.w = ldexpf(acc[rb][3][i], -cexp[3]) * f;
+        *reinterpret_cast<float4*>(a.out + static_cast<size_t>(r) * a.N + col0) = o;
+      }
+    }
+}
+
+}  // namespace
+
+w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stream) {
+  if (num_tasks == 0) return W4A16_OK;
+  if (num_tasks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
+  if (a.mode != 0 || a.dense_rows <= 0 || a.Mp % kWideRows != 0 || a.G % kWw != 0 || a.gps % kWw != 0)
+    return W4A16_ERR_UNSUPPORTED;
+  wide_kernel<<<static_cast<unsigned>(num_tasks), kWideThreads, 0, stream>>>(a);
+  return launch_status();
+}
+
+}  // namespace w4

@@ -125,3 +125,55 @@ def test_gemm_bf16_tiles_hold_any_scale_range(M, spread, base):
     err = rel_err(y, O.gemm64(x_values(x), qw, sc))
     print(f"gemm bf16 M={M} spread={spread} base={base:g} relF={err:.3e}", flush=True)
     assert err <= 1e-2
+
+
+# Row counts from 256 up take the wide tiles (256 x 128 per workgroup) for bf16
+# activations: ragged row tiles, a column count that leaves a tile's second
+# wave without columns (N = 64, 192), K splits (K = 7168 over few tiles) and
+# a single group (K = 32).
+@pytest.mark.parametrize("K,N", [(32, 64), (256, 192), (1024, 512), (7168, 256)])
+@pytest.mark.parametrize("M", [256, 300, 513, 1000])
+def test_gemm_wide_tiles(M, K, N):
+    qw, sc, w = _make(K, N, 500 + K + N)
+    x = x_for_dtype(W.activations(M, K, 500 + M).cuda(), "bf16")
+    y, _ = _run_gemm(x, w, N)
+    ref = O.gemm64(x_values(x), qw, sc)
+    err = rel_err(y, ref)
+    print(f"gemm wide M={M} K={K} N={N} bf16 relF={err:.3e}", flush=True)
+    assert err <= tol_for("bf16")
+
+
+@pytest.mark.parametrize("M", [256, 1000])
+@pytest.mark.parametrize("spread,base", [(0, 1e-30), (20, 1.0), (40, 1.0)])
+def test_gemm_wide_tiles_hold_any_scale_range(M, spread, base):
+    """The wide tiles' per-column anchor over all of K keeps every product in
+    the f16 range for any float32 scales; groups far below a column's largest
+    scale keep an absolute precision of about 2^-25 of it."""
+    K, N = 1024, 192
+    qw, sc = _wide_scales(K, N, 900 + spread, spread, base)
+    w = weight_from_codes(qw, sc)
+    x = x_for_dtype(W.activations(M, K, 910 + M).cuda(), "bf16")
+    y, _ = _run_gemm(x, w, N)
+    ref = O.gemm64(x_values(x), qw, sc)
+    err = rel_err(y, ref)
+    print(f"gemm wide M={M} spread={spread} base={base:g} relF={err:.3e}", flush=True)
+    assert np.isfinite(y.cpu().numpy()).all()
+    assert err <= tol_for("bf16")
+
+
+def test_gemm_hot_expert_full_size():
+    """The hot-expert GEMM (2048 x 7168 -> 4096, bf16): weights drawn on the
+    GPU and quantized by the library; 64 sampled rows against the oracle
+    applied to the oracle's own quantization of the same weights."""
+    cfg = W.CONFIGS["gemm_m2048_hot_expert"]
+    wt = W.weights(cfg.K, cfg.N, cfg.index, W.TAG_GATE, device="cuda")
+    w = L.quantize_to_weight(wt)
+    qw, sc = O.quantize_w4a16(wt.cpu().numpy())
+    del wt
+    x = x_for_dtype(W.activations(cfg.M, cfg.K, cfg.index).cuda(), "bf16")
+    y, _ = _run_gemm(x, w, cfg.N)
+    rows = np.sort(np.random.default_rng(cfg.M).choice(cfg.M, size=64, replace=False))
+    ref = O.gemm64(x_values(x)[rows], qw, sc)
+    err = rel_err(y[torch.as_tensor(rows, device="cuda")], ref)
+    print(f"gemm_m2048_hot_expert relF={err:.3e} (64 sampled rows)", flush=True)
+    assert err <= tol_for("bf16")
