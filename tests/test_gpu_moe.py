@@ -89,6 +89,26 @@ def test_moe_small(M, E, k, H, I, routing, dtype):
     assert err <= tol_for(dtype)
 
 
+@pytest.mark.parametrize("M,E,k,H,I", [(600, 4, 2, 256, 192), (1000, 8, 3, 128, 128)])
+def test_moe_all_heavy_bf16(M, E, k, H, I):
+    """bf16 activations with every expert above 128 rows: only MFMA items, the
+    last of each expert ragged, I = 192 not a multiple of the tile's 128 h
+    columns."""
+    cfg = 520 + M
+    (gq, gs), (uq, us), (dq, ds) = _experts(E, H, I, cfg)
+    g, u, d = weight_from_codes(gq, gs), weight_from_codes(uq, us), weight_from_codes(dq, ds)
+    ids = W.topk_uniform(M, E, k, cfg)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert counts.min() >= 128 and (counts % 256 != 0).all()
+    wts = W.gate_weights(M, k, cfg)
+    x = x_for_dtype(W.activations(M, H, cfg).cuda(), "bf16")
+    y = _moe_gpu(x, to_dev(ids), to_dev(wts), g, u, d)
+    ref = O.moe64(x_values(x), ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E)
+    err = rel_err(y, ref)
+    print(f"moe all-heavy M={M} E={E} k={k} H={H} I={I} bf16 relF={err:.3e}", flush=True)
+    assert err <= tol_for("bf16")
+
+
 def _full_moe(name, sample_tokens):
     """Full expert stacks drawn and quantized on the GPU; the oracle regenerates
     and quantizes only the experts that the sampled tokens use."""
