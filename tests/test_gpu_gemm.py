@@ -74,6 +74,28 @@ def test_gemm_deterministic_and_workspace_reuse():
     assert np.array_equal(outs[0].view(np.uint32), outs[4].view(np.uint32))
 
 
+def test_gemm_bf16_deterministic_across_paths_and_workspace_reuse():
+    """bf16 activations through every path in turn on one workspace (GEMV,
+    64-row tiles, wide tiles with K splits, wide tiles without): each call
+    meets the bound, and repeating a shape gives the same bits, so split-K
+    counters are left at zero and the partial sums run in a fixed order."""
+    K, N = 7168, 256
+    qw, sc, w = _make(K, N, 303)
+    ms = (300, 4, 100, 1024, 300, 100)
+    ws = L.new_workspace(max(L.gemm_workspace_bytes(m, w, L.BF16) for m in ms))
+    outs = {}
+    for M in ms:
+        x = x_for_dtype(W.activations(M, K, 303 + M).cuda(), "bf16")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        L.gemm(x, w, y, ws)
+        torch.cuda.synchronize()
+        assert rel_err(y, O.gemm64(x_values(x), qw, sc)) <= tol_for("bf16")
+        got = y.cpu().numpy().view(np.uint32)
+        if M in outs:
+            assert np.array_equal(outs[M], got)
+        outs[M] = got
+
+
 def test_gemm_zero_rows_and_m0():
     K, N = 256, 128
     qw, sc, w = _make(K, N, 303)

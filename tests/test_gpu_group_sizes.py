@@ -55,8 +55,10 @@ def _gemm(x, w, N):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("group", [64, 128])
 @pytest.mark.parametrize("M,K,N", [(1, 256, 512), (4, 7168, 256), (8, 1024, 192), (9, 1024, 64), (64, 7168, 256),
-                                   (130, 512, 320)])
+                                   (130, 512, 320), (300, 1024, 192), (513, 7168, 256)])
 def test_gemm_other_group_sizes(M, K, N, group, dtype):
+    """Every GEMM path (GEMV, 64-row tiles, and from 256 bf16 rows the wide
+    tiles, with K splits at K = 7168) reads scale row k / group."""
     qw, sc = O.quantize_w4a16(W.weights(K, N, 960 + K + N, W.TAG_GATE).numpy(), group)
     w = weight_from_codes(qw, sc)
     x = x_for_dtype(W.activations(M, K, 961 + M).cuda(), dtype)
