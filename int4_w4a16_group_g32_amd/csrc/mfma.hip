@@ -21,7 +21,11 @@ namespace w4 {
 namespace {
 
 constexpr int kGw = 4;           // groups per staged activation window (double-buffered)
-constexpr int kTileRing = 2 * kGw;  // groups of codes in flight per wave
+constexpr int kTileRing = 2 * kGw;  // groups of codes in flight per wave (two windows)
+// Grouped launches (MoE items) hold many workgroups: they run three waves per
+// SIMD with a ring of one window, which the register budget of three waves
+// allows; dense launches keep two waves and two windows.
+constexpr int kGroupedRing = kGw;
 constexpr int kPrepThreads = 1024;
 
 // ------------------------------------------------------------ activation pieces
@@ -180,7 +184,7 @@ __device__ __forceinline__ void load_tile_codes(const u32x4* wp, const float* sp
 // (the lanes that share a column see the same scales and so keep the same
 // c), and the MFMA accumulates straight into the accumulators; the epilogue
 // multiplies by 2^-c.  c starts so that the largest scale of the split's first
-// kTileRing groups lands in [1/2, 1) (2^138 if they are all zero); a later
+// ring of groups lands in [1/2, 1) (2^138 if they are all zero); a later
 // group whose scaled value would reach 2^12 (where q * s could leave the f16
 // range) moves c to bring it to [1/2, 1) and rescales that column block's
 // accumulators by the same power of two, so no product overflows.  Each
@@ -247,8 +251,8 @@ __device__ __forceinline__ void mma_tile_group(const uint4* buf, int gl, int lc,
   }
 }
 
-template <int P>
-__global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <int P, int R, int kWaves>
+__global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(kWaves, kWaves)))
 void mfma_kernel(const MfmaArgs a) {
   __shared__ MfmaLds<P> lds;
   __shared__ int last;
@@ -313,14 +317,15 @@ void mfma_kernel(const MfmaArgs a) {
   const int g_last = g_hi - 1;
   const int nwin = (g_hi - g_lo + kGw - 1) / kGw;
   uint4 ra[kWinUnits<P> / kMfmaThreads];
-  // ring of kTileRing groups of codes in flight: group g_lo + i sits in slot
-  // i % kTileRing, two windows' worth, so a window always uses the same half
-  TileCodes ring[kTileRing];
+  // ring of R groups of codes in flight (one or two windows): group g_lo + i
+  // sits in slot i % R, so a window always uses the same slots
+  static_assert(R == kGw || R == 2 * kGw, "ring of one or two windows");
+  TileCodes ring[R];
   // A wave past the matrix's last column streams column block 0 and stores
   // nothing, so every load below is unconditional.
   load_a_window<P>(a, pos0, g_lo, g_hi, ra);
 #pragma unroll
-  for (int j = 0; j < kTileRing; ++j) {
+  for (int j = 0; j < R; ++j) {
     load_tile_codes(wp, sp, gstride, g_lo + j, g_last, a.gshift, ring[j]);
     __builtin_amdgcn_sched_barrier(0);  // issue order = use order
   }
@@ -331,7 +336,7 @@ void mfma_kernel(const MfmaArgs a) {
   if (P == 1) {
     f32x4 mx = ring[0].s;
 #pragma unroll
-    for (int j = 1; j < kTileRing; ++j)
+    for (int j = 1; j < R; ++j)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) mx[cb] = fmaxf(fabsf(mx[cb]), fabsf(ring[j].s[cb]));
     // an all-zero start takes the first nonzero group's anchor on arrival:
@@ -351,8 +356,8 @@ void mfma_kernel(const MfmaArgs a) {
     load_a_window<P>(a, pos0, gw + kGw, g_hi, ra);  // the next window, in flight
 #pragma unroll
     for (int j = 0; j < kGw; ++j) {
-      mma_tile_group<P>(lds.a[h], j, lc, kb, magic, ring[kGw * h + j], nrb, cexp, acc);
-      load_tile_codes(wp, sp, gstride, gw + j + kTileRing, g_last, a.gshift, ring[kGw * h + j]);
+      mma_tile_group<P>(lds.a[h], j, lc, kb, magic, ring[(kGw * h + j) % R], nrb, cexp, acc);
+      load_tile_codes(wp, sp, gstride, gw + j + R, g_last, a.gshift, ring[(kGw * h + j) % R]);
       __builtin_amdgcn_sched_barrier(0);
     }
     store_a_window<P>(lds.a[1 - h], gw + kGw, g_hi, ra);
@@ -480,14 +485,23 @@ w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, 
   return launch_status();
 }
 
+namespace {
+void launch_one_piece(const MfmaArgs& a, unsigned grid, hipStream_t stream) {
+  if (a.dense_rows > 0)
+    mfma_kernel<1, kTileRing, 2><<<grid, kMfmaThreads, 0, stream>>>(a);
+  else
+    mfma_kernel<1, kGroupedRing, 3><<<grid, kMfmaThreads, 0, stream>>>(a);
+}
+}  // namespace
+
 w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream_t stream) {
   if (num_tasks == 0) return W4A16_OK;
   if (num_tasks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   const unsigned grid = static_cast<unsigned>(num_tasks);
   if (P == 2)
-    mfma_kernel<2><<<grid, kMfmaThreads, 0, stream>>>(a);
+    mfma_kernel<2, kTileRing, 2><<<grid, kMfmaThreads, 0, stream>>>(a);
   else
-    mfma_kernel<1><<<grid, kMfmaThreads, 0, stream>>>(a);
+    launch_one_piece(a, grid, stream);
   return launch_status();
 }
 
