@@ -408,17 +408,20 @@ void mfma_kernel(const MfmaArgs a) {
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s0 = 0; s0 < a.S; s0 += 2) {
-      float p[2][64];
+    // partials in flight per round: two (128 loads per thread) at two waves
+    // per SIMD, one at three (its register budget)
+    constexpr int kB = kWaves >= 3 ? 1 : 2;
+    for (int s0 = 0; s0 < a.S; s0 += kB) {
+      float p[kB][64];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < kB; ++b) {
         const float* ps = base + static_cast<size_t>(min(s0 + b, a.S - 1)) * tf;
 #pragma unroll
         for (int e = 0; e < 64; ++e)
           p[b][e] = __hip_atomic_load(ps + e * kMfmaThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < kB; ++b) {
         if (s0 + b < a.S) {
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb)
