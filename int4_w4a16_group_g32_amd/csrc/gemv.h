@@ -63,6 +63,16 @@ GemvShape gemv_shape(size_t items, int N, int mode, int G, size_t max_split_task
 // floats of one split-K partial tile
 constexpr size_t kPartialTileFloats = static_cast<size_t>(kMaxGemvRows) * kGemvCols;
 
+#ifndef W4_GEMV_KT
+#define W4_GEMV_KT 0  // column tiles per workgroup; 0: chosen per launch
+#endif
+constexpr size_t kGemvResidentTasks = 1024;  // four-wave workgroups resident at once (4 per CU)
+constexpr size_t kGemvMinWorkgroups = 240;   // about one workgroup per CU
+
+// Column tiles per workgroup (1, 2 or 4 quads of four waves) for a launch of
+// num_tasks = items * tiles * S tasks.
+int gemv_tiles_per_workgroup(size_t num_tasks, int tiles);
+// num_tasks must be items * a.tiles * a.S.
 w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stream);
 
 }  // namespace w4

@@ -30,6 +30,10 @@
 namespace w4 {
 namespace {
 
+#ifndef W4_GEMV_PACE
+#define W4_GEMV_PACE 1
+#endif
+constexpr int kPace = W4_GEMV_PACE;      // ring rounds between pacing barriers (0: none)
 constexpr int kWin = 32;                 // groups per staging window
 #ifndef W4_GEMV_RING
 #define W4_GEMV_RING 4
@@ -44,8 +48,8 @@ struct GemvLds {
   float f[kMaxGemvRows];  // 2^-e per row for the current window
 };
 static_assert(kWin % kRing == 0, "ring slots must stay aligned across windows");
-static_assert(sizeof(uint4) * kWin * kUnitsPerGroup >= sizeof(float) * kMaxGemvRows * kGemvCols,
-              "tile buffer must fit in the staging buffer");
+static_assert(sizeof(uint4) * kWin * kUnitsPerGroup >= sizeof(float) * 4 * kMaxGemvRows * kGemvCols,
+              "the tile buffers of four quads must fit in the staging buffer");
 
 // k blocks are XOR-swizzled by row so the 16 rows of one k block fall in
 // distinct LDS banks.
@@ -53,22 +57,28 @@ __device__ __forceinline__ int a_unit(int g, int r, int kb) {
   return (g * 16 + r) * 4 + (kb ^ ((r >> 2) & 3));
 }
 
-// Staging of groups [gw, gw + nw) of rows pos0 .. pos0 + nrows - 1.  Wave wv
-// takes rows wv and wv + 4; lane l takes 16 consecutive activations of a row:
-// group l >> 1, k blocks 2(l & 1) and 2(l & 1) + 1.  The raw loads are split
-// from the conversion so they can be issued ahead of the weight prefetch
-// (vector loads complete in order).
-constexpr int kRowsPerWave = kMaxGemvRows / (kGemvThreads / kWave);
+// Staging of groups [gw, gw + nw) of rows pos0 .. pos0 + nrows - 1 by a
+// workgroup of kW waves.  Wave wv takes rows wv + j * kRowStride (waves past
+// the eighth stage nothing); lane l takes 16 consecutive activations of a
+// row: group l >> 1, k blocks 2(l & 1) and 2(l & 1) + 1.  The raw loads are
+// split from the conversion so they can be issued ahead of the weight
+// prefetch (vector loads complete in order).
+template <int kW>
+struct Staging {
+  static constexpr int kRowStride = kW < kMaxGemvRows ? kW : kMaxGemvRows;
+  static constexpr int kRowsPerWave = kMaxGemvRows / kRowStride;
+};
 
+template <int kW>
 __device__ __forceinline__ void load_window(const GemvArgs& a, int gw, int nw, int pos0, int nrows,
-                                            int wv, int lane, float v[kRowsPerWave][16]) {
+                                            int wv, int lane, float v[Staging<kW>::kRowsPerWave][16]) {
   const int gl = lane >> 1, hb = lane & 1;
 #pragma unroll
-  for (int j = 0; j < kRowsPerWave; ++j) {
-    const int m = wv + j * (kGemvThreads / kWave);
+  for (int j = 0; j < Staging<kW>::kRowsPerWave; ++j) {
+    const int m = wv + j * Staging<kW>::kRowStride;
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[j][i] = 0.0f;
-    if (m >= nrows) continue;
+    if (m >= nrows || wv >= kMaxGemvRows) continue;
     long src = pos0 + m;
     if (a.gather != nullptr) {
       const int pr = a.gather[pos0 + m];
@@ -105,12 +115,14 @@ __device__ __forceinline__ void load_window(const GemvArgs& a, int gw, int nw, i
 // Per row: the window's largest magnitude sets e (max * 2^e in [2^14, 2^15)),
 // the pieces of x * 2^e go to LDS in the A layout and 2^-e to lds.f.  Absent
 // rows get the factor 0 and are never read as A.
+template <int kW>
 __device__ __forceinline__ void convert_window(GemvLds& lds, int nw, int nrows, int wv, int lane,
-                                               const float v[kRowsPerWave][16]) {
+                                               const float v[Staging<kW>::kRowsPerWave][16]) {
   const int gl = lane >> 1, hb = lane & 1;
+  if (wv >= kMaxGemvRows) return;  // (wave-uniform) rows are staged by the first eight waves
 #pragma unroll
-  for (int j = 0; j < kRowsPerWave; ++j) {
-    const int m = wv + j * (kGemvThreads / kWave);
+  for (int j = 0; j < Staging<kW>::kRowsPerWave; ++j) {
+    const int m = wv + j * Staging<kW>::kRowStride;
     if (m >= nrows) {
       if (lane == 0) lds.f[m] = 0.0f;
       continue;
@@ -216,17 +228,24 @@ __device__ __forceinline__ void read_partials(const float* base, int S, int nrow
 
 // kMulti: the split spans more than one staging window (each window's
 // accumulators are scaled by its own 2^-e before they join the total).
-template <bool kMulti>
-__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(4)))
+// A workgroup is kT quads of four waves.  Quad q takes column tile
+// tg * kT + q of one item and one K split, so the quads share the staged
+// activation window and start streaming together (a later workgroup on a CU
+// would wait for its activations behind the weight streams of the ones
+// already running there).  A quad whose tile lies past the last one streams
+// column block 0 and stores nothing.
+template <bool kMulti, int kT>
+__global__ __launch_bounds__(kGemvThreads * kT) __attribute__((amdgpu_waves_per_eu(4)))
 void gemv_kernel(const GemvArgs a) {
+  constexpr int kW = 4 * kT;  // waves
   __shared__ GemvLds lds;
-  __shared__ int last;
+  __shared__ int last[kT];
 
+  const int tgs = (a.tiles + kT - 1) / kT;  // tile groups per item
   const int task = blockIdx.x;
   const int split = task % a.S;
   const int rest = task / a.S;
-  const int tile = rest % a.tiles;
-  const int item = rest / a.tiles;
+  const int item = rest / tgs;
 
   int expert = 0, pos0, nrows;
   if (a.dense_rows > 0) {
@@ -241,18 +260,21 @@ void gemv_kernel(const GemvArgs a) {
   }
 
   const int wv = wave_id();
+  const int q = wv >> 2, wq = wv & 3;  // quad, wave within the quad
+  const int tile = (rest % tgs) * kT + q;
+  const bool tile_ok = tile < a.tiles;
   const int lane = lane_id();
   const int lc = lane & 15, kb = lane >> 4;
-  // plain: wave wv owns columns tile*256 + 64wv ..; SwiGLU: waves 0, 1 the gate
-  // and waves 2, 3 the up columns tile*128 + 64(wv & 1) ..
+  // plain: wave wq owns columns tile*256 + 64wq ..; SwiGLU: waves 0, 1 the gate
+  // and waves 2, 3 the up columns tile*128 + 64(wq & 1) ..
   int mat = 0, c0;
   if (a.mode == 1) {
-    mat = wv >> 1;
-    c0 = tile * (kGemvCols / 2) + (wv & 1) * 64;
+    mat = wq >> 1;
+    c0 = tile * (kGemvCols / 2) + (wq & 1) * 64;
   } else {
-    c0 = tile * kGemvCols + wv * 64;
+    c0 = tile * kGemvCols + wq * 64;
   }
-  const bool wave_ok = c0 < a.N;
+  const bool wave_ok = tile_ok && c0 < a.N;
   const size_t ebase = static_cast<size_t>(expert) * a.expert_stride;
   const int g_lo = split * a.gps;
   const int g_hi = min(a.G, g_lo + a.gps);
@@ -275,8 +297,8 @@ void gemv_kernel(const GemvArgs a) {
   for (int cb = 0; cb < 4; ++cb) tot[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // ring of kRing groups in flight: group g sits in slot (g - g_lo) % kRing
   GroupCodes ring[kRing];
-  float xv[kRowsPerWave][16];
-  load_window(a, g_lo, min(kWin, g_hi - g_lo), pos0, nrows, wv, lane, xv);  // ahead of the weights
+  float xv[Staging<kW>::kRowsPerWave][16];
+  load_window<kW>(a, g_lo, min(kWin, g_hi - g_lo), pos0, nrows, wv, lane, xv);  // ahead of the weights
   // A wave past the matrix's last column streams column block 0 and stores
   // nothing: the ring loads stay unconditional, so the compiler's waits can
   // count them.
@@ -287,9 +309,9 @@ void gemv_kernel(const GemvArgs a) {
     const int nw = min(kWin, g_hi - gw);
     if (gw != g_lo) {
       __syncthreads();  // the previous window is consumed
-      load_window(a, gw, nw, pos0, nrows, wv, lane, xv);
+      load_window<kW>(a, gw, nw, pos0, nrows, wv, lane, xv);
     }
-    convert_window(lds, nw, nrows, wv, lane, xv);
+    convert_window<kW>(lds, nw, nrows, wv, lane, xv);
     __syncthreads();
     {
       f32x4 wacc[4];
@@ -310,6 +332,11 @@ void gemv_kernel(const GemvArgs a) {
           // otherwise sink all refills to the end and drain the ring
           __builtin_amdgcn_sched_barrier(0);
         }
+        // Pacing: each SIMD issues for its oldest wave first, so without a
+        // barrier the quads of a workgroup finish one after another and the
+        // CU's loads in flight fall off long before the end.  A bare barrier
+        // (no memory fence, so no wait on the ring) keeps them in step.
+        if (kT > 1 && kPace > 0 && (gl / kRing) % kPace == kPace - 1) __builtin_amdgcn_s_barrier();
       }
       // accumulator element i of this lane is A row 4kb + i: row (4kb + i) & 7
       const float4 f4 = *reinterpret_cast<const float4*>(&lds.f[4 * (kb & 1)]);
@@ -335,57 +362,71 @@ void gemv_kernel(const GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[cb][i] = tot[cb][i] + __shfl_xor(tot[cb][i], 32);
   __syncthreads();  // every wave is done with the staged activations
-  float* red = reinterpret_cast<float*>(lds.buf);  // [kMaxGemvRows][kGemvCols]
+  float* red = reinterpret_cast<float*>(lds.buf);  // [kT][kMaxGemvRows][kGemvCols]
   if (lane < 32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * kb + i;
       if (m < nrows) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) red[m * kGemvCols + wv * 64 + 4 * lc + cb] = pv[cb][i];
+        for (int cb = 0; cb < 4; ++cb)
+          red[(q * kMaxGemvRows + m) * kGemvCols + wq * 64 + 4 * lc + cb] = pv[cb][i];
       }
     }
   }
   __syncthreads();
 
-  // Thread t owns column t of the tile, rows 0 .. nrows - 1.
-  const int t = static_cast<int>(threadIdx.x);
+  // Thread t of quad tq owns column t of its tile, rows 0 .. nrows - 1.
+  const int tq = static_cast<int>(threadIdx.x) / kGemvThreads;
+  const int t = static_cast<int>(threadIdx.x) % kGemvThreads;
+  const int ttile = (rest % tgs) * kT + tq;
+  const bool ttile_ok = ttile < a.tiles;
+  float* tred = red + tq * kMaxGemvRows * kGemvCols;
   float v[kMaxGemvRows];
 #pragma unroll
-  for (int r = 0; r < kMaxGemvRows; ++r) v[r] = r < nrows ? red[r * kGemvCols + t] : 0.0f;
+  for (int r = 0; r < kMaxGemvRows; ++r) v[r] = r < nrows ? tred[r * kGemvCols + t] : 0.0f;
 
+  // Every thread reaches every barrier below; a quad that is not the last
+  // arriver of its tile only skips the stores.
+  bool mine = ttile_ok;
   if (a.S > 1) {
     // Partials are written through to the device coherence point (agent-scope
     // stores), the arrival counter is an agent-scope atomic, and the last
     // workgroup of the tile reads the partials back with agent-scope loads,
     // many in flight at once, and sums them in split order.
-    const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
+    const size_t ct = static_cast<size_t>(item) * a.tiles + (ttile_ok ? ttile : 0);
     const size_t tf = kPartialTileFloats;
     float* base = a.partials + ct * a.S * tf;
+    if (ttile_ok) {
 #pragma unroll
-    for (int r = 0; r < kMaxGemvRows; ++r)
-      if (r < nrows)
-        __hip_atomic_store(base + split * tf + r * kGemvCols + t, v[r], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      for (int r = 0; r < kMaxGemvRows; ++r)
+        if (r < nrows)
+          __hip_atomic_store(base + split * tf + r * kGemvCols + t, v[r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-      const int prev = __hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = (prev == a.S - 1);
+    if (t == 0) {
+      last[tq] = ttile_ok ? (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) == a.S - 1)
+                          : 0;
     }
     __syncthreads();
-    if (!last) return;
-    if (a.S <= 8)
-      read_partials<8>(base, a.S, nrows, t, v);
-    else
-      read_partials<16>(base, a.S, nrows, t, v);
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    mine = last[tq] != 0;
+    if (kT == 1 && !mine) return;  // a one-quad workgroup has no other quad to wait for
+    if (mine) {
+      if (a.S <= 8)
+        read_partials<8>(base, a.S, nrows, t, v);
+      else
+        read_partials<16>(base, a.S, nrows, t, v);
+      if (t == 0)
+        __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   if (a.mode == 0) {
-    const int n = tile * kGemvCols + t;
-    if (n < a.N) {
+    const int n = ttile * kGemvCols + t;
+    if (mine && n < a.N) {
 #pragma unroll
       for (int r = 0; r < kMaxGemvRows; ++r)
         if (r < nrows) a.out[static_cast<size_t>(pos0 + r) * a.N + n] = v[r];
@@ -393,17 +434,19 @@ void gemv_kernel(const GemvArgs a) {
     return;
   }
   // SwiGLU: columns 0..127 of the tile are gate, 128..255 the matching up columns
+  if (mine) {
 #pragma unroll
-  for (int r = 0; r < kMaxGemvRows; ++r)
-    if (r < nrows) red[r * kGemvCols + t] = v[r];
+    for (int r = 0; r < kMaxGemvRows; ++r)
+      if (r < nrows) tred[r * kGemvCols + t] = v[r];
+  }
   __syncthreads();
-  const int n = tile * (kGemvCols / 2) + t;
-  if (t < kGemvCols / 2 && n < a.N) {
+  const int n = ttile * (kGemvCols / 2) + t;
+  if (mine && t < kGemvCols / 2 && n < a.N) {
 #pragma unroll
     for (int r = 0; r < kMaxGemvRows; ++r)
       if (r < nrows)
         a.h[static_cast<size_t>(pos0 + r) * a.N + n] =
-            silu(red[r * kGemvCols + t]) * red[r * kGemvCols + kGemvCols / 2 + t];
+            silu(tred[r * kGemvCols + t]) * tred[r * kGemvCols + kGemvCols / 2 + t];
   }
 }
 
@@ -430,13 +473,40 @@ GemvShape gemv_shape(size_t items, int N, int mode, int G, size_t max_split_task
   return sh;
 }
 
+int gemv_tiles_per_workgroup(size_t num_tasks, int tiles) {
+  if (W4_GEMV_KT > 0) return W4_GEMV_KT;
+  // A launch that fits one round of four-wave workgroups (four per CU) takes
+  // the largest workgroups that still give every CU one; longer launches keep
+  // four-wave workgroups, which overlap one's tail with the others' streams.
+  if (num_tasks > kGemvResidentTasks || tiles <= 0) return 1;
+  const size_t rows_splits = num_tasks / static_cast<size_t>(tiles);
+  for (int kt = 4; kt > 1; kt /= 2)
+    if (rows_splits * ((tiles + kt - 1) / kt) >= kGemvMinWorkgroups) return kt;
+  return 1;
+}
+
+namespace {
+template <bool kMulti>
+void launch_kt(const GemvArgs& a, int kt, unsigned blocks, hipStream_t stream) {
+  switch (kt) {
+    case 4: gemv_kernel<kMulti, 4><<<blocks, kGemvThreads * 4, 0, stream>>>(a); break;
+    case 2: gemv_kernel<kMulti, 2><<<blocks, kGemvThreads * 2, 0, stream>>>(a); break;
+    default: gemv_kernel<kMulti, 1><<<blocks, kGemvThreads, 0, stream>>>(a); break;
+  }
+}
+}  // namespace
+
 w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stream) {
   if (num_tasks == 0) return W4A16_OK;
-  if (num_tasks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
+  if (a.tiles <= 0 || a.S <= 0 || num_tasks % (static_cast<size_t>(a.tiles) * a.S) != 0)
+    return W4A16_ERR_INVALID_ARG;
+  const int kt = gemv_tiles_per_workgroup(num_tasks, a.tiles);
+  const size_t blocks = num_tasks / a.tiles * ((a.tiles + kt - 1) / kt);
+  if (blocks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   if (a.gps > kWin)
-    gemv_kernel<true><<<static_cast<unsigned>(num_tasks), kGemvThreads, 0, stream>>>(a);
+    launch_kt<true>(a, kt, static_cast<unsigned>(blocks), stream);
   else
-    gemv_kernel<false><<<static_cast<unsigned>(num_tasks), kGemvThreads, 0, stream>>>(a);
+    launch_kt<false>(a, kt, static_cast<unsigned>(blocks), stream);
   return launch_status();
 }
 
