@@ -130,8 +130,9 @@ def run_mlp(args, cfg):
 
     # kernels the library launches for one MLP call: decode sizes run the fused
     # gate/up + SwiGLU GEMV then the down GEMV; larger M runs activation pieces,
-    # gate/up MFMA, pieces of h, down MFMA
-    cap = 5
+    # gate/up MFMA, pieces of h, down MFMA.  The timed entry point brackets each
+    # kernel with a start and a stop event taken from its own dispatch.
+    cap = 8
 
     def step(i, evs=None):
         g, u, d = copies[i % len(copies)]
@@ -145,12 +146,12 @@ def run_mlp(args, cfg):
 
     probe = _events(cap)
     marks = step(0, _handles(probe))
-    names = {3: ["gate_up", "down"], 5: ["prep_x", "gate_up", "prep_h", "down"]}[marks]
+    names = {4: ["gate_up", "down"], 8: ["prep_x", "gate_up", "prep_h", "down"]}[marks]
 
     for i in range(args.warmup):
         step(i)
     ms_step = timed_steps_ms(args, lambda i: step(i))
-    kern, ms_marked = per_kernel_ms(args, names, lambda i, h: step(i, h), cap)
+    kern, ms_marked = per_kernel_ms(args, names, lambda i, h: step(i, h), cap, paired=True)
     step_bytes = mlp_bytes(M, H, I, xbytes)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     # dominant kernel: the fused gate/up + SwiGLU launch
@@ -393,12 +394,14 @@ def timed_steps_ms(args, step):
     return t0.elapsed_time(t1) / args.steps
 
 
-def per_kernel_ms(args, names, step, cap=None):
-    """A second pass of args.steps steps through the *_timed entry point: the
-    library records an event before each of its kernels and one after the
-    last, on the stream the kernels run on.  Returns the mean milliseconds per
-    kernel (each interval also holds that kernel's dispatch gap) and the step
-    time of this pass (the marks themselves cost a few microseconds)."""
+def per_kernel_ms(args, names, step, cap=None, paired=False):
+    """A second pass of args.steps steps through the *_timed entry point.
+    paired: the library brackets kernel j with events 2j and 2j + 1, taken
+    from the kernel's own dispatch (its execution time).  Otherwise it records
+    an event before each of its kernels and one after the last, on the stream
+    the kernels run on, and each interval also holds that kernel's dispatch
+    gap.  Returns the mean milliseconds per kernel and the step time of this
+    pass (the events themselves cost a few microseconds)."""
     import torch
     evs = [_events(cap or len(names) + 1) for _ in range(args.steps)]
     handles = [_handles(e) for e in evs]
@@ -409,7 +412,10 @@ def per_kernel_ms(args, names, step, cap=None):
         step(i, handles[i])
     t1.record()
     torch.cuda.synchronize()
-    kern = {n: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    if paired:
+        kern = {n: statistics.mean(e[2 * j].elapsed_time(e[2 * j + 1]) for e in evs) for j, n in enumerate(names)}
+    else:
+        kern = {n: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
     return kern, t0.elapsed_time(t1) / args.steps
 
 

@@ -183,10 +183,12 @@ W4A16_API w4a16_status_t w4a16_swiglu_mlp(const void* x, w4a16_dtype_t xt, int32
 
 /*
  * Measurement variant of w4a16_swiglu_mlp: identical work and results, and in
- * addition records the caller's events on `stream` around the kernels it
- * launches: events[i] just before kernel i and one more after the last, at
- * most `capacity` events; *recorded (if not NULL) receives how many were
- * recorded.  For M <= 8 the dense MLP launches two kernels (fused gate/up
+ * addition brackets each kernel it launches with two of the caller's events:
+ * events[2i] at the start and events[2i+1] at the end of kernel i, taken by
+ * the runtime from the kernel's own dispatch (hipExtLaunchKernel), so their
+ * interval is the kernel's execution time without the launch gap.  At most
+ * `capacity` events (kernels beyond capacity / 2 run unbracketed); *recorded
+ * (if not NULL) receives how many were used.  For M <= 8 the dense MLP launches two kernels (fused gate/up
  * GEMV with the SwiGLU epilogue, down GEMV); for larger M four (activation
  * pieces, fused gate/up MFMA tiles, pieces of the intermediate, down MFMA).  Events are created and
  * owned by the caller.  Errors as w4a16_swiglu_mlp, plus INVALID_ARG for

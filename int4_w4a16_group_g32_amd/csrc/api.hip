@@ -314,25 +314,24 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
     float* h = reinterpret_cast<float*>(wsb + p.h_off);
     _Float16* aph = reinterpret_cast<_Float16*>(wsb + p.aph_off);
     float* rsh = reinterpret_cast<float*>(wsb + p.rsh_off);
-    if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma_prep(x, xt, M, p.gu.Mp, H, p.gu.P, nullptr, 0, nullptr, apx, rsx, stream);
+    EventMarks::Bracket b = ev.bracket();
+    st = launch_mfma_prep(x, xt, M, p.gu.Mp, H, p.gu.P, nullptr, 0, nullptr, apx, rsx, stream, b.start, b.stop);
     if (st != W4A16_OK) return st;
     MfmaArgs a = mfma_dense_args(p.gu, M, gate, up, 1, apx, rsx, wsb, p.partials_off, p.counters_off);
     a.h = h;
     a.h_bf16 = 0;
-    if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma(a, p.gu.P, p.gu.tasks * p.gu.S, stream);
+    b = ev.bracket();
+    st = launch_mfma(a, p.gu.P, p.gu.tasks * p.gu.S, stream, b.start, b.stop);
     if (st != W4A16_OK) return st;
-    if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma_prep(h, W4A16_F32, M, p.dn.Mp, I, p.dn.P, nullptr, 0, nullptr, aph, rsh, stream);
+    b = ev.bracket();
+    st = launch_mfma_prep(h, W4A16_F32, M, p.dn.Mp, I, p.dn.P, nullptr, 0, nullptr, aph, rsh, stream, b.start,
+                          b.stop);
     if (st != W4A16_OK) return st;
     MfmaArgs d = mfma_dense_args(p.dn, M, down, nullptr, 0, aph, rsh, wsb, p.partials_off,
                                  p.counters_off);
     d.out = y;
-    if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma(d, p.dn.P, p.dn.tasks * p.dn.S, stream);
-    if (st != W4A16_OK) return st;
-    return ev.mark(stream);
+    b = ev.bracket();
+    return launch_mfma(d, p.dn.P, p.dn.tasks * p.dn.S, stream, b.start, b.stop);
   }
   if (!counters_fit(p.tasks_gu, p.S_gu) || !counters_fit(p.tasks_d, p.S_d))
     return W4A16_ERR_UNSUPPORTED;
@@ -340,16 +339,14 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
   GemvArgs a = gemv_dense_args(M, gate, up, 1, x, xt == W4A16_BF16, p.tiles_gu, p.S_gu, p.gps_gu,
                                wsb, p.partials_off, p.counters_off);
   a.h = h;
-  if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(a, p.tasks_gu * p.S_gu, stream);
+  EventMarks::Bracket b = ev.bracket();
+  st = launch_gemv(a, p.tasks_gu * p.S_gu, stream, b.start, b.stop);
   if (st != W4A16_OK) return st;
   GemvArgs d = gemv_dense_args(M, down, nullptr, 0, h, false, p.tiles_d, p.S_d, p.gps_d, wsb,
                                p.partials_off, p.counters_off);
   d.out = y;
-  if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(d, p.tasks_d * p.S_d, stream);
-  if (st != W4A16_OK) return st;
-  return ev.mark(stream);
+  b = ev.bracket();
+  return launch_gemv(d, p.tasks_d * p.S_d, stream, b.start, b.stop);
 }
 }  // namespace w4
 

@@ -57,6 +57,19 @@ struct EventMarks {
     if (events == nullptr || recorded >= capacity) return W4A16_OK;
     return hipEventRecord(events[recorded++], stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
   }
+  // The start and stop events of the next kernel (both null once the caller's
+  // array is used up, or without events).
+  struct Bracket {
+    hipEvent_t start = nullptr, stop = nullptr;
+  };
+  Bracket bracket() {
+    Bracket b;
+    if (events != nullptr && recorded + 2 <= capacity) {
+      b.start = events[recorded++];
+      b.stop = events[recorded++];
+    }
+    return b;
+  }
 };
 
 size_t gemv_partial_bytes(size_t tasks, int S);

@@ -73,6 +73,8 @@ constexpr size_t kGemvMinWorkgroups = 240;   // about one workgroup per CU
 // num_tasks = items * tiles * S tasks.
 int gemv_tiles_per_workgroup(size_t num_tasks, int tiles);
 // num_tasks must be items * a.tiles * a.S.
-w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stream);
+// start / stop (optional) are recorded at the kernel's own start and end.
+w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stream,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace w4

@@ -25,6 +25,8 @@
 // [2^14, 2^15), so f16 neither overflows nor loses the large values); each
 // window's accumulators are scaled back by 2^-e before they join the total.
 #include "gemv.h"
+
+#include <hip/hip_ext.h>
 #include "mfma_ops.h"
 
 namespace w4 {
@@ -487,16 +489,27 @@ int gemv_tiles_per_workgroup(size_t num_tasks, int tiles) {
 
 namespace {
 template <bool kMulti>
-void launch_kt(const GemvArgs& a, int kt, unsigned blocks, hipStream_t stream) {
+void launch_kt(const GemvArgs& a, int kt, unsigned blocks, hipStream_t stream, hipEvent_t start,
+               hipEvent_t stop) {
   switch (kt) {
-    case 4: gemv_kernel<kMulti, 4><<<blocks, kGemvThreads * 4, 0, stream>>>(a); break;
-    case 2: gemv_kernel<kMulti, 2><<<blocks, kGemvThreads * 2, 0, stream>>>(a); break;
-    default: gemv_kernel<kMulti, 1><<<blocks, kGemvThreads, 0, stream>>>(a); break;
+    case 4:
+      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 4>, dim3(blocks), dim3(kGemvThreads * 4), 0, stream, start,
+                            stop, 0, a);
+      break;
+    case 2:
+      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 2>, dim3(blocks), dim3(kGemvThreads * 2), 0, stream, start,
+                            stop, 0, a);
+      break;
+    default:
+      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 1>, dim3(blocks), dim3(kGemvThreads), 0, stream, start, stop,
+                            0, a);
+      break;
   }
 }
 }  // namespace
 
-w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stream) {
+w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stream, hipEvent_t start,
+                           hipEvent_t stop) {
   if (num_tasks == 0) return W4A16_OK;
   if (a.tiles <= 0 || a.S <= 0 || num_tasks % (static_cast<size_t>(a.tiles) * a.S) != 0)
     return W4A16_ERR_INVALID_ARG;
@@ -504,9 +517,9 @@ w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stre
   const size_t blocks = num_tasks / a.tiles * ((a.tiles + kt - 1) / kt);
   if (blocks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   if (a.gps > kWin)
-    launch_kt<true>(a, kt, static_cast<unsigned>(blocks), stream);
+    launch_kt<true>(a, kt, static_cast<unsigned>(blocks), stream, start, stop);
   else
-    launch_kt<false>(a, kt, static_cast<unsigned>(blocks), stream);
+    launch_kt<false>(a, kt, static_cast<unsigned>(blocks), stream, start, stop);
   return launch_status();
 }
 

@@ -76,8 +76,11 @@ struct MfmaArgs {
 // need[p] != 0 are written (the others are never read).
 w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, int K, int P,
                                 const int* gather, int top_k, const int* need, _Float16* ap,
-                                float* rs, hipStream_t stream);
-w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream_t stream);
+                                float* rs, hipStream_t stream, hipEvent_t start = nullptr,
+                                hipEvent_t stop = nullptr);
+// start / stop (optional) are recorded at the kernel's own start and end.
+w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream_t stream,
+                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Wide-tile launch (mode 0, dense rows, Mp a multiple of kWideRows); a.tiles
 // counts 128-column tiles.
 w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stream);

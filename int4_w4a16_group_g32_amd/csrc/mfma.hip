@@ -15,6 +15,8 @@
 #include <type_traits>
 
 #include "mfma.h"
+
+#include <hip/hip_ext.h>
 #include "mfma_ops.h"
 
 namespace w4 {
@@ -471,40 +473,47 @@ void mfma_kernel(const MfmaArgs a) {
 
 w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, int K, int P,
                                 const int* gather, int top_k, const int* need, _Float16* ap,
-                                float* rs, hipStream_t stream) {
+                                float* rs, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (Mp == 0) return W4A16_OK;
+  const float* xf = static_cast<const float*>(x);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const dim3 g(Mp), b(kPrepThreads);
   if (xt == W4A16_F32 && P == 2)
-    mfma_prep_kernel<float, 2><<<Mp, kPrepThreads, 0, stream>>>(static_cast<const float*>(x), R, Mp, K, gather,
-                                                       top_k, need, ap, rs);
+    hipExtLaunchKernelGGL(mfma_prep_kernel<float, 2>, g, b, 0, stream, start, stop, 0, xf, R, Mp, K, gather,
+                          top_k, need, ap, rs);
   else if (xt == W4A16_F32)
-    mfma_prep_kernel<float, 1><<<Mp, kPrepThreads, 0, stream>>>(static_cast<const float*>(x), R, Mp, K, gather,
-                                                       top_k, need, ap, rs);
+    hipExtLaunchKernelGGL(mfma_prep_kernel<float, 1>, g, b, 0, stream, start, stop, 0, xf, R, Mp, K, gather,
+                          top_k, need, ap, rs);
   else if (P == 2)
-    mfma_prep_kernel<uint16_t, 2><<<Mp, kPrepThreads, 0, stream>>>(static_cast<const uint16_t*>(x), R, Mp, K,
-                                                          gather, top_k, need, ap, rs);
+    hipExtLaunchKernelGGL(mfma_prep_kernel<uint16_t, 2>, g, b, 0, stream, start, stop, 0, xb, R, Mp, K, gather,
+                          top_k, need, ap, rs);
   else
-    mfma_prep_kernel<uint16_t, 1><<<Mp, kPrepThreads, 0, stream>>>(static_cast<const uint16_t*>(x), R, Mp, K,
-                                                          gather, top_k, need, ap, rs);
+    hipExtLaunchKernelGGL(mfma_prep_kernel<uint16_t, 1>, g, b, 0, stream, start, stop, 0, xb, R, Mp, K, gather,
+                          top_k, need, ap, rs);
   return launch_status();
 }
 
 namespace {
-void launch_one_piece(const MfmaArgs& a, unsigned grid, hipStream_t stream) {
+void launch_one_piece(const MfmaArgs& a, unsigned grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (a.dense_rows > 0)
-    mfma_kernel<1, kTileRing, 2><<<grid, kMfmaThreads, 0, stream>>>(a);
+    hipExtLaunchKernelGGL(mfma_kernel<1, kTileRing, 2>, dim3(grid), dim3(kMfmaThreads), 0, stream, start, stop,
+                          0, a);
   else
-    mfma_kernel<1, kGroupedRing, 3><<<grid, kMfmaThreads, 0, stream>>>(a);
+    hipExtLaunchKernelGGL(mfma_kernel<1, kGroupedRing, 3>, dim3(grid), dim3(kMfmaThreads), 0, stream, start,
+                          stop, 0, a);
 }
 }  // namespace
 
-w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream_t stream) {
+w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream_t stream, hipEvent_t start,
+                           hipEvent_t stop) {
   if (num_tasks == 0) return W4A16_OK;
   if (num_tasks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   const unsigned grid = static_cast<unsigned>(num_tasks);
   if (P == 2)
-    mfma_kernel<2, kTileRing, 2><<<grid, kMfmaThreads, 0, stream>>>(a);
+    hipExtLaunchKernelGGL(mfma_kernel<2, kTileRing, 2>, dim3(grid), dim3(kMfmaThreads), 0, stream, start, stop,
+                          0, a);
   else
-    launch_one_piece(a, grid, stream);
+    launch_one_piece(a, grid, stream, start, stop);
   return launch_status();
 }
 

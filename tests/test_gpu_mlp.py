@@ -80,3 +80,39 @@ def test_mlp_full_size(dense_mlp, name, dtype):
     # the library's quantization of the same weights agrees with the oracle's
     qd = canonical_words(d.qw.cpu().numpy(), I, H)[0][:, cols]
     assert np.array_equal(qd, _sampled_down(w_down, cols)[0])
+
+
+@pytest.mark.parametrize("M,dtype,kernels", [(4, "f32", 2), (64, "bf16", 4)])
+def test_mlp_timed_brackets_each_kernel(M, dtype, kernels):
+    """w4a16_swiglu_mlp_timed does the same work as w4a16_swiglu_mlp (same
+    output bits) and brackets each of its kernels with a start and a stop event."""
+    import ctypes
+
+    H, I, cfg = 256, 512, 470
+    codes = [O.quantize_w4a16(w.numpy()) for w in (W.weights(H, I, cfg, W.TAG_GATE), W.weights(H, I, cfg, W.TAG_UP),
+                                                   W.weights(I, H, cfg, W.TAG_DOWN))]
+    g, u, d = (weight_from_codes(*c) for c in codes)
+    x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
+    y_plain = _mlp_gpu(x, g, u, d)
+    xt = L.F32 if dtype == "f32" else L.BF16
+    ws = L.new_workspace(L.swiglu_mlp_workspace_bytes(M, xt, g, u, d))
+    y = torch.full((M, H), float("nan"), dtype=torch.float32, device="cuda")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for e in evs:  # torch creates the HIP event on its first record
+        e.record()
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * 8)(*[e.cuda_event for e in evs])
+    rec = ctypes.c_int32(-1)
+    lib = L.load_library()
+    st = lib.w4a16_swiglu_mlp_timed(L._ptr(x), xt, M, ctypes.byref(g.desc()), ctypes.byref(u.desc()),
+                                    ctypes.byref(d.desc()), L._ptr(y), L._ptr(ws), ws.numel(),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), handles, 8,
+                                    ctypes.byref(rec))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert rec.value == 2 * kernels
+    assert torch.equal(y, y_plain)
+    for j in range(kernels):
+        assert evs[2 * j].elapsed_time(evs[2 * j + 1]) > 0.0
+        if j > 0:  # kernels run in launch order on the stream
+            assert evs[2 * j - 1].elapsed_time(evs[2 * j]) >= 0.0
