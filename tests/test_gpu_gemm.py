@@ -199,3 +199,27 @@ def test_gemm_hot_expert_full_size():
     err = rel_err(y[torch.as_tensor(rows, device="cuda")], ref)
     print(f"gemm_m2048_hot_expert relF={err:.3e} (64 sampled rows)", flush=True)
     assert err <= tol_for("bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_gemv_four_tile_workgroups_ragged(M, dtype):
+    """K = 16384, N = 16128: 63 column tiles of 256 and 16 K splits, 1008 tasks,
+    which the GEMV runs as 256 workgroups of four column tiles; the last
+    workgroup has one quad past the matrix.  Sampled columns (the last tiles
+    among them) against the oracle, which quantizes the same float32 weights."""
+    K, N, cfg = 16384, 16128, 520
+    wd = W.weights(K, N, cfg, W.TAG_GATE, device="cuda")
+    w = L.quantize_to_weight(wd)
+    x = x_for_dtype(W.activations(M, K, cfg + M).cuda(), dtype)
+    y, _ = _run_gemm(x, w, N)
+    rng = np.random.default_rng(cfg + M)
+    cols = np.sort(np.concatenate([rng.choice(60 * 256, size=192, replace=False),
+                                   np.arange(60 * 256, N, 7)]))
+    qw, sc = O.quantize_w4a16(np.ascontiguousarray(wd.cpu().numpy()[:, cols]))
+    del wd
+    ref = O.gemm64(x_values(x), qw, sc)
+    err = rel_err(y[:, torch.as_tensor(cols, device="cuda")], ref)
+    print(f"gemv 4-tile workgroups M={M} K={K} N={N} {dtype} relF={err:.3e}", flush=True)
+    assert err <= tol_for(dtype)
+    assert not torch.isnan(y).any()

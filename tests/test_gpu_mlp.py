@@ -116,3 +116,27 @@ def test_mlp_timed_brackets_each_kernel(M, dtype, kernels):
         assert evs[2 * j].elapsed_time(evs[2 * j + 1]) > 0.0
         if j > 0:  # kernels run in launch order on the stream
             assert evs[2 * j - 1].elapsed_time(evs[2 * j]) >= 0.0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mlp_gemv_four_tile_workgroups_ragged(dtype):
+    """Hidden 32768, intermediate 1920 at M = 4: the fused gate/up GEMV has 15
+    SwiGLU tiles of 128 outputs and 32 K splits (480 tasks), run as 256
+    workgroups of two tiles, the last with one quad past the matrix.  Sampled
+    output columns against the oracle."""
+    H, I, M, cfg = 32768, 1920, 4, 530
+    gate = W.weights(H, I, cfg, W.TAG_GATE)
+    up = W.weights(H, I, cfg, W.TAG_UP)
+    down = W.weights(I, H, cfg, W.TAG_DOWN)
+    gq, uq = O.quantize_w4a16(gate.numpy()), O.quantize_w4a16(up.numpy())
+    g, u = weight_from_codes(*gq), weight_from_codes(*uq)
+    d = L.quantize_to_weight(down.cuda())
+    x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
+    y = _mlp_gpu(x, g, u, d)
+    cols = np.sort(np.random.default_rng(cfg).choice(H, size=512, replace=False))
+    xv = x_values(x)
+    h = O.silu64(O.gemm64(xv, *gq)) * O.gemm64(xv, *uq)
+    ref = h @ O.dequant64(*_sampled_down(down.numpy(), cols))
+    err = rel_err(y[:, torch.as_tensor(cols, device="cuda")], ref)
+    print(f"mlp H={H} I={I} M={M} {dtype} relF={err:.3e} (512 sampled columns)", flush=True)
+    assert err <= tol_for(dtype)
