@@ -114,7 +114,7 @@ MfmaArgs mfma_dense_args(const MfmaPlan& m, int rows, const w4a16_weight_t* w0,
 
 GemmPlan plan_gemm(int M, const w4a16_weight_t* w, w4a16_dtype_t xt) {
   GemmPlan p;
-  if (M > kMaxGemvRows) {
+  if (M > gemv_rows(xt)) {
     p.mfma = true;
     p.mf = plan_mfma(M, w->N, 0, w->K, xt, true);
     Carve c;
@@ -127,7 +127,7 @@ GemmPlan plan_gemm(int M, const w4a16_weight_t* w, w4a16_dtype_t xt) {
     return p;
   }
   const int G = w->K / kGroup;
-  const size_t items = (static_cast<size_t>(M) + kMaxGemvRows - 1) / kMaxGemvRows;
+  const size_t items = (static_cast<size_t>(M) + gemv_rows(xt) - 1) / gemv_rows(xt);
   const GemvShape sh = gemv_shape(items, w->N, 0, G, kCounterBytes / sizeof(int));
   p.tiles = sh.tiles;
   p.tasks = items * p.tiles;
@@ -142,7 +142,7 @@ GemmPlan plan_gemm(int M, const w4a16_weight_t* w, w4a16_dtype_t xt) {
 
 MlpPlan plan_mlp(int M, w4a16_dtype_t xt, const w4a16_weight_t* gate, const w4a16_weight_t* down) {
   MlpPlan p;
-  if (M > kMaxGemvRows) {
+  if (M > gemv_rows(xt)) {
     const int H = gate->K, I = gate->N;
     p.mfma = true;
     p.gu = plan_mfma(M, I, 1, H, xt, false);
@@ -161,7 +161,7 @@ MlpPlan plan_mlp(int M, w4a16_dtype_t xt, const w4a16_weight_t* gate, const w4a1
   }
   const int H = gate->K, I = gate->N;
   const int GH = H / kGroup, GI = I / kGroup;
-  const size_t items = (static_cast<size_t>(M) + kMaxGemvRows - 1) / kMaxGemvRows;
+  const size_t items = (static_cast<size_t>(M) + gemv_rows(xt) - 1) / gemv_rows(xt);
   const GemvShape gu = gemv_shape(items, I, 1, GH, kCounterBytes / sizeof(int));
   p.tiles_gu = gu.tiles;
   p.tasks_gu = items * p.tiles_gu;
@@ -199,11 +199,12 @@ bool ranges_overlap(const void* a, size_t abytes, const void* b, size_t bbytes) 
 size_t dtype_bytes(w4a16_dtype_t xt) { return xt == W4A16_F32 ? 4 : 2; }
 
 GemvArgs gemv_dense_args(int M, const w4a16_weight_t* w0, const w4a16_weight_t* w1, int mode,
-                         const void* x, bool x_bf16, int tiles, int S, int gps, char* ws,
+                         const void* x, bool x_bf16, int pieces, int tiles, int S, int gps, char* ws,
                          size_t partials_off, size_t counters_off) {
   GemvArgs a{};
   a.x = x;
   a.x_bf16 = x_bf16 ? 1 : 0;
+  a.pieces = pieces;
   a.G = w0->K / kGroup;
   a.K = w0->K;
   a.qw0 = reinterpret_cast<const u32x4*>(w0->qw);
@@ -261,7 +262,7 @@ extern "C" w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M,
     return launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream);
   }
   if (!counters_fit(p.tasks, p.S)) return W4A16_ERR_UNSUPPORTED;
-  GemvArgs a = gemv_dense_args(M, w, nullptr, 0, x, xt == W4A16_BF16, p.tiles, p.S, p.gps, wsb,
+  GemvArgs a = gemv_dense_args(M, w, nullptr, 0, x, xt == W4A16_BF16, gemv_pieces(xt), p.tiles, p.S, p.gps, wsb,
                                p.partials_off, p.counters_off);
   a.out = y;
   return launch_gemv(a, p.tasks * p.S, stream);
@@ -336,13 +337,13 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
   if (!counters_fit(p.tasks_gu, p.S_gu) || !counters_fit(p.tasks_d, p.S_d))
     return W4A16_ERR_UNSUPPORTED;
   float* h = reinterpret_cast<float*>(wsb + p.h_off);
-  GemvArgs a = gemv_dense_args(M, gate, up, 1, x, xt == W4A16_BF16, p.tiles_gu, p.S_gu, p.gps_gu,
+  GemvArgs a = gemv_dense_args(M, gate, up, 1, x, xt == W4A16_BF16, gemv_pieces(xt), p.tiles_gu, p.S_gu, p.gps_gu,
                                wsb, p.partials_off, p.counters_off);
   a.h = h;
   EventMarks::Bracket b = ev.bracket();
   st = launch_gemv(a, p.tasks_gu * p.S_gu, stream, b.start, b.stop);
   if (st != W4A16_OK) return st;
-  GemvArgs d = gemv_dense_args(M, down, nullptr, 0, h, false, p.tiles_d, p.S_d, p.gps_d, wsb,
+  GemvArgs d = gemv_dense_args(M, down, nullptr, 0, h, false, gemv_pieces(xt), p.tiles_d, p.S_d, p.gps_d, wsb,
                                p.partials_off, p.counters_off);
   d.out = y;
   b = ev.bracket();

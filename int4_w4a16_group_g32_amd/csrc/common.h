@@ -13,7 +13,8 @@ namespace w4 {
 constexpr int kGroup = 32;       // rows of K in one code block (one MFMA k step); scale groups are
                                  // kGroup << gshift rows, gshift = 0, 1, 2 (group size 32, 64, 128)
 constexpr int kWave = 64;        // CDNA wavefront width
-constexpr int kMaxGemvRows = 8;  // largest row count the GEMV kernels take per task
+constexpr int kMaxGemvRows = 8;  // rows per GEMV task with two f16 pieces (float32 activations)
+constexpr int kGemvRowsOnePiece = 16;  // rows per GEMV task with one piece (bf16 activations)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

@@ -81,8 +81,10 @@ w4a16_status_t check_mlp(const w4a16_weight_t* gate, const w4a16_weight_t* up,
                          const w4a16_weight_t* down);
 bool ranges_overlap(const void* a, size_t abytes, const void* b, size_t bbytes);
 size_t dtype_bytes(w4a16_dtype_t xt);
+// pieces: gemv_pieces of the layer's activation type (the float32
+// intermediate of a bf16 layer takes one piece, as its rows do)
 GemvArgs gemv_dense_args(int M, const w4a16_weight_t* w0, const w4a16_weight_t* w1, int mode,
-                         const void* x, bool x_bf16, int tiles, int S, int gps, char* ws,
+                         const void* x, bool x_bf16, int pieces, int tiles, int S, int gps, char* ws,
                          size_t partials_off, size_t counters_off);
 
 }  // namespace w4

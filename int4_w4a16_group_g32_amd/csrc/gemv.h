@@ -5,12 +5,13 @@
 
 namespace w4 {
 
-// One task covers up to kMaxGemvRows positions (rows) of one item, one column
+// One task covers up to gemv_rows(pieces) positions (rows) of one item, one column
 // tile and one K split.  Activations are read raw (float32 or bf16) and turned
 // into f16 pieces inside the kernel, one staging window of groups at a time.
 struct GemvArgs {
   const void* x;        // activations [rows][K], float32 or bf16
   int x_bf16;
+  int pieces;           // f16 pieces per activation: 2 (tasks of 8 rows) or 1 (tasks of 16 rows)
   const int* gather;    // position p reads row gather[p] / top_k (negative: a zero row);
   int top_k;            //   nullptr: position p reads row p
   int K, G;             // G = K / 32
@@ -31,7 +32,7 @@ struct GemvArgs {
   int tiles;             // column tiles per row item
   int S;                 // K splits across workgroups
   int gps;               // groups per split
-  int dense_rows;        // > 0: dense rows 0..dense_rows-1, items of kMaxGemvRows rows
+  int dense_rows;        // > 0: dense rows 0..dense_rows-1, items of gemv_rows(pieces) rows
   const int4* items;     // grouped mode: {expert, first position, rows, 0}
   const int* n_items;    // grouped mode: number of valid items (device)
   int mode;              // 0: plain, out[position][N]; 1: SwiGLU, h[position][N]
@@ -60,8 +61,13 @@ struct GemvShape {
 };
 GemvShape gemv_shape(size_t items, int N, int mode, int G, size_t max_split_tasks);
 
-// floats of one split-K partial tile
-constexpr size_t kPartialTileFloats = static_cast<size_t>(kMaxGemvRows) * kGemvCols;
+// floats of one split-K partial tile (room for 16 rows)
+constexpr size_t kPartialTileFloats = static_cast<size_t>(kGemvRowsOnePiece) * kGemvCols;
+
+// Pieces per activation and rows per task of the GEMV for an activation type:
+// bf16 fits one f16 piece exactly (16 rows per task), float32 takes two (8).
+inline int gemv_pieces(w4a16_dtype_t xt) { return xt == W4A16_BF16 ? 1 : 2; }
+inline int gemv_rows(w4a16_dtype_t xt) { return xt == W4A16_BF16 ? kGemvRowsOnePiece : kMaxGemvRows; }
 
 #ifndef W4_GEMV_KT
 #define W4_GEMV_KT 0  // column tiles per workgroup; 0: chosen per launch
@@ -69,9 +75,9 @@ constexpr size_t kPartialTileFloats = static_cast<size_t>(kMaxGemvRows) * kGemvC
 constexpr size_t kGemvResidentTasks = 1024;  // four-wave workgroups resident at once (4 per CU)
 constexpr size_t kGemvMinWorkgroups = 240;   // about one workgroup per CU
 
-// Column tiles per workgroup (1, 2 or 4 quads of four waves) for a launch of
-// num_tasks = items * tiles * S tasks.
-int gemv_tiles_per_workgroup(size_t num_tasks, int tiles);
+// Column tiles per workgroup (1, 2 or 4 quads of four waves; at most 2 with
+// one piece) for a launch of num_tasks = items * tiles * S tasks.
+int gemv_tiles_per_workgroup(size_t num_tasks, int tiles, int pieces);
 // num_tasks must be items * a.tiles * a.S.
 // start / stop (optional) are recorded at the kernel's own start and end.
 w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stream,

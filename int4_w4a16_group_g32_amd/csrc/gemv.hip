@@ -45,13 +45,14 @@ constexpr int kUnitsPerGroup = 16 * 4;   // 16-byte units of one group's A (16 r
 
 struct GemvLds {
   // A operand of the window, unit (g, r, kb) at a_unit(g, r, kb); reused after
-  // the main loop as the tile buffer [kMaxGemvRows][kGemvCols] of floats
+  // the main loop as the tile buffers [kT][rows][kGemvCols] of floats
   uint4 buf[kWin * kUnitsPerGroup];
-  float f[kMaxGemvRows];  // 2^-e per row for the current window
+  float f[kGemvRowsOnePiece];  // 2^-e per row for the current window
 };
 static_assert(kWin % kRing == 0, "ring slots must stay aligned across windows");
+// four quads of 8 rows, or two of 16
 static_assert(sizeof(uint4) * kWin * kUnitsPerGroup >= sizeof(float) * 4 * kMaxGemvRows * kGemvCols,
-              "the tile buffers of four quads must fit in the staging buffer");
+              "the tile buffers of a workgroup must fit in the staging buffer");
 
 // k blocks are XOR-swizzled by row so the 16 rows of one k block fall in
 // distinct LDS banks.
@@ -59,28 +60,33 @@ __device__ __forceinline__ int a_unit(int g, int r, int kb) {
   return (g * 16 + r) * 4 + (kb ^ ((r >> 2) & 3));
 }
 
-// Staging of groups [gw, gw + nw) of rows pos0 .. pos0 + nrows - 1 by a
-// workgroup of kW waves.  Wave wv takes rows wv + j * kRowStride (waves past
-// the eighth stage nothing); lane l takes 16 consecutive activations of a
+// Staging of groups [gw, gw + nw) of rows pos0 .. pos0 + nrows - 1 (up to
+// kRows) by a workgroup of kW waves.  Wave wv takes rows wv + j * kRowStride
+// (waves past kRowStride stage nothing), at most kHold rows at a time in
+// registers, in kPasses passes; lane l takes 16 consecutive activations of a
 // row: group l >> 1, k blocks 2(l & 1) and 2(l & 1) + 1.  The raw loads are
-// split from the conversion so they can be issued ahead of the weight
-// prefetch (vector loads complete in order).
-template <int kW>
+// split from the conversion so the first pass can be issued ahead of the
+// weight prefetch (vector loads complete in order).
+template <int kW, int kRows>
 struct Staging {
-  static constexpr int kRowStride = kW < kMaxGemvRows ? kW : kMaxGemvRows;
-  static constexpr int kRowsPerWave = kMaxGemvRows / kRowStride;
+  static constexpr int kRowStride = kW < kRows ? kW : kRows;
+  static constexpr int kRowsPerWave = kRows / kRowStride;
+  static constexpr int kHold = kRowsPerWave < 2 ? kRowsPerWave : 2;
+  static constexpr int kPasses = kRowsPerWave / kHold;
 };
 
-template <int kW>
+template <int kW, int kRows>
 __device__ __forceinline__ void load_window(const GemvArgs& a, int gw, int nw, int pos0, int nrows,
-                                            int wv, int lane, float v[Staging<kW>::kRowsPerWave][16]) {
+                                            int wv, int lane, int pass,
+                                            float v[Staging<kW, kRows>::kHold][16]) {
+  using St = Staging<kW, kRows>;
   const int gl = lane >> 1, hb = lane & 1;
 #pragma unroll
-  for (int j = 0; j < Staging<kW>::kRowsPerWave; ++j) {
-    const int m = wv + j * Staging<kW>::kRowStride;
+  for (int j = 0; j < St::kHold; ++j) {
+    const int m = wv + (pass * St::kHold + j) * St::kRowStride;
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[j][i] = 0.0f;
-    if (m >= nrows || wv >= kMaxGemvRows) continue;
+    if (m >= nrows || wv >= St::kRowStride) continue;
     long src = pos0 + m;
     if (a.gather != nullptr) {
       const int pr = a.gather[pos0 + m];
@@ -115,16 +121,19 @@ __device__ __forceinline__ void load_window(const GemvArgs& a, int gw, int nw, i
 }
 
 // Per row: the window's largest magnitude sets e (max * 2^e in [2^14, 2^15)),
-// the pieces of x * 2^e go to LDS in the A layout and 2^-e to lds.f.  Absent
-// rows get the factor 0 and are never read as A.
-template <int kW>
-__device__ __forceinline__ void convert_window(GemvLds& lds, int nw, int nrows, int wv, int lane,
-                                               const float v[Staging<kW>::kRowsPerWave][16]) {
+// the pieces of x * 2^e go to LDS in the A layout and 2^-e to lds.f.  Two
+// pieces (8 rows): piece 0 is A row m, piece 1 A row 8 + m.  One piece (16
+// rows, for bf16 activations it is exact): A row m.  Absent rows get the
+// factor 0 and are never read as A.
+template <int kW, int kRows, int kP>
+__device__ __forceinline__ void convert_window(GemvLds& lds, int nw, int nrows, int wv, int lane, int pass,
+                                               const float v[Staging<kW, kRows>::kHold][16]) {
+  using St = Staging<kW, kRows>;
   const int gl = lane >> 1, hb = lane & 1;
-  if (wv >= kMaxGemvRows) return;  // (wave-uniform) rows are staged by the first eight waves
+  if (wv >= St::kRowStride) return;  // (wave-uniform) rows are staged by the first waves
 #pragma unroll
-  for (int j = 0; j < Staging<kW>::kRowsPerWave; ++j) {
-    const int m = wv + j * Staging<kW>::kRowStride;
+  for (int j = 0; j < St::kHold; ++j) {
+    const int m = wv + (pass * St::kHold + j) * St::kRowStride;
     if (m >= nrows) {
       if (lane == 0) lds.f[m] = 0.0f;
       continue;
@@ -151,11 +160,11 @@ __device__ __forceinline__ void convert_window(GemvLds& lds, int nw, int nrows, 
           const float t = v[j][8 * b + kCodeOrder[i]] * scale;
           const _Float16 h0 = static_cast<_Float16>(t);
           p0[i] = h0;
-          p1[i] = static_cast<_Float16>(t - static_cast<float>(h0));
+          if (kP == 2) p1[i] = static_cast<_Float16>(t - static_cast<float>(h0));
         }
         const int kb = 2 * hb + b;
         *reinterpret_cast<half8*>(&lds.buf[a_unit(gl, m, kb)]) = p0;
-        *reinterpret_cast<half8*>(&lds.buf[a_unit(gl, 8 + m, kb)]) = p1;
+        if (kP == 2) *reinterpret_cast<half8*>(&lds.buf[a_unit(gl, 8 + m, kb)]) = p1;
       }
     }
   }
@@ -197,12 +206,11 @@ __device__ __forceinline__ void mma_group(const GemvLds& lds, int gl, int lc, in
 // Sums of the S split partials of rows 0..nrows-1, column t, in split order:
 // blocks of 4 rows x kB splits are loaded together (indices clamped into
 // range, so no load is predicated) and then added.
-template <int kB>
-__device__ __forceinline__ void read_partials(const float* base, int S, int nrows, int t,
-                                              float v[kMaxGemvRows]) {
+template <int kB, int kRows>
+__device__ __forceinline__ void read_partials(const float* base, int S, int nrows, int t, float v[kRows]) {
   constexpr size_t tf = kPartialTileFloats;
 #pragma unroll
-  for (int r0 = 0; r0 < kMaxGemvRows; r0 += 4) {
+  for (int r0 = 0; r0 < kRows; r0 += 4) {
     if (r0 >= nrows) break;
     float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < S; s0 += kB) {
@@ -236,10 +244,17 @@ __device__ __forceinline__ void read_partials(const float* base, int S, int nrow
 // would wait for its activations behind the weight streams of the ones
 // already running there).  A quad whose tile lies past the last one streams
 // column block 0 and stores nothing.
-template <bool kMulti, int kT>
+//
+// kP = 2: two f16 pieces of 8 rows per task (float32 activations); kP = 1:
+// one piece of 16 rows (bf16 activations, which one f16 piece holds exactly,
+// or the float32 intermediate of a bf16 layer).
+template <bool kMulti, int kT, int kP>
 __global__ __launch_bounds__(kGemvThreads * kT) __attribute__((amdgpu_waves_per_eu(4)))
 void gemv_kernel(const GemvArgs a) {
   constexpr int kW = 4 * kT;  // waves
+  constexpr int kRows = kP == 2 ? kMaxGemvRows : kGemvRowsOnePiece;  // rows per task
+  static_assert(kT * kRows <= 4 * kMaxGemvRows, "tile buffers exceed the staging buffer");
+  using St = Staging<kW, kRows>;
   __shared__ GemvLds lds;
   __shared__ int last[kT];
 
@@ -251,8 +266,8 @@ void gemv_kernel(const GemvArgs a) {
 
   int expert = 0, pos0, nrows;
   if (a.dense_rows > 0) {
-    pos0 = item * kMaxGemvRows;
-    nrows = min(kMaxGemvRows, a.dense_rows - pos0);
+    pos0 = item * kRows;
+    nrows = min(kRows, a.dense_rows - pos0);
   } else {
     if (item >= *a.n_items) return;
     const int4 it = a.items[item];
@@ -291,16 +306,17 @@ void gemv_kernel(const GemvArgs a) {
   const size_t gstride = static_cast<size_t>(a.N);  // chunks (and scales) per group row
   const int g_last = g_hi - 1;
   const uint32_t magic = magic_vgpr();
-  // A rows whose activations are absent read as zero (lc & 7 is the row)
-  const bool arow = (lc & 7) < nrows;
+  // A rows whose activations are absent read as zero (A row lc holds row
+  // lc & 7 with two pieces, row lc with one)
+  const bool arow = (kP == 2 ? (lc & 7) : lc) < nrows;
 
   f32x4 tot[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) tot[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // ring of kRing groups in flight: group g sits in slot (g - g_lo) % kRing
   GroupCodes ring[kRing];
-  float xv[Staging<kW>::kRowsPerWave][16];
-  load_window<kW>(a, g_lo, min(kWin, g_hi - g_lo), pos0, nrows, wv, lane, xv);  // ahead of the weights
+  float xv[St::kHold][16];
+  load_window<kW, kRows>(a, g_lo, min(kWin, g_hi - g_lo), pos0, nrows, wv, lane, 0, xv);  // ahead of the weights
   // A wave past the matrix's last column streams column block 0 and stores
   // nothing: the ring loads stay unconditional, so the compiler's waits can
   // count them.
@@ -311,9 +327,14 @@ void gemv_kernel(const GemvArgs a) {
     const int nw = min(kWin, g_hi - gw);
     if (gw != g_lo) {
       __syncthreads();  // the previous window is consumed
-      load_window<kW>(a, gw, nw, pos0, nrows, wv, lane, xv);
+      load_window<kW, kRows>(a, gw, nw, pos0, nrows, wv, lane, 0, xv);
     }
-    convert_window<kW>(lds, nw, nrows, wv, lane, xv);
+    convert_window<kW, kRows, kP>(lds, nw, nrows, wv, lane, 0, xv);
+#pragma unroll
+    for (int pass = 1; pass < St::kPasses; ++pass) {
+      load_window<kW, kRows>(a, gw, nw, pos0, nrows, wv, lane, pass, xv);
+      convert_window<kW, kRows, kP>(lds, nw, nrows, wv, lane, pass, xv);
+    }
     __syncthreads();
     {
       f32x4 wacc[4];
@@ -341,7 +362,8 @@ void gemv_kernel(const GemvArgs a) {
         if (kT > 1 && kPace > 0 && (gl / kRing) % kPace == kPace - 1) __builtin_amdgcn_s_barrier();
       }
       // accumulator element i of this lane is A row 4kb + i: row (4kb + i) & 7
-      const float4 f4 = *reinterpret_cast<const float4*>(&lds.f[4 * (kb & 1)]);
+      // with two pieces, row 4kb + i with one
+      const float4 f4 = *reinterpret_cast<const float4*>(&lds.f[kP == 2 ? 4 * (kb & 1) : 4 * kb]);
       const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
       if (kMulti) {
 #pragma unroll
@@ -357,22 +379,23 @@ void gemv_kernel(const GemvArgs a) {
     }
   }
 
-  // piece 0 (lanes 0..31) + piece 1 (lanes 32..63) of rows 4kb + i
+  // two pieces: piece 0 (lanes 0..31) + piece 1 (lanes 32..63) of rows
+  // 4kb + i; one piece: every lane holds rows 4kb + i
   float pv[4][4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[cb][i] = tot[cb][i] + __shfl_xor(tot[cb][i], 32);
+    for (int i = 0; i < 4; ++i) pv[cb][i] = kP == 2 ? tot[cb][i] + __shfl_xor(tot[cb][i], 32) : tot[cb][i];
   __syncthreads();  // every wave is done with the staged activations
-  float* red = reinterpret_cast<float*>(lds.buf);  // [kT][kMaxGemvRows][kGemvCols]
-  if (lane < 32) {
+  float* red = reinterpret_cast<float*>(lds.buf);  // [kT][kRows][kGemvCols]
+  if (kP == 1 || lane < 32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 4 * kb + i;
       if (m < nrows) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
-          red[(q * kMaxGemvRows + m) * kGemvCols + wq * 64 + 4 * lc + cb] = pv[cb][i];
+          red[(q * kRows + m) * kGemvCols + wq * 64 + 4 * lc + cb] = pv[cb][i];
       }
     }
   }
@@ -383,10 +406,10 @@ void gemv_kernel(const GemvArgs a) {
   const int t = static_cast<int>(threadIdx.x) % kGemvThreads;
   const int ttile = (rest % tgs) * kT + tq;
   const bool ttile_ok = ttile < a.tiles;
-  float* tred = red + tq * kMaxGemvRows * kGemvCols;
-  float v[kMaxGemvRows];
+  float* tred = red + tq * kRows * kGemvCols;
+  float v[kRows];
 #pragma unroll
-  for (int r = 0; r < kMaxGemvRows; ++r) v[r] = r < nrows ? tred[r * kGemvCols + t] : 0.0f;
+  for (int r = 0; r < kRows; ++r) v[r] = r < nrows ? tred[r * kGemvCols + t] : 0.0f;
 
   // Every thread reaches every barrier below; a quad that is not the last
   // arriver of its tile only skips the stores.
@@ -401,7 +424,7 @@ void gemv_kernel(const GemvArgs a) {
     float* base = a.partials + ct * a.S * tf;
     if (ttile_ok) {
 #pragma unroll
-      for (int r = 0; r < kMaxGemvRows; ++r)
+      for (int r = 0; r < kRows; ++r)
         if (r < nrows)
           __hip_atomic_store(base + split * tf + r * kGemvCols + t, v[r], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -418,9 +441,9 @@ void gemv_kernel(const GemvArgs a) {
     if (kT == 1 && !mine) return;  // a one-quad workgroup has no other quad to wait for
     if (mine) {
       if (a.S <= 8)
-        read_partials<8>(base, a.S, nrows, t, v);
+        read_partials<8, kRows>(base, a.S, nrows, t, v);
       else
-        read_partials<16>(base, a.S, nrows, t, v);
+        read_partials<16, kRows>(base, a.S, nrows, t, v);
       if (t == 0)
         __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -430,7 +453,7 @@ void gemv_kernel(const GemvArgs a) {
     const int n = ttile * kGemvCols + t;
     if (mine && n < a.N) {
 #pragma unroll
-      for (int r = 0; r < kMaxGemvRows; ++r)
+      for (int r = 0; r < kRows; ++r)
         if (r < nrows) a.out[static_cast<size_t>(pos0 + r) * a.N + n] = v[r];
     }
     return;
@@ -438,14 +461,14 @@ void gemv_kernel(const GemvArgs a) {
   // SwiGLU: columns 0..127 of the tile are gate, 128..255 the matching up columns
   if (mine) {
 #pragma unroll
-    for (int r = 0; r < kMaxGemvRows; ++r)
+    for (int r = 0; r < kRows; ++r)
       if (r < nrows) tred[r * kGemvCols + t] = v[r];
   }
   __syncthreads();
   const int n = ttile * (kGemvCols / 2) + t;
   if (mine && t < kGemvCols / 2 && n < a.N) {
 #pragma unroll
-    for (int r = 0; r < kMaxGemvRows; ++r)
+    for (int r = 0; r < kRows; ++r)
       if (r < nrows)
         a.h[static_cast<size_t>(pos0 + r) * a.N + n] =
             silu(tred[r * kGemvCols + t]) * tred[r * kGemvCols + kGemvCols / 2 + t];
@@ -475,14 +498,15 @@ GemvShape gemv_shape(size_t items, int N, int mode, int G, size_t max_split_task
   return sh;
 }
 
-int gemv_tiles_per_workgroup(size_t num_tasks, int tiles) {
-  if (W4_GEMV_KT > 0) return W4_GEMV_KT;
+int gemv_tiles_per_workgroup(size_t num_tasks, int tiles, int pieces) {
+  const int max_kt = pieces == 1 ? 2 : 4;  // the tile buffers of 16-row quads: two fit
+  if (W4_GEMV_KT > 0) return W4_GEMV_KT < max_kt ? W4_GEMV_KT : max_kt;
   // A launch that fits one round of four-wave workgroups (four per CU) takes
   // the largest workgroups that still give every CU one; longer launches keep
   // four-wave workgroups, which overlap one's tail with the others' streams.
   if (num_tasks > kGemvResidentTasks || tiles <= 0) return 1;
   const size_t rows_splits = num_tasks / static_cast<size_t>(tiles);
-  for (int kt = 4; kt > 1; kt /= 2)
+  for (int kt = max_kt; kt > 1; kt /= 2)
     if (rows_splits * ((tiles + kt - 1) / kt) >= kGemvMinWorkgroups) return kt;
   return 1;
 }
@@ -491,17 +515,26 @@ namespace {
 template <bool kMulti>
 void launch_kt(const GemvArgs& a, int kt, unsigned blocks, hipStream_t stream, hipEvent_t start,
                hipEvent_t stop) {
+  if (a.pieces == 1) {
+    if (kt == 2)
+      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 2, 1>, dim3(blocks), dim3(kGemvThreads * 2), 0, stream, start,
+                            stop, 0, a);
+    else
+      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 1, 1>, dim3(blocks), dim3(kGemvThreads), 0, stream, start, stop,
+                            0, a);
+    return;
+  }
   switch (kt) {
     case 4:
-      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 4>, dim3(blocks), dim3(kGemvThreads * 4), 0, stream, start,
+      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 4, 2>, dim3(blocks), dim3(kGemvThreads * 4), 0, stream, start,
                             stop, 0, a);
       break;
     case 2:
-      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 2>, dim3(blocks), dim3(kGemvThreads * 2), 0, stream, start,
+      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 2, 2>, dim3(blocks), dim3(kGemvThreads * 2), 0, stream, start,
                             stop, 0, a);
       break;
     default:
-      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 1>, dim3(blocks), dim3(kGemvThreads), 0, stream, start, stop,
+      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 1, 2>, dim3(blocks), dim3(kGemvThreads), 0, stream, start, stop,
                             0, a);
       break;
   }
@@ -513,7 +546,8 @@ w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stre
   if (num_tasks == 0) return W4A16_OK;
   if (a.tiles <= 0 || a.S <= 0 || num_tasks % (static_cast<size_t>(a.tiles) * a.S) != 0)
     return W4A16_ERR_INVALID_ARG;
-  const int kt = gemv_tiles_per_workgroup(num_tasks, a.tiles);
+  if (a.pieces != 1 && a.pieces != 2) return W4A16_ERR_INVALID_ARG;
+  const int kt = gemv_tiles_per_workgroup(num_tasks, a.tiles, a.pieces);
   const size_t blocks = num_tasks / a.tiles * ((a.tiles + kt - 1) / kt);
   if (blocks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   if (a.gps > kWin)

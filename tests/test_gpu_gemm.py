@@ -34,7 +34,7 @@ SHAPES = [(32, 64), (64, 128), (192, 64), (256, 512), (1024, 192), (7168, 256)]
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("K,N", SHAPES)
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 17, 64, 65, 130])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 16, 17, 64, 65, 130])
 def test_gemm_small_shapes(M, K, N, dtype):
     qw, sc, w = _make(K, N, 200 + K + N)
     x = x_for_dtype(W.activations(M, K, 200 + M).cuda(), dtype)

@@ -25,7 +25,7 @@ def _mlp_gpu(x, g, u, d):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("H,I", [(64, 128), (256, 512), (1024, 2048)])
-@pytest.mark.parametrize("M", [1, 3, 4, 8, 9, 64, 100])
+@pytest.mark.parametrize("M", [1, 3, 4, 8, 9, 16, 64, 100])
 def test_mlp_small(M, H, I, dtype):
     cfg = 400 + H
     ws_np = [W.weights(H, I, cfg, W.TAG_GATE).numpy(), W.weights(H, I, cfg, W.TAG_UP).numpy(),

@@ -37,8 +37,9 @@ def _run_shared(x, ids, wts, routed, shared):
 @pytest.mark.parametrize("M,E,k,H,I", [(1, 4, 2, 64, 128), (5, 6, 2, 128, 64), (9, 8, 3, 128, 64),
                                        (64, 16, 8, 64, 64), (130, 6, 2, 256, 128), (300, 8, 2, 128, 64)])
 def test_moe_shared_small(M, E, k, H, I, dtype):
-    """M <= 8: the shared expert is a GEMV item; M > 8: MFMA tiles (130 rows: a
-    ragged last tile) next to the routed experts' items (M = 300: five tiles)."""
+    """M <= 64: the shared expert is GEMV items of 8 rows; M > 64: MFMA tiles
+    (130 rows: a ragged last tile) next to the routed experts' items (M = 300:
+    five tiles)."""
     cfg = 700 + M
     (gq, gs), (uq, us), (dq, ds) = _stacks(E, H, I, cfg)
     (sgq, sgs), (suq, sus), (sdq, sds) = _stacks(1, H, I, cfg, first=SHARED_INDEX)
