@@ -47,8 +47,10 @@ struct GemvLds {
   // A operand of the window, unit (g, r, kb) at a_unit(g, r, kb); reused after
   // the main loop as the tile buffers [kT][rows][kGemvCols] of floats
   uint4 buf[kWin * kUnitsPerGroup];
-  float f[kGemvRowsOnePiece];  // 2^-e per row for the current window
+  float f[kGemvRowsOnePiece];  // per row: 2^(e - e before this window), the accumulators' rescale
+  int e[kGemvRowsOnePiece];    // per row: the running exponent e (kNoExp before any nonzero value)
 };
+constexpr int kNoExp = 1 << 20;
 static_assert(kWin % kRing == 0, "ring slots must stay aligned across windows");
 // four quads of 8 rows, or two of 16
 static_assert(sizeof(uint4) * kWin * kUnitsPerGroup >= sizeof(float) * 4 * kMaxGemvRows * kGemvCols,
@@ -120,14 +122,18 @@ __device__ __forceinline__ void load_window(const GemvArgs& a, int gw, int nw, i
   }
 }
 
-// Per row: the window's largest magnitude sets e (max * 2^e in [2^14, 2^15)),
-// the pieces of x * 2^e go to LDS in the A layout and 2^-e to lds.f.  Two
-// pieces (8 rows): piece 0 is A row m, piece 1 A row 8 + m.  One piece (16
-// rows, for bf16 activations it is exact): A row m.  Absent rows get the
+// Per row, a running power of two 2^e over the windows of the split: e is
+// the smallest of the previous e and the one that puts this window's largest
+// magnitude in [2^14, 2^15), so f16 never overflows and the largest values so
+// far keep full precision.  The pieces of x * 2^e go to LDS in the A layout;
+// lds.f gets 2^(e - e before), by which the accumulators are rescaled before
+// the window joins them (an exact power of two, at most 1), and lds.e the new
+// e.  Two pieces (8 rows): piece 0 is A row m, piece 1 A row 8 + m.  One piece
+// (16 rows, for bf16 activations it is exact): A row m.  Absent rows get the
 // factor 0 and are never read as A.
 template <int kW, int kRows, int kP>
 __device__ __forceinline__ void convert_window(GemvLds& lds, int nw, int nrows, int wv, int lane, int pass,
-                                               const float v[Staging<kW, kRows>::kHold][16]) {
+                                               bool first, const float v[Staging<kW, kRows>::kHold][16]) {
   using St = Staging<kW, kRows>;
   const int gl = lane >> 1, hb = lane & 1;
   if (wv >= St::kRowStride) return;  // (wave-uniform) rows are staged by the first waves
@@ -135,7 +141,10 @@ __device__ __forceinline__ void convert_window(GemvLds& lds, int nw, int nrows, 
   for (int j = 0; j < St::kHold; ++j) {
     const int m = wv + (pass * St::kHold + j) * St::kRowStride;
     if (m >= nrows) {
-      if (lane == 0) lds.f[m] = 0.0f;
+      if (lane == 0) {
+        lds.f[m] = 0.0f;
+        lds.e[m] = kNoExp;
+      }
       continue;
     }
     float amax = 0.0f;
@@ -143,14 +152,19 @@ __device__ __forceinline__ void convert_window(GemvLds& lds, int nw, int nrows, 
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    int e = 0;
+    int e_win = kNoExp;
     if (amax > 0.0f) {
       int lg = ilogbf(amax);
-      lg = lg > 120 ? 120 : (lg < -120 ? -120 : lg);
-      e = 14 - lg;
+      lg = lg > 120 ? 120 : (lg < -112 ? -112 : lg);  // 2^e stays a normal float
+      e_win = 14 - lg;
     }
-    const float scale = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
-    if (lane == 0) lds.f[m] = amax > 0.0f ? ldexpf(1.0f, -e) : 0.0f;
+    const int e_old = first ? kNoExp : lds.e[m];  // (all lanes read before lane 0 writes)
+    const int e = min(e_old, e_win);
+    const float scale = e < kNoExp ? ldexpf(1.0f, e) : 0.0f;
+    if (lane == 0) {
+      lds.f[m] = e_old < kNoExp ? ldexpf(1.0f, e - e_old) : 1.0f;
+      lds.e[m] = e;
+    }
     if (gl < nw) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -236,8 +250,6 @@ __device__ __forceinline__ void read_partials(const float* base, int S, int nrow
   }
 }
 
-// kMulti: the split spans more than one staging window (each window's
-// accumulators are scaled by its own 2^-e before they join the total).
 // A workgroup is kT quads of four waves.  Quad q takes column tile
 // tg * kT + q of one item and one K split, so the quads share the staged
 // activation window and start streaming together (a later workgroup on a CU
@@ -248,7 +260,7 @@ __device__ __forceinline__ void read_partials(const float* base, int S, int nrow
 // kP = 2: two f16 pieces of 8 rows per task (float32 activations); kP = 1:
 // one piece of 16 rows (bf16 activations, which one f16 piece holds exactly,
 // or the float32 intermediate of a bf16 layer).
-template <bool kMulti, int kT, int kP>
+template <int kT, int kP>
 __global__ __launch_bounds__(kGemvThreads * kT) __attribute__((amdgpu_waves_per_eu(4)))
 void gemv_kernel(const GemvArgs a) {
   constexpr int kW = 4 * kT;  // waves
@@ -329,20 +341,27 @@ void gemv_kernel(const GemvArgs a) {
       __syncthreads();  // the previous window is consumed
       load_window<kW, kRows>(a, gw, nw, pos0, nrows, wv, lane, 0, xv);
     }
-    convert_window<kW, kRows, kP>(lds, nw, nrows, wv, lane, 0, xv);
+    convert_window<kW, kRows, kP>(lds, nw, nrows, wv, lane, 0, gw == g_lo, xv);
 #pragma unroll
     for (int pass = 1; pass < St::kPasses; ++pass) {
       load_window<kW, kRows>(a, gw, nw, pos0, nrows, wv, lane, pass, xv);
-      convert_window<kW, kRows, kP>(lds, nw, nrows, wv, lane, pass, xv);
+      convert_window<kW, kRows, kP>(lds, nw, nrows, wv, lane, pass, gw == g_lo, xv);
     }
     __syncthreads();
     {
-      f32x4 wacc[4];
-      f32x4* acc = kMulti ? wacc : tot;
-      if (kMulti) {
+      // accumulator element i of this lane is A row 4kb + i: row (4kb + i) & 7
+      // with two pieces, row 4kb + i with one.  Bring the accumulators to this
+      // window's powers of two.
+      const int r0 = kP == 2 ? 4 * (kb & 1) : 4 * kb;
+      if (gw != g_lo) {
+        const float4 f4 = *reinterpret_cast<const float4*>(&lds.f[r0]);
+        const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) wacc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tot[cb][i] *= fr[i];
       }
+      f32x4* acc = tot;
       // kWin is a multiple of kRing, so slots stay aligned across windows; the
       // loads run kRing groups ahead
       for (int gl = 0; gl < nw; gl += kRing) {
@@ -361,21 +380,18 @@ void gemv_kernel(const GemvArgs a) {
         // (no memory fence, so no wait on the ring) keeps them in step.
         if (kT > 1 && kPace > 0 && (gl / kRing) % kPace == kPace - 1) __builtin_amdgcn_s_barrier();
       }
-      // accumulator element i of this lane is A row 4kb + i: row (4kb + i) & 7
-      // with two pieces, row 4kb + i with one
-      const float4 f4 = *reinterpret_cast<const float4*>(&lds.f[kP == 2 ? 4 * (kb & 1) : 4 * kb]);
-      const float fr[4] = {f4.x, f4.y, f4.z, f4.w};
-      if (kMulti) {
+    }
+  }
+  {
+    // back from the running powers of two (rows that never had a nonzero
+    // value, and absent rows, give 0)
+    const int r0 = kP == 2 ? 4 * (kb & 1) : 4 * kb;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+    for (int i = 0; i < 4; ++i) {
+      const int e = lds.e[r0 + i];
+      const float fr = e < kNoExp ? ldexpf(1.0f, -e) : 0.0f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) tot[cb][i] = fmaf(wacc[cb][i], fr[i], tot[cb][i]);
-      } else {
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tot[cb][i] *= fr[i];
-      }
+      for (int cb = 0; cb < 4; ++cb) tot[cb][i] *= fr;
     }
   }
 
@@ -512,30 +528,27 @@ int gemv_tiles_per_workgroup(size_t num_tasks, int tiles, int pieces) {
 }
 
 namespace {
-template <bool kMulti>
 void launch_kt(const GemvArgs& a, int kt, unsigned blocks, hipStream_t stream, hipEvent_t start,
                hipEvent_t stop) {
   if (a.pieces == 1) {
     if (kt == 2)
-      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 2, 1>, dim3(blocks), dim3(kGemvThreads * 2), 0, stream, start,
-                            stop, 0, a);
+      hipExtLaunchKernelGGL(gemv_kernel<2, 1>, dim3(blocks), dim3(kGemvThreads * 2), 0, stream, start, stop, 0,
+                            a);
     else
-      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 1, 1>, dim3(blocks), dim3(kGemvThreads), 0, stream, start, stop,
-                            0, a);
+      hipExtLaunchKernelGGL(gemv_kernel<1, 1>, dim3(blocks), dim3(kGemvThreads), 0, stream, start, stop, 0, a);
     return;
   }
   switch (kt) {
     case 4:
-      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 4, 2>, dim3(blocks), dim3(kGemvThreads * 4), 0, stream, start,
-                            stop, 0, a);
+      hipExtLaunchKernelGGL(gemv_kernel<4, 2>, dim3(blocks), dim3(kGemvThreads * 4), 0, stream, start, stop, 0,
+                            a);
       break;
     case 2:
-      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 2, 2>, dim3(blocks), dim3(kGemvThreads * 2), 0, stream, start,
-                            stop, 0, a);
+      hipExtLaunchKernelGGL(gemv_kernel<2, 2>, dim3(blocks), dim3(kGemvThreads * 2), 0, stream, start, stop, 0,
+                            a);
       break;
     default:
-      hipExtLaunchKernelGGL(gemv_kernel<kMulti, 1, 2>, dim3(blocks), dim3(kGemvThreads), 0, stream, start, stop,
-                            0, a);
+      hipExtLaunchKernelGGL(gemv_kernel<1, 2>, dim3(blocks), dim3(kGemvThreads), 0, stream, start, stop, 0, a);
       break;
   }
 }
@@ -550,10 +563,7 @@ w4a16_status_t launch_gemv(const GemvArgs& a, size_t num_tasks, hipStream_t stre
   const int kt = gemv_tiles_per_workgroup(num_tasks, a.tiles, a.pieces);
   const size_t blocks = num_tasks / a.tiles * ((a.tiles + kt - 1) / kt);
   if (blocks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
-  if (a.gps > kWin)
-    launch_kt<true>(a, kt, static_cast<unsigned>(blocks), stream, start, stop);
-  else
-    launch_kt<false>(a, kt, static_cast<unsigned>(blocks), stream, start, stop);
+  launch_kt(a, kt, static_cast<unsigned>(blocks), stream, start, stop);
   return launch_status();
 }
 

@@ -13,6 +13,14 @@ namespace {
 
 constexpr int kRouteThreads = 1024;
 constexpr int kSharedGemvRows = 64;
+#ifndef W4_GEMV_EXPERT_ROWS_BF16
+#define W4_GEMV_EXPERT_ROWS_BF16 16
+#endif
+// Experts with at most this many rows run on the GEMV (as items of
+// gemv_rows(xt) rows each), heavier ones on the MFMA tiles.
+inline int gemv_expert_rows(w4a16_dtype_t xt) {
+  return xt == W4A16_BF16 ? W4_GEMV_EXPERT_ROWS_BF16 : kMaxGemvRows;
+}
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kRouteLdsInts = 12288;  // 48 KiB: per-wave expert counts and totals
 
@@ -43,10 +51,10 @@ __device__ __forceinline__ uint64_t same_key_lanes(int key, int bits) {
 // running position for its expert plus the number of lower lanes in the same
 // 64-pair step with the same expert, so the order within an expert is pair
 // order.  Ids outside [0, E) are skipped (inv = -1).  Optionally also emits
-// the work items of the grouped layer: an expert with at most gemv_rows rows
-// (8 for float32 activations, 16 for bf16) is one GEMV item, a heavier one is
-// cut into MFMA items of kMfmaRows rows, and heavy[pos] marks the positions
-// that belong to MFMA items.  With
+// the work items of the grouped layer: an expert with at most expert_rows
+// rows is cut into GEMV items of gemv_rows rows (8 for float32 activations,
+// 16 for bf16), a heavier one into MFMA items of kMfmaRows rows, and
+// heavy[pos] marks the positions that belong to MFMA items.  With
 // shared_rows = M a shared expert (id E) takes the positions M * top_k + t,
 // t = 0 .. M-1, one per token in token order (gather entry t * top_k): up to
 // kSharedGemvRows rows as GEMV items of kMaxGemvRows rows, which join the
@@ -56,7 +64,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int32_t* __restrict__ ids, int M, int top_k, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv,
     int4* __restrict__ items_g, int4* __restrict__ items_m, int32_t* __restrict__ n_items,
-    int32_t* __restrict__ heavy, int shared_rows, int gemv_rows) {
+    int32_t* __restrict__ heavy, int shared_rows, int gemv_rows, int expert_rows) {
   extern __shared__ int lds[];  // wc[W][E], then tot[E]
   __shared__ int carry;
   __shared__ int scan[kRouteThreads];
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         const int pos = wc[wv * E + key] + __popcll(m & below);
         sorted_pairs[pos] = p;
         inv[p] = pos;
-        if (heavy != nullptr) heavy[pos] = counts[key] > gemv_rows ? 1 : 0;
+        if (heavy != nullptr) heavy[pos] = counts[key] > expert_rows ? 1 : 0;
       } else if (p < p1) {
         inv[p] = -1;
       }
@@ -168,8 +176,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       const int e = base + tid;
       const int c0 = e < E ? counts[e] : 0;
       int n = 0;
-      if (kind == 0) n = (c0 > 0 && c0 <= gemv_rows) ? 1 : 0;
-      else n = c0 > gemv_rows ? (c0 + kMfmaRows - 1) / kMfmaRows : 0;
+      if (kind == 0) n = (c0 > 0 && c0 <= expert_rows) ? (c0 + gemv_rows - 1) / gemv_rows : 0;
+      else n = c0 > expert_rows ? (c0 + kMfmaRows - 1) / kMfmaRows : 0;
       scan[tid] = n;
       __syncthreads();
       for (int off = 1; off < kRouteThreads; off <<= 1) {
@@ -182,7 +190,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         int it = carry + scan[tid] - n;
         const int o0 = offsets[e];
         if (kind == 0) {
-          items_g[it] = make_int4(e, o0, c0, 0);
+          for (int r = 0; r < c0; r += gemv_rows, ++it)
+            items_g[it] = make_int4(e, o0 + r, min(gemv_rows, c0 - r), 0);
         } else {
           for (int r = 0; r < c0; r += kMfmaRows, ++it)
             items_m[it] = make_int4(e, o0 + r, min(kMfmaRows, c0 - r), 0);
@@ -250,12 +259,12 @@ size_t route_lds_bytes(int E) { return static_cast<size_t>(route_waves(E) + 1) *
 w4a16_status_t launch_route(const int32_t* ids, int M, int top_k, int E, int32_t* counts,
                             int32_t* offsets, int32_t* sorted_pairs, int32_t* inv, int4* items_g,
                             int4* items_m, int32_t* n_items, int32_t* heavy, int shared_rows,
-                            int gemv_rows, hipStream_t stream) {
+                            int gemv_rows, int expert_rows, hipStream_t stream) {
   if (2 * E > kRouteLdsInts) return W4A16_ERR_UNSUPPORTED;
   const size_t lds = route_lds_bytes(E);
   route_kernel<<<1, kRouteThreads, lds, stream>>>(ids, M, top_k, E, counts, offsets, sorted_pairs,
                                                    inv, items_g, items_m, n_items, heavy, shared_rows,
-                                                   gemv_rows);
+                                                   gemv_rows, expert_rows);
   return launch_status();
 }
 
@@ -266,7 +275,7 @@ struct MoePlan {
   size_t counts_off, offsets_off, sorted_off, inv_off, items_off, mitems_off, nitems_off, heavy_off;
   size_t h_off, o_off;
   size_t apx_off, rsx_off, aph_off, rsh_off;
-  bool mfma = false;  // some expert can have more than gemv_rows(xt) rows
+  bool mfma = false;  // some expert can have more than gemv_expert_rows(xt) rows
   size_t bytes = 0;
 };
 
@@ -276,9 +285,12 @@ MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate,
   const int E = gate->num_experts, H = gate->K, I = gate->N;
   p.pairs = static_cast<size_t>(M) * top_k;
   p.positions = p.pairs + (shared ? static_cast<size_t>(M) : 0);
-  p.max_items = std::min<size_t>(E, p.pairs) + 1;  // one GEMV item per light expert
-  p.mfma = M > gemv_rows(xt);                      // an expert gets at most M rows
-  p.max_mitems = p.mfma ? p.pairs / kMfmaRows + std::min<size_t>(E, p.pairs / (gemv_rows(xt) + 1)) + 1 : 0;
+  // GEMV items of the light experts
+  const int per_expert = (gemv_expert_rows(xt) + gemv_rows(xt) - 1) / gemv_rows(xt);
+  p.max_items = std::min<size_t>(E, p.pairs) * per_expert + 1;
+  p.mfma = M > gemv_expert_rows(xt);  // an expert gets at most M rows
+  p.max_mitems =
+      p.mfma ? p.pairs / kMfmaRows + std::min<size_t>(E, p.pairs / (gemv_expert_rows(xt) + 1)) + 1 : 0;
   if (shared) {  // the shared expert is one more expert with M rows
     if (M <= kSharedGemvRows)
       p.max_items += (static_cast<size_t>(M) + kMaxGemvRows - 1) / kMaxGemvRows;
@@ -352,7 +364,7 @@ extern "C" w4a16_status_t w4a16_moe_route(const int32_t* topk_ids, int32_t M, in
       return W4A16_ERR_INVALID_ARG;
   }
   return launch_route(topk_ids, M, top_k, E, counts, offsets, sorted_pairs, inv, nullptr, nullptr,
-                      nullptr, nullptr, 0, kMaxGemvRows, stream);
+                      nullptr, nullptr, 0, kMaxGemvRows, kMaxGemvRows, stream);
 }
 
 extern "C" size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype_t xt,
@@ -417,7 +429,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   // 1. expert grouping and work items
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
   st = launch_route(topk_ids, M, top_k, E, counts, offsets, sorted, inv, items, mitems, n_items,
-                    heavy, shared ? M : 0, gemv_rows(xt), stream);
+                    heavy, shared ? M : 0, gemv_rows(xt), gemv_expert_rows(xt), stream);
   if (st != W4A16_OK) return st;
 
   // 2. gate/up with the SwiGLU epilogue: light experts on the GEMV, heavy on MFMA tiles
