@@ -82,7 +82,7 @@ def test_mlp_full_size(dense_mlp, name, dtype):
     assert np.array_equal(qd, _sampled_down(w_down, cols)[0])
 
 
-@pytest.mark.parametrize("M,dtype,kernels", [(4, "f32", 2), (64, "bf16", 4)])
+@pytest.mark.parametrize("M,dtype,kernels", [(4, "f32", 2), (100, "bf16", 4)])
 def test_mlp_timed_brackets_each_kernel(M, dtype, kernels):
     """w4a16_swiglu_mlp_timed does the same work as w4a16_swiglu_mlp (same
     output bits) and brackets each of its kernels with a start and a stop event."""
