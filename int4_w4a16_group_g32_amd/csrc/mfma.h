@@ -42,7 +42,11 @@ constexpr int kMfmaWgOverheadGroups = W4_MFMA_WG_OVERHEAD_GROUPS;
 struct MfmaArgs {
   const _Float16* ap;  // [P][Mp][K]
   const float* rs;     // [Mp]
-  int Mp;              // rows per piece plane (a multiple of 64, >= positions + 64)
+  int Mp;              // rows per piece plane (a multiple of 64, >= positions + 64, or the token count)
+  // Optional: position p takes piece row arow[min(p, arow_n - 1)] / arow_div
+  // (the token of a routed pair) instead of row p.
+  const int* arow;
+  int arow_div, arow_n;
   int K, G;
   const u32x4* qw0;    // GROUPED chunks, matrix 0 (plain, or gate)
   const float* sc0;

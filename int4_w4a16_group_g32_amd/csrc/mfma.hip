@@ -139,14 +139,23 @@ struct MfmaLds {
 // end are zeroed when the window is stored, so the tail needs no masking.  A
 // load under a branch, or a use of its value before the window's groups are
 // done, would make the compiler's wait cover the code ring as well.
+// The thread's units cover four tile rows, the same in every window and
+// piece plane: srow[j] is the piece row of tile row row_of_unit(j).
+constexpr int kUnitRows = 4;
+__device__ __forceinline__ int row_of_unit(int i) {
+  const int u = static_cast<int>(threadIdx.x) + kMfmaThreads * i;
+  return (u >> 2) / kGw % kMfmaRows;
+}
+
 template <int P>
-__device__ __forceinline__ void load_a_window(const MfmaArgs& a, int pos0, int gw, int g_hi,
+__device__ __forceinline__ void load_a_window(const MfmaArgs& a, const int srow[kUnitRows], int gw, int g_hi,
                                               uint4 r[kWinUnits<P> / kMfmaThreads]) {
+  static_assert(kMfmaThreads * kUnitRows / 4 / kGw == kMfmaRows, "a thread's units repeat every 4 rows");
 #pragma unroll
   for (int i = 0; i < kWinUnits<P> / kMfmaThreads; ++i) {
     const int u = static_cast<int>(threadIdx.x) + kMfmaThreads * i;
-    const int kb = u & 3, gl = (u >> 2) % kGw, row = (u >> 2) / kGw % kMfmaRows, p = (u >> 2) / kGw / kMfmaRows;
-    r[i] = *reinterpret_cast<const uint4*>(a.ap + (static_cast<size_t>(p) * a.Mp + pos0 + row) * a.K +
+    const int kb = u & 3, gl = (u >> 2) % kGw, p = (u >> 2) / kGw / kMfmaRows;
+    r[i] = *reinterpret_cast<const uint4*>(a.ap + (static_cast<size_t>(p) * a.Mp + srow[i % kUnitRows]) * a.K +
                                            static_cast<size_t>(min(gw + gl, g_hi - 1)) * kGroup + 8 * kb);
   }
 }
@@ -325,7 +334,13 @@ void mfma_kernel(const MfmaArgs a) {
   TileCodes ring[R];
   // A wave past the matrix's last column streams column block 0 and stores
   // nothing, so every load below is unconditional.
-  load_a_window<P>(a, pos0, g_lo, g_hi, ra);
+  int srow[kUnitRows];
+#pragma unroll
+  for (int j = 0; j < kUnitRows; ++j) {
+    const int pr = pos0 + row_of_unit(j);
+    srow[j] = a.arow != nullptr ? a.arow[min(pr, a.arow_n - 1)] / a.arow_div : pr;
+  }
+  load_a_window<P>(a, srow, g_lo, g_hi, ra);
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     load_tile_codes(wp, sp, gstride, g_lo + j, g_last, a.gshift, ring[j]);
@@ -355,7 +370,7 @@ void mfma_kernel(const MfmaArgs a) {
   auto window = [&](int wi, auto hc) {
     constexpr int h = decltype(hc)::value;
     const int gw = g_lo + wi * kGw;
-    load_a_window<P>(a, pos0, gw + kGw, g_hi, ra);  // the next window, in flight
+    load_a_window<P>(a, srow, gw + kGw, g_hi, ra);  // the next window, in flight
 #pragma unroll
     for (int j = 0; j < kGw; ++j) {
       mma_tile_group<P>(lds.a[h], j, lc, kb, magic, ring[(kGw * h + j) % R], nrb, cexp, acc);
@@ -446,7 +461,7 @@ void mfma_kernel(const MfmaArgs a) {
       const int r = rb * 16 + 4 * kb + i;
       const bool live = r < nrows;
       const size_t prow = static_cast<size_t>(pos0 + (live ? r : 0));
-      const float f = live ? a.rs[prow] : 0.0f;
+      const float f = live ? a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow] : 0.0f;
       if (a.mode == 0) {
         if (live) {
 #pragma unroll

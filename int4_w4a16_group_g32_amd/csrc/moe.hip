@@ -311,8 +311,10 @@ MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate,
   c.take(p.heavy_off, p.positions * 4);
   c.take(p.h_off, std::max<size_t>(p.positions, p.Mp) * I * 4);
   c.take(p.o_off, p.positions * H * 4);
-  c.take(p.apx_off, static_cast<size_t>(p.P) * p.Mp * H * 2);
-  c.take(p.rsx_off, static_cast<size_t>(p.Mp) * 4);
+  // activation pieces: one row per token (the tiles map positions to tokens)
+  const size_t xrows = p.mfma ? static_cast<size_t>(M) : 0;
+  c.take(p.apx_off, static_cast<size_t>(p.P) * xrows * H * 2);
+  c.take(p.rsx_off, xrows * 4);
   c.take(p.aph_off, static_cast<size_t>(p.P) * p.Mp * I * 2);
   c.take(p.rsh_off, static_cast<size_t>(p.Mp) * 4);
   p.bytes = c.cursor;
@@ -474,11 +476,15 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   MfmaArgs ma{};
   if (p.mfma) {
     if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma_prep(x, xt, T, p.Mp, H, p.P, sorted, top_k, heavy, apx, rsx, stream);
+    // pieces once per token; the tiles read position p from token sorted[p] / top_k
+    st = launch_mfma_prep(x, xt, M, M, H, p.P, nullptr, 0, nullptr, apx, rsx, stream);
     if (st != W4A16_OK) return st;
     ma.ap = apx;
     ma.rs = rsx;
-    ma.Mp = p.Mp;
+    ma.Mp = M;
+    ma.arow = sorted;
+    ma.arow_div = top_k;
+    ma.arow_n = T;
     ma.K = H;
     ma.G = H / kGroup;
     ma.qw0 = a.qw0;
@@ -542,6 +548,8 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     MfmaArgs md = ma;
     md.ap = aph;
     md.rs = rsh;
+    md.Mp = p.Mp;  // pieces of h: one row per position
+    md.arow = nullptr;
     md.K = I;
     md.G = I / kGroup;
     md.qw0 = d.qw0;
