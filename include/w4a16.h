@@ -150,8 +150,10 @@ W4A16_API size_t w4a16_gemm_workspace_bytes(int32_t M, const w4a16_weight_t* w, 
 /*
  * y[M][N] = x[M][K] * dequant(W), float32 accumulation and output (page "The
  * Weight of Precision", section "The Kernel: w4a16_gemm").  W must be a dense
- * (num_experts == 1) GROUPED weight.  M <= 8 runs a split-K GEMV on the
- * matrix cores (all rows in one MFMA tile); larger M runs 64-row MFMA tiles.
+ * (num_experts == 1) GROUPED weight.  Up to 8 rows (float32 activations) or
+ * 16 rows (bf16) run a split-K GEMV on the matrix cores (all rows in one MFMA
+ * tile); larger M runs 64-row MFMA tiles, and bf16 from 256 rows 256 x 128
+ * tiles.
  * Deterministic: the same inputs give bitwise the same y.
  * Errors: INVALID_ARG (null/misaligned, M < 0, bad dtype, y aliasing x),
  * UNSUPPORTED (layout, group size, K % group size, N % 64, num_experts != 1),
@@ -188,7 +190,8 @@ W4A16_API w4a16_status_t w4a16_swiglu_mlp(const void* x, w4a16_dtype_t xt, int32
  * the runtime from the kernel's own dispatch (hipExtLaunchKernel), so their
  * interval is the kernel's execution time without the launch gap.  At most
  * `capacity` events (kernels beyond capacity / 2 run unbracketed); *recorded
- * (if not NULL) receives how many were used.  For M <= 8 the dense MLP launches two kernels (fused gate/up
+ * (if not NULL) receives how many were used.  Up to 8 rows (float32) or 16
+ * (bf16) the dense MLP launches two kernels (fused gate/up
  * GEMV with the SwiGLU epilogue, down GEMV); for larger M four (activation
  * pieces, fused gate/up MFMA tiles, pieces of the intermediate, down MFMA).  Events are created and
  * owned by the caller.  Errors as w4a16_swiglu_mlp, plus INVALID_ARG for
@@ -248,8 +251,8 @@ W4A16_API size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype
  * and topk_w [M][top_k] (int32 / float32), y [M][H] float32.  The routing lists
  * (as w4a16_moe_route), the per-pair intermediate and the per-pair outputs
  * live in the workspace; per-expert row counts never leave the device.
- * Experts with at most 8 rows run on the GEMV kernels, heavier experts on MFMA
- * tiles of 64 rows.
+ * Experts with at most 8 rows (float32 activations) or 16 rows (bf16) run on
+ * the GEMV kernels, heavier experts on MFMA tiles of 64 rows.
  * Errors as w4a16_swiglu_mlp plus INVALID_ARG for top_k < 1 or top_k > E and
  * UNSUPPORTED for more than 6144 experts.
  */
@@ -289,11 +292,17 @@ W4A16_API w4a16_status_t w4a16_moe_grouped_shared(const void* x, w4a16_dtype_t x
                                         size_t ws_bytes, hipStream_t stream);
 
 /*
- * Measurement variant of w4a16_moe_grouped, with the event convention of
- * w4a16_swiglu_mlp_timed.  Kernels in launch order: expert grouping; gate/up
- * GEMV for experts with at most 8 rows; when M > 8, activation pieces and
- * gate/up MFMA tiles for heavier experts; down GEMV; when M > 8, pieces of the
- * intermediate and down MFMA tiles; weighted combine.
+ * Measurement variant of w4a16_moe_grouped: identical work and results, and in
+ * addition records the caller's events on `stream` between the kernels it
+ * launches: events[i] just before kernel i and one more after the last (each
+ * interval also holds the next kernel's dispatch gap), at most `capacity`
+ * events; *recorded (if not NULL) receives how many were recorded.  Kernels in
+ * launch order: expert grouping; gate/up GEMV for the light experts (at most
+ * 8 rows with float32 activations, 16 with bf16); when some expert can be
+ * heavier, activation pieces (one row per token) and gate/up MFMA tiles; down
+ * GEMV; then pieces of the intermediate and down MFMA tiles; weighted combine.
+ * Errors as w4a16_moe_grouped, plus INVALID_ARG for capacity < 0 or
+ * events == NULL with capacity > 0, and HIP if recording fails.
  */
 W4A16_API w4a16_status_t w4a16_moe_grouped_timed(
     const void* x, w4a16_dtype_t xt, int32_t M, const int32_t* topk_ids, const float* topk_w,
