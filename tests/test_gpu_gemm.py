@@ -223,3 +223,27 @@ def test_gemv_four_tile_workgroups_ragged(M, dtype):
     print(f"gemv 4-tile workgroups M={M} K={K} N={N} {dtype} relF={err:.3e}", flush=True)
     assert err <= tol_for(dtype)
     assert not torch.isnan(y).any()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("pattern", ["rising", "falling", "alternating"])
+def test_gemv_running_power_of_two_across_windows(pattern, dtype):
+    """K = 65536, N = 256, M = 4: 32 K splits of 64 groups, so every split of
+    the GEMV spans two 32-group staging windows.  Each 1024-column window of x
+    is scaled by its own power of two (2^-40 .. 2^40), so the running power of
+    two of a row moves between windows and the accumulators are rescaled.  The
+    result matches the oracle and holds no inf or NaN."""
+    K, N, M = 65536, 256, 4
+    qw, sc, w = _make(K, N, 540)
+    win = 1024
+    nwin = K // win
+    exps = {"rising": np.linspace(-40, 40, nwin), "falling": np.linspace(40, -40, nwin),
+            "alternating": np.where(np.arange(nwin) % 2 == 0, 40.0, -40.0)}[pattern]
+    factors = np.repeat(np.exp2(np.round(exps)), win).astype(np.float32)
+    x32 = W.activations(M, K, 541) * torch.as_tensor(factors)[None, :]
+    x = x_for_dtype(x32.cuda(), dtype)
+    y, _ = _run_gemm(x, w, N)
+    assert torch.isfinite(y).all()
+    err = rel_err(y, O.gemm64(x_values(x), qw, sc))
+    print(f"gemv running 2^e {pattern} {dtype} relF={err:.3e}", flush=True)
+    assert err <= tol_for(dtype)
