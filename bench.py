@@ -223,8 +223,12 @@ def run_moe(args, cfg):
     ws = L.new_workspace(L.moe_workspace_bytes(M, k, xt, *stacks))
     lib = L.load_library()
     sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    names = (["route", "gate_up_gemv", "down_gemv", "combine"] if M <= 8 else
-             ["route", "gate_up_gemv", "prep_x", "gate_up_mfma", "down_gemv", "prep_h", "down_mfma", "combine"])
+    # the kernels of one layer: light experts (at most 8 rows with float32
+    # activations, 16 with bf16) on the GEMV; when an expert can be heavier,
+    # activation pieces and 64-row tiles as well
+    mfma = M > (16 if xt == L.BF16 else 8)
+    names = (["route", "gate_up_gemv", "prep_x", "gate_up_mfma", "down_gemv", "prep_h", "down_mfma", "combine"]
+             if mfma else ["route", "gate_up_gemv", "down_gemv", "combine"])
     nev = len(names) + 1
 
     def step(evs=None):

@@ -70,6 +70,7 @@ def _moe_gpu(x, ids, wts, g, u, d):
     (1, 4, 2, 64, 128, "uniform"), (9, 8, 3, 128, 64, "uniform"), (40, 6, 2, 256, 128, "uniform"),
     (64, 16, 8, 64, 64, "uniform"),
     (24, 16, 8, 128, 128, "uniform"),   # 9-16 rows per expert: GEMV items for bf16, tiles for float32
+    (40, 16, 8, 128, 128, "uniform"),   # 14-26 rows per expert: 64-row tiles with one or two live row blocks
     (200, 4, 2, 128, 256, "uniform"),   # every expert heavy: MFMA tiles only, ragged last tile
     (300, 64, 4, 256, 128, "zipf"),     # heavy head, light tail: both paths in one call
 ])
