@@ -258,6 +258,7 @@ def run_moe(args, cfg):
         "kernels_us": {n: round(v * 1e3, 2) for n, v in kern.items()},
         "ms_per_step_marked": round(ms_marked, 5),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        **({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_moe(cfg, ids_np, wts, x)}),
     }
 
 
@@ -352,6 +353,7 @@ def run_gemm(args, cfg):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.x_dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "M": M, "K": K, "N": N, "bytes_per_step": step_bytes, "flops_per_step": flops},
         "pct_mfma_peak_bf16": round(100 * tflops / 2500.0, 1), "gbs": round(gbs, 1),
+        **({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_gemm(cfg, x, big)}),
     }
 
 
@@ -421,6 +423,69 @@ def per_kernel_ms(args, names, step, cap=None, paired=False):
     else:
         kern = {n: statistics.mean(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
     return kern, t0.elapsed_time(t1) / args.steps
+
+
+def _blas_threads():
+    from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+
+def cpu_baseline_moe(cfg, ids_np, wts, x, tokens=2, repeats=3):
+    """The oracle's float64 MoE layer on a bounded sample: the first `tokens`
+    tokens, through every expert they are routed to (weights drawn by the
+    same generator and quantized by the oracle, not timed).  Value in the
+    metric's unit: the sample's algorithmic bytes (its experts' weights, its
+    activations and outputs) per second of oracle time."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+
+    E, H, I = cfg.experts, cfg.K, cfg.N
+    sample = np.arange(tokens)
+    experts = np.unique(ids_np[sample])
+    codes = {}
+    for e in experts:
+        codes[int(e)] = tuple(O.quantize_w4a16(W.weights(K, N, cfg.index, tag, int(e), device="cuda").cpu().numpy())
+                              for tag, (K, N) in ((W.TAG_GATE, (H, I)), (W.TAG_UP, (H, I)), (W.TAG_DOWN, (I, H))))
+    xs = x.float().cpu().numpy()
+    w_np = wts.cpu().numpy()
+    times = []
+    for _ in range(repeats):
+        t = time.perf_counter()
+        O.moe64(xs, ids_np, w_np, lambda e: codes[e], E, tokens=sample)
+        times.append(time.perf_counter() - t)
+    sec = statistics.median(times)
+    xbytes = 4 if cfg.x_dtype == "f32" else 2
+    nbytes = len(experts) * 3 * H * I * 5 // 8 + tokens * H * (xbytes + 4)
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{tokens} of the {cfg.M} tokens through their {len(experts)} experts ({nbytes} algorithmic "
+                      f"bytes), numpy float64 dequantize-then-matmul, median of {repeats} runs of {sec:.2f}s",
+            "seconds": round(sec, 3)}
+
+
+def cpu_baseline_gemm(cfg, x, big, repeats=3):
+    """The oracle's float64 GEMM (dequantize, then matmul) on the whole
+    workload, the weights drawn by the same generator and quantized by the
+    oracle (not timed); in TFLOP/s when M >= 512, else GB/s."""
+    import oracle as O
+    import workloads as W
+
+    M, K, N = cfg.M, cfg.K, cfg.N
+    qw, sc = O.quantize_w4a16(W.weights(K, N, cfg.index, W.TAG_GATE, 0, device="cuda").cpu().numpy())
+    xs = x.float().cpu().numpy()
+    times = []
+    for _ in range(repeats):
+        t = time.perf_counter()
+        O.gemm64(xs, qw, sc)
+        times.append(time.perf_counter() - t)
+    sec = statistics.median(times)
+    xbytes = 4 if cfg.x_dtype == "f32" else 2
+    nbytes = K * N * 5 // 8 + M * K * xbytes + M * N * 4
+    value = 2.0 * M * K * N / sec / 1e12 if big else nbytes / sec / 1e9
+    return {"value": round(value, 6), "unit": "TFLOP/s" if big else "GB/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"the whole {cfg.name} GEMM, numpy float64 dequantize-then-matmul, median of {repeats} runs "
+                      f"of {sec:.3f}s", "seconds": round(sec, 4)}
 
 
 def cpu_baseline_mlp(cfg, base, repeats=7):
