@@ -219,7 +219,8 @@ __device__ __forceinline__ void mma_group(const GemvLds& lds, int gl, int lc, in
 
 // Sums of the S split partials of rows 0..nrows-1, column t, in split order:
 // blocks of 4 rows x kB splits are loaded together (indices clamped into
-// range, so no load is predicated) and then added.
+// range, so no load is predicated) and then added.  Up to 20 splits take one
+// round trip (the decode down projection runs 18).
 template <int kB, int kRows>
 __device__ __forceinline__ void read_partials(const float* base, int S, int nrows, int t, float v[kRows]) {
   constexpr size_t tf = kPartialTileFloats;
@@ -458,6 +459,8 @@ void gemv_kernel(const GemvArgs a) {
     if (mine) {
       if (a.S <= 8)
         read_partials<8, kRows>(base, a.S, nrows, t, v);
+      else if (a.S <= 20)
+        read_partials<20, kRows>(base, a.S, nrows, t, v);
       else
         read_partials<16, kRows>(base, a.S, nrows, t, v);
       if (t == 0)
