@@ -13,6 +13,10 @@ namespace {
 
 constexpr int kRouteThreads = 1024;
 constexpr int kSharedGemvRows = 64;
+#ifndef W4_SHARED_FIRST
+#define W4_SHARED_FIRST 1
+#endif
+constexpr bool kSharedFirst = W4_SHARED_FIRST != 0;  // shared expert's items ahead of the routed ones
 #ifndef W4_GEMV_EXPERT_ROWS_BF16
 #define W4_GEMV_EXPERT_ROWS_BF16 16
 #endif
@@ -59,7 +63,8 @@ __device__ __forceinline__ uint64_t same_key_lanes(int key, int bits) {
 // t = 0 .. M-1, one per token in token order (gather entry t * top_k): up to
 // kSharedGemvRows rows as GEMV items of kMaxGemvRows rows, which join the
 // routed experts' GEMV launches (the MFMA items have no K split, so a lone
-// heavy expert would be a long serial tail), more as MFMA items.
+// heavy expert would be a long serial tail), more as MFMA items; either way
+// they take the first item indices of their launch.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int32_t* __restrict__ ids, int M, int top_k, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ inv,
@@ -168,9 +173,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   }
   if (items_g == nullptr) return;
   __syncthreads();
-  // C. work items: exclusive scans over experts of the GEMV and MFMA item counts
+  // C. work items: exclusive scans over experts of the GEMV and MFMA item counts.
+  // The shared expert's items (all of one kind) take the first indices of
+  // their launch, so they are dispatched first and the routed experts' items
+  // fill in behind them.
+  const int shared_kind = shared_rows > kSharedGemvRows ? 1 : 0;
+  const int shared_step = shared_kind == 1 ? kMfmaRows : kMaxGemvRows;
+  const int shared_items = (shared_rows + shared_step - 1) / shared_step;
   for (int kind = 0; kind < 2; ++kind) {
-    if (tid == 0) carry = 0;
+    const int lead = (kSharedFirst && kind == shared_kind) ? shared_items : 0;
+    if (tid == 0) carry = lead;
     __syncthreads();
     for (int base = 0; base < E; base += kRouteThreads) {
       const int e = base + tid;
@@ -201,21 +213,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
       if (tid == kRouteThreads - 1) carry += scan[tid];
       __syncthreads();
     }
-    if (tid == 0) n_items[kind] = carry;
+    if (tid == 0) n_items[kind] = carry + ((!kSharedFirst && kind == shared_kind) ? shared_items : 0);
     __syncthreads();
   }
-  if (shared_rows > 0 && tid == 0) {  // the shared expert's items go last
-    if (shared_rows <= kSharedGemvRows) {
-      int it = n_items[0];
-      for (int r = 0; r < shared_rows; r += kMaxGemvRows, ++it)
-        items_g[it] = make_int4(E, pairs + r, min(kMaxGemvRows, shared_rows - r), 0);
-      n_items[0] = it;
-    } else {
-      int it = n_items[1];
-      for (int r = 0; r < shared_rows; r += kMfmaRows, ++it)
-        items_m[it] = make_int4(E, pairs + r, min(kMfmaRows, shared_rows - r), 0);
-      n_items[1] = it;
-    }
+  if (shared_rows > 0 && tid == 0) {
+    int it = kSharedFirst ? 0 : n_items[shared_kind] - shared_items;
+    int4* dst = shared_kind == 1 ? items_m : items_g;
+    for (int r = 0; r < shared_rows; r += shared_step, ++it)
+      dst[it] = make_int4(E, pairs + r, min(shared_step, shared_rows - r), 0);
   }
 }
 
