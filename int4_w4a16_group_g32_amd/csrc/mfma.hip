@@ -29,6 +29,10 @@ constexpr int kTileRing = 2 * kGw;  // groups of codes in flight per wave (two w
 // allows; dense launches keep two waves and two windows.
 constexpr int kGroupedRing = kGw;
 constexpr int kPrepThreads = 1024;
+#ifndef W4_PREP_WAVE
+#define W4_PREP_WAVE 1
+#endif
+constexpr bool kPrepWave = W4_PREP_WAVE != 0;  // one wave per row for rows of at most 4096 values
 
 // ------------------------------------------------------------ activation pieces
 
@@ -114,6 +118,93 @@ __global__ __launch_bounds__(kPrepThreads) void mfma_prep_kernel(const XT* __res
     *reinterpret_cast<half8*>(ap + static_cast<size_t>(row) * K + 8 * b) = h0;
     if (P == 2) *reinterpret_cast<half8*>(ap + (static_cast<size_t>(Mp) + row) * K + 8 * b) = h1;
   }
+}
+
+// The same pieces for rows of at most 64 * kB blocks of 8: one wave per row,
+// four rows per workgroup.  Each lane keeps its kB blocks in registers
+// between the two passes, and the largest magnitude needs only a wave
+// reduction, so short rows (the down projection's h of an expert, K = 2048)
+// no longer leave most of a 1024-thread workgroup idle.
+constexpr int kPrepWaveThreads = 256;
+
+template <typename XT, int P, int kB>
+__global__ __launch_bounds__(kPrepWaveThreads) void mfma_prep_wave_kernel(const XT* __restrict__ x, int R, int Mp,
+                                                                          int K, const int* __restrict__ gather,
+                                                                          int top_k, const int* __restrict__ need,
+                                                                          _Float16* __restrict__ ap,
+                                                                          float* __restrict__ rs) {
+  const int row = static_cast<int>(blockIdx.x) * (kPrepWaveThreads / kWave) + wave_id();
+  if (row >= Mp) return;
+  if (need != nullptr && (row >= R || need[row] == 0)) return;
+  long src = row < R ? row : -1;
+  if (src >= 0 && gather != nullptr) {
+    const int pr = gather[row];
+    src = pr < 0 ? -1 : pr / top_k;
+  }
+  const XT* xr = x + (src < 0 ? 0 : src) * static_cast<size_t>(K);
+  const int nb = K / 8;
+  const int lane = lane_id();
+  float v[kB][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kB; ++i) {
+    const int b = lane + kWave * i;
+    if (src >= 0 && b < nb) {
+      load8<XT>(xr, b, v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  int e = 0;
+  if (amax > 0.0f) {
+    int lg = ilogbf(amax);
+    lg = lg > 120 ? 120 : (lg < -120 ? -120 : lg);
+    e = 14 - lg;
+  }
+  const float scale = (src >= 0 && amax > 0.0f) ? ldexpf(1.0f, e) : 0.0f;
+  if (lane == 0) rs[row] = scale > 0.0f ? ldexpf(1.0f, -e) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < kB; ++i) {
+    const int b = lane + kWave * i;
+    if (b >= nb) break;
+    half8 h0, h1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // a row without a nonzero value stores +0 pieces, as the workgroup form does
+      const float t = scale != 0.0f ? v[i][kCodeOrder[j]] * scale : 0.0f;
+      const _Float16 hi = static_cast<_Float16>(t);
+      h0[j] = hi;
+      if (P == 2) h1[j] = static_cast<_Float16>(t - static_cast<float>(hi));
+    }
+    *reinterpret_cast<half8*>(ap + static_cast<size_t>(row) * K + 8 * b) = h0;
+    if (P == 2) *reinterpret_cast<half8*>(ap + (static_cast<size_t>(Mp) + row) * K + 8 * b) = h1;
+  }
+}
+
+template <int kB>
+void launch_prep_wave(const void* x, w4a16_dtype_t xt, int R, int Mp, int K, int P, const int* gather, int top_k,
+                      const int* need, _Float16* ap, float* rs, hipStream_t stream, hipEvent_t start,
+                      hipEvent_t stop) {
+  const float* xf = static_cast<const float*>(x);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const dim3 g((Mp + kPrepWaveThreads / kWave - 1) / (kPrepWaveThreads / kWave)), b(kPrepWaveThreads);
+  if (xt == W4A16_F32 && P == 2)
+    hipExtLaunchKernelGGL(mfma_prep_wave_kernel<float, 2, kB>, g, b, 0, stream, start, stop, 0, xf, R, Mp, K,
+                          gather, top_k, need, ap, rs);
+  else if (xt == W4A16_F32)
+    hipExtLaunchKernelGGL(mfma_prep_wave_kernel<float, 1, kB>, g, b, 0, stream, start, stop, 0, xf, R, Mp, K,
+                          gather, top_k, need, ap, rs);
+  else if (P == 2)
+    hipExtLaunchKernelGGL(mfma_prep_wave_kernel<uint16_t, 2, kB>, g, b, 0, stream, start, stop, 0, xb, R, Mp, K,
+                          gather, top_k, need, ap, rs);
+  else
+    hipExtLaunchKernelGGL(mfma_prep_wave_kernel<uint16_t, 1, kB>, g, b, 0, stream, start, stop, 0, xb, R, Mp, K,
+                          gather, top_k, need, ap, rs);
 }
 
 // ------------------------------------------------------------ the MFMA kernel
@@ -490,6 +581,14 @@ w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, 
                                 const int* gather, int top_k, const int* need, _Float16* ap,
                                 float* rs, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (Mp == 0) return W4A16_OK;
+  if (kPrepWave && K / 8 <= kWave * 4) {
+    launch_prep_wave<4>(x, xt, R, Mp, K, P, gather, top_k, need, ap, rs, stream, start, stop);
+    return launch_status();
+  }
+  if (kPrepWave && K / 8 <= kWave * 8) {
+    launch_prep_wave<8>(x, xt, R, Mp, K, P, gather, top_k, need, ap, rs, stream, start, stop);
+    return launch_status();
+  }
   const float* xf = static_cast<const float*>(x);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const dim3 g(Mp), b(kPrepThreads);
