@@ -17,6 +17,10 @@ constexpr int kSharedGemvRows = 64;
 #define W4_SHARED_FIRST 1
 #endif
 constexpr bool kSharedFirst = W4_SHARED_FIRST != 0;  // shared expert's items ahead of the routed ones
+#ifndef W4_COMBINE_BATCH
+#define W4_COMBINE_BATCH 8
+#endif
+constexpr int kCombineBatch = W4_COMBINE_BATCH;  // routed slots whose loads the combine issues together
 #ifndef W4_GEMV_EXPERT_ROWS_BF16
 #define W4_GEMV_EXPERT_ROWS_BF16 16
 #endif
@@ -238,15 +242,29 @@ __global__ void combine_kernel(const float* __restrict__ o, const int32_t* __res
   const int t = static_cast<int>(idx / H4);
   const int n4 = static_cast<int>(idx % H4);
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int s = 0; s < top_k; ++s) {
-    const int pos = inv[t * top_k + s];
-    if (pos >= 0) {
-      const float w = topk_w[t * top_k + s];
-      const float4 v = reinterpret_cast<const float4*>(o + static_cast<size_t>(pos) * H)[n4];
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
+  // Slots in batches of kCombineBatch: all loads of a batch are issued before
+  // its first fma (a skipped slot reads row 0 and leaves acc unchanged), and
+  // the fmas run in slot order.
+  for (int s0 = 0; s0 < top_k; s0 += kCombineBatch) {
+    int pos[kCombineBatch];
+    float w[kCombineBatch];
+    float4 v[kCombineBatch];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      const int s = s0 + i;
+      pos[i] = s < top_k ? inv[t * top_k + s] : -1;
+      w[i] = s < top_k ? topk_w[t * top_k + s] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i)
+      v[i] = reinterpret_cast<const float4*>(o + static_cast<size_t>(pos[i] < 0 ? 0 : pos[i]) * H)[n4];
+#pragma unroll
+    for (int i = 0; i < kCombineBatch; ++i) {
+      if (pos[i] < 0) continue;
+      acc.x = fmaf(w[i], v[i].x, acc.x);
+      acc.y = fmaf(w[i], v[i].y, acc.y);
+      acc.z = fmaf(w[i], v[i].z, acc.z);
+      acc.w = fmaf(w[i], v[i].w, acc.w);
     }
   }
   if (shared0 >= 0) {
