@@ -13,6 +13,7 @@ from .w4a16 import (  # noqa: F401
     dequant32,
     dequant64,
     gemm64,
+    gemm_abs64,
     silu64,
     swiglu_mlp64,
     route,

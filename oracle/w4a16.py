@@ -122,6 +122,19 @@ def gemm64(x: np.ndarray, qw: np.ndarray, sc: np.ndarray) -> np.ndarray:
     return x @ dequant64(qw, sc)
 
 
+def gemm_abs64(a: np.ndarray, qw: np.ndarray, sc: np.ndarray) -> np.ndarray:
+    """|a| @ |dequant(W)| in float64: the sum of the magnitudes of the terms of
+    every dot product of gemm64.
+
+    Not a step of the method: it is the scale against which the rounding error
+    of one output element is bounded (a computed dot product differs from
+    the exact one by at most a small multiple of this sum), so that a parity
+    test can hold every element to a bound instead of only the norm.
+    """
+    a = np.abs(np.asarray(a, dtype=np.float64))
+    return a @ np.abs(dequant64(qw, sc))
+
+
 def silu64(z: np.ndarray) -> np.ndarray:
     """SiLU, z / (1 + exp(-z)).  The pages name SwiGLU ([WP] "The Context That
     Produced This Message"); the gate activation is read as SiLU."""
@@ -193,7 +206,12 @@ def moe_topk(logits: np.ndarray, top_k: int):
     return ids, w
 
 
-def moe64(x, topk_ids, topk_w, expert, num_experts, tokens=None) -> np.ndarray:
+def _expert_job(job):
+    xs, gate, up, down = job
+    return swiglu_mlp64(xs, gate, up, down)
+
+
+def moe64(x, topk_ids, topk_w, expert, num_experts, tokens=None, map_fn=map) -> np.ndarray:
     """Routed-expert SwiGLU MoE layer in float64.
 
     [FW] "What the Edit Actually Changes": for each token the router selects
@@ -205,6 +223,9 @@ def moe64(x, topk_ids, topk_w, expert, num_experts, tokens=None) -> np.ndarray:
     ``expert(e)`` returns ((qw_g, sc_g), (qw_u, sc_u), (qw_d, sc_d)) for expert
     e, so only experts that are used are ever dequantized.  ``tokens`` limits
     the evaluation to a subset of token rows (returned in that order).
+    ``map_fn`` evaluates the experts' MLPs, which are independent of one
+    another (the builtin map by default; a process pool's map runs them in
+    parallel without changing any arithmetic).
     """
     x = np.asarray(x, dtype=np.float64)
     ids = np.asarray(topk_ids, dtype=np.int64)
@@ -213,10 +234,10 @@ def moe64(x, topk_ids, topk_w, expert, num_experts, tokens=None) -> np.ndarray:
     rows = np.arange(M) if tokens is None else np.asarray(tokens, dtype=np.int64)
     sub_ids = ids[rows]
     out = {}  # (row index in ``rows``, slot) -> expert output
-    for e in np.unique(sub_ids):
-        sel = np.argwhere(sub_ids == e)  # (row, slot), row-major = token order
-        gate, up, down = expert(int(e))
-        o = swiglu_mlp64(x[rows[sel[:, 0]]], gate, up, down)
+    experts = np.unique(sub_ids)
+    sels = [np.argwhere(sub_ids == e) for e in experts]  # (row, slot), row-major = token order
+    jobs = ((x[rows[sel[:, 0]]], *expert(int(e))) for e, sel in zip(experts, sels))
+    for sel, o in zip(sels, map_fn(_expert_job, jobs)):
         for (r, s), v in zip(sel, o):
             out[(int(r), int(s))] = v
     H = None
@@ -233,7 +254,7 @@ def moe64(x, topk_ids, topk_w, expert, num_experts, tokens=None) -> np.ndarray:
     return y
 
 
-def moe_shared64(x, topk_ids, topk_w, expert, num_experts, shared, tokens=None) -> np.ndarray:
+def moe_shared64(x, topk_ids, topk_w, expert, num_experts, shared, tokens=None, map_fn=map) -> np.ndarray:
     """Routed experts plus one shared expert, float64.
 
     [WP] section "The Engine Dispatch: Model::linear" puts the shared expert
@@ -247,7 +268,7 @@ def moe_shared64(x, topk_ids, topk_w, expert, num_experts, shared, tokens=None) 
     """
     x = np.asarray(x, dtype=np.float64)
     rows = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    routed = moe64(x, topk_ids, topk_w, expert, num_experts, tokens)
+    routed = moe64(x, topk_ids, topk_w, expert, num_experts, tokens, map_fn)
     return routed + swiglu_mlp64(x[rows], *shared)
 
 

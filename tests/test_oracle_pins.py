@@ -457,3 +457,74 @@ def test_gemm64_brute_force_other_group_sizes(M, K, N, group):
             for k in range(K):
                 acc += Fraction(float(x[m, k])) * int(q[k, n]) * Fraction(float(sc[k // group, n]))
             assert Fraction(float(y[m, n])) == acc, (m, n)
+
+
+# ---------------------------------------------------------------- error-bound scale, metric, map_fn
+
+@pytest.mark.parametrize("M,K,N", [(1, 32, 1), (3, 64, 8), (2, 96, 5)])
+def test_gemm_abs64_matches_exact_rational_brute_force(M, K, N):
+    """sum_k |x| * |q| * |s| by a scalar Fraction loop, exact on dyadic inputs
+    (negative scales included, so a dropped abs on either factor fails)."""
+    rng = np.random.default_rng(7 * M + K + N)
+    x = _dyadic(rng, (M, K), 6, -3, 3)
+    q = rng.integers(-8, 8, size=(K, N))
+    qw = O.pack_nibbles(q + 8)
+    sc = _dyadic(rng, (K // 32, N), 6, -8, -2)
+    y = O.gemm_abs64(x, qw, sc)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += abs(Fraction(float(x[m, k]))) * abs(int(q[k, n])) * abs(Fraction(float(sc[k // 32, n])))
+            assert Fraction(float(y[m, n])) == acc, (m, n)
+
+
+def test_gemm_abs64_bounds_gemm64_and_equals_it_for_nonnegative_terms():
+    rng = np.random.default_rng(41)
+    K, N = 256, 64
+    x = rng.standard_normal((5, K)).astype(np.float32)
+    q = rng.integers(-8, 8, size=(K, N))
+    sc = (rng.random((K // 32, N)) + 0.5).astype(np.float32)
+    qw = O.pack_nibbles(q + 8)
+    assert (np.abs(O.gemm64(x, qw, sc)) <= O.gemm_abs64(x, qw, sc)).all()
+    assert np.array_equal(O.gemm_abs64(-x, qw, sc), O.gemm_abs64(x, qw, sc))
+    # every term nonnegative (x >= 0, q >= 0, s > 0): the two coincide
+    qp = O.pack_nibbles(np.minimum(np.abs(q), 7) + 8)
+    assert np.array_equal(O.gemm_abs64(np.abs(x), qp, sc), O.gemm64(np.abs(x), qp, sc))
+
+
+def test_rel_frobenius_hand_values():
+    """||y - ref||_F / ||ref||_F worked by hand: y = [3, 4], ref = [0, 5] gives
+    ||[3, -1]|| / 5 = sqrt(10) / 5; a matrix case; equal inputs give 0; a zero
+    reference returns the absolute norm."""
+    assert O.rel_frobenius([3.0, 4.0], [0.0, 5.0]) == pytest.approx(np.sqrt(10.0) / 5.0, rel=1e-15)
+    assert O.rel_frobenius([[1.0, 2.0], [2.0, 0.0]], [[1.0, 0.0], [0.0, 0.0]]) == pytest.approx(np.sqrt(8.0),
+                                                                                              rel=1e-15)
+    assert O.rel_frobenius([[1.0, -2.0]], [[1.0, -2.0]]) == 0.0
+    assert O.rel_frobenius([0.0, 3.0, 4.0], [0.0, 0.0, 0.0]) == 5.0
+
+
+def test_moe_map_fn_and_repeated_ids():
+    """The experts' MLPs are independent: evaluating them in another order
+    gives the same bits.  A token that names one expert twice gets that
+    expert's output once per slot (the per-(token, slot) definition)."""
+    rng = np.random.default_rng(43)
+    M, E, k, H, I = 6, 4, 3, 32, 64
+    x = rng.standard_normal((M, H)).astype(np.float32)
+    ex = _experts(rng, E, H, I)
+    ids = rng.integers(0, E, size=(M, k))
+    ids[0] = [2, 2, 1]
+    ids[1] = [3, 3, 3]
+    w = rng.random((M, k)).astype(np.float32)
+    y = O.moe64(x, ids, w, ex, E)
+
+    def reversed_map(fn, it):
+        jobs = list(it)
+        return [fn(j) for j in jobs[::-1]][::-1]
+
+    assert np.array_equal(O.moe64(x, ids, w, ex, E, map_fn=reversed_map), y)
+    for t in range(M):
+        want = np.zeros(H)
+        for s in range(k):
+            want += float(w[t, s]) * O.swiglu_mlp64(x[t:t + 1], *ex(int(ids[t, s])))[0]
+        assert np.allclose(y[t], want, rtol=0, atol=1e-13 * np.abs(want).max())
