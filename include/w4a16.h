@@ -106,43 +106,61 @@ W4A16_API w4a16_status_t w4a16_workspace_init(void* ws, size_t bytes, hipStream_
  * uses scale = max|w| / 7 per 32-row group and column (one IEEE float32
  * division) and code = clamp(round-half-even(w / scale), -8, 7) with the
  * quotient formed in float64; an all-zero group gets scale 0 and code 0.
- * Weights must be finite (not checked on the device).
- * Errors: INVALID_ARG for null/misaligned pointers or K, N, E < 0;
+ * Weights must be finite (not checked on the device).  qw_bytes and
+ * scales_bytes are the sizes of the caller's output buffers: at least
+ * E * K/8 * N * 4 and E * K/32 * N * 4 bytes.
+ * Errors: INVALID_ARG for null/misaligned pointers, K, N, E < 0 or an output
+ * buffer smaller than its size above (nothing is enqueued then);
  * UNSUPPORTED for K % 32 != 0.
  */
 W4A16_API w4a16_status_t w4a16_quantize(const float* w, int32_t K, int32_t N, int32_t num_experts,
-                              int32_t* qw, float* scales, hipStream_t stream);
+                              int32_t* qw, size_t qw_bytes, float* scales, size_t scales_bytes,
+                              hipStream_t stream);
 
 /*
  * w4a16_quantize with group_size rows per scale (32, 64 or 128): scales are
- * sc[E][K/group_size][N], scale = max|w| / 7 over each group, codes as above.
- * Errors as w4a16_quantize, plus UNSUPPORTED for another group size or
+ * sc[E][K/group_size][N] (scales_bytes >= E * K/group_size * N * 4),
+ * scale = max|w| / 7 over each group, codes as above.  Errors as
+ * w4a16_quantize, plus UNSUPPORTED for another group size or
  * K % group_size != 0.
  */
 W4A16_API w4a16_status_t w4a16_quantize_group(const float* w, int32_t K, int32_t N, int32_t num_experts,
-                                    int32_t group_size, int32_t* qw, float* scales, hipStream_t stream);
+                                    int32_t group_size, int32_t* qw, size_t qw_bytes, float* scales,
+                                    size_t scales_bytes, hipStream_t stream);
+
+/*
+ * Bytes of GROUPED codes that w4a16_prepack writes for the weight `w`
+ * (E * K/8 * N * 4: the GROUPED layout is a permutation of the canonical
+ * words, so the size does not change; gate and up stay separate weights).
+ * 0 for a descriptor that fails the checks of w4a16_prepack.
+ */
+W4A16_API size_t w4a16_prepacked_bytes(const w4a16_weight_t* w);
 
 /*
  * Permute CANONICAL codes into the GROUPED layout the compute kernels stream
  * (one-time load step; the weight and scale maps of page "The Final Wire",
  * section "The Multi-Step Integration Chain").  Scales are not moved: `out`
  * receives a GROUPED descriptor that points at `dst_qw` and at src->scales.
- * dst_qw must hold src->num_experts * K * N / 8 int32 and must not overlap
- * src->qw.  Errors: INVALID_ARG (null/misaligned, out == NULL, overlap),
- * UNSUPPORTED (src not CANONICAL, group size, K % group size, N % 64).
+ * dst_qw (dst_bytes bytes) must hold w4a16_prepacked_bytes(src) bytes and
+ * must not overlap src->qw.  Errors: INVALID_ARG (null/misaligned, out ==
+ * NULL, overlap, dst_bytes too small; nothing is enqueued then), UNSUPPORTED
+ * (src not CANONICAL, group size, K % group size, N % 64).
  */
-W4A16_API w4a16_status_t w4a16_prepack(const w4a16_weight_t* src, int32_t* dst_qw, w4a16_weight_t* out,
-                             hipStream_t stream);
+W4A16_API w4a16_status_t w4a16_prepack(const w4a16_weight_t* src, int32_t* dst_qw, size_t dst_bytes,
+                             w4a16_weight_t* out, hipStream_t stream);
 
 /*
  * Test hook, not on the hot path: materialise out[E][K][N] = float32(q * s),
  * the exact product rounded once (page "The First Line of Code: Implementing
  * W4A16 Quantization in a Native Speculative Decoding Engine", section "What
  * the Edit Actually Does": dequantization must be identical to the
- * reference's).  Accepts both layouts.  Same errors as w4a16_prepack, without
- * the layout restriction.
+ * reference's).  Accepts both layouts.  out_bytes is the size of `out`, at
+ * least E * K * N * 4.  Errors: INVALID_ARG (null/misaligned, out_bytes too
+ * small; nothing is enqueued then), UNSUPPORTED (group size, K % group size,
+ * N % 64, layout).
  */
-W4A16_API w4a16_status_t w4a16_dequantize(const w4a16_weight_t* w, float* out, hipStream_t stream);
+W4A16_API w4a16_status_t w4a16_dequantize(const w4a16_weight_t* w, float* out, size_t out_bytes,
+                                hipStream_t stream);
 
 /* Bytes of workspace w4a16_gemm needs for this M, weight and activation type. */
 W4A16_API size_t w4a16_gemm_workspace_bytes(int32_t M, const w4a16_weight_t* w, w4a16_dtype_t xt);
@@ -174,9 +192,10 @@ W4A16_API size_t w4a16_swiglu_mlp_workspace_bytes(int32_t M, w4a16_dtype_t xt, c
  * SwiGLU).  gate and up are [H -> I], down is [I -> H], all dense GROUPED.
  * x is [M][H], y is [M][H] float32.  The gate and up projections run in one
  * pass with the SiLU-times-up product formed in the epilogue; the
- * intermediate h[M][I] lives in the workspace, float32 for float32 x and bf16
- * for bf16 x.  Errors as w4a16_gemm, plus UNSUPPORTED if the three shapes do
- * not chain.
+ * intermediate h[M][I] lives in the workspace in float32 for both activation
+ * types (the down projection then stages it as f16 pieces, two for float32
+ * x and one for bf16 x).  Errors as w4a16_gemm, plus UNSUPPORTED if the three
+ * shapes do not chain.
  */
 W4A16_API w4a16_status_t w4a16_swiglu_mlp(const void* x, w4a16_dtype_t xt, int32_t M,
                                 const w4a16_weight_t* gate, const w4a16_weight_t* up,

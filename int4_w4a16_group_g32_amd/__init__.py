@@ -27,6 +27,7 @@ EXPORTS = (
     "w4a16_workspace_init",
     "w4a16_quantize",
     "w4a16_quantize_group",
+    "w4a16_prepacked_bytes",
     "w4a16_prepack",
     "w4a16_dequantize",
     "w4a16_gemm_workspace_bytes",
@@ -77,10 +78,11 @@ def load_library() -> ctypes.CDLL:
         sig = {
             "w4a16_status_string": (ctypes.c_char_p, [i32]),
             "w4a16_workspace_init": (i32, [vp, sz, vp]),
-            "w4a16_quantize": (i32, [vp, i32, i32, i32, vp, vp, vp]),
-            "w4a16_quantize_group": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
-            "w4a16_prepack": (i32, [dp, vp, dp, vp]),
-            "w4a16_dequantize": (i32, [dp, vp, vp]),
+            "w4a16_quantize": (i32, [vp, i32, i32, i32, vp, sz, vp, sz, vp]),
+            "w4a16_quantize_group": (i32, [vp, i32, i32, i32, i32, vp, sz, vp, sz, vp]),
+            "w4a16_prepacked_bytes": (sz, [dp]),
+            "w4a16_prepack": (i32, [dp, vp, sz, dp, vp]),
+            "w4a16_dequantize": (i32, [dp, vp, sz, vp]),
             "w4a16_gemm_workspace_bytes": (sz, [i32, dp, i32]),
             "w4a16_gemm": (i32, [vp, i32, i32, dp, vp, vp, sz, vp]),
             "w4a16_swiglu_mlp_workspace_bytes": (sz, [i32, i32, dp, dp, dp]),
@@ -132,6 +134,36 @@ def _dtype_code(x: torch.Tensor) -> int:
     raise TypeError(f"activations must be float32 or bfloat16, got {x.dtype}")
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    """Check a tensor handed to the library: dtype, contiguity and shape."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _on_device(**tensors):
+    """Every tensor the library reads or writes must be device memory."""
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor, got {t.device}")
+
+
+def _need_x(x: torch.Tensor, K: int):
+    _dtype_code(x)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"activations must be [M][{K}], got {tuple(x.shape)}")
+    _need(x, "x", x.dtype)
+
+
 @dataclass
 class Weight:
     """A W4A16 weight (or expert stack): codes, scales and their shape."""
@@ -161,25 +193,39 @@ def workspace_init(ws: torch.Tensor, stream=None):
 
 def quantize(w: torch.Tensor, qw: torch.Tensor, scales: torch.Tensor, stream=None, group_size: int = GROUP):
     """w float32 [E][K][N] (or [K][N]) -> CANONICAL qw, scales [E][K/group_size][N] (caller-allocated)."""
+    _need(w, "w", torch.float32)
+    _need(qw, "qw", torch.int32)
+    _need(scales, "scales", torch.float32)
+    _on_device(w=w, qw=qw, scales=scales)
     E = 1 if w.dim() == 2 else w.shape[0]
     K, N = w.shape[-2], w.shape[-1]
     if group_size == GROUP:
-        st = load_library().w4a16_quantize(_ptr(w), K, N, E, _ptr(qw), _ptr(scales), _stream(stream))
+        st = load_library().w4a16_quantize(_ptr(w), K, N, E, _ptr(qw), _nbytes(qw), _ptr(scales), _nbytes(scales),
+                                           _stream(stream))
     else:
-        st = load_library().w4a16_quantize_group(_ptr(w), K, N, E, group_size, _ptr(qw), _ptr(scales),
-                                                 _stream(stream))
+        st = load_library().w4a16_quantize_group(_ptr(w), K, N, E, group_size, _ptr(qw), _nbytes(qw),
+                                                 _ptr(scales), _nbytes(scales), _stream(stream))
     _check(st, "w4a16_quantize")
 
 
+def prepacked_bytes(src: Weight) -> int:
+    """Bytes of GROUPED codes w4a16_prepack writes for `src` (0 for an unsupported descriptor)."""
+    return load_library().w4a16_prepacked_bytes(_dref(src))
+
+
 def prepack(src: Weight, dst_qw: torch.Tensor, stream=None) -> Weight:
+    _need(dst_qw, "dst_qw", torch.int32)
+    _on_device(dst_qw=dst_qw, qw=src.qw, scales=src.scales)
     out = WeightDesc()
-    _check(load_library().w4a16_prepack(_dref(src), _ptr(dst_qw), ctypes.byref(out), _stream(stream)),
-           "w4a16_prepack")
+    _check(load_library().w4a16_prepack(_dref(src), _ptr(dst_qw), _nbytes(dst_qw), ctypes.byref(out),
+                                        _stream(stream)), "w4a16_prepack")
     return Weight(dst_qw, src.scales, out.K, out.N, out.num_experts, out.layout, out.group_size)
 
 
 def dequantize(w: Weight, out: torch.Tensor, stream=None):
-    _check(load_library().w4a16_dequantize(_dref(w), _ptr(out), _stream(stream)), "w4a16_dequantize")
+    _need(out, "out", torch.float32)
+    _on_device(out=out, qw=w.qw, scales=w.scales)
+    _check(load_library().w4a16_dequantize(_dref(w), _ptr(out), _nbytes(out), _stream(stream)), "w4a16_dequantize")
 
 
 # ---------------------------------------------------------------- compute
@@ -189,6 +235,10 @@ def gemm_workspace_bytes(M: int, w: Weight, xt: int) -> int:
 
 
 def gemm(x: torch.Tensor, w: Weight, y: torch.Tensor, ws: torch.Tensor, stream=None):
+    _need_x(x, w.K)
+    _need(y, "y", torch.float32, (x.shape[0], w.N))
+    _need(ws, "ws", torch.uint8)
+    _on_device(x=x, y=y, ws=ws)
     _check(load_library().w4a16_gemm(_ptr(x), _dtype_code(x), x.shape[0], _dref(w), _ptr(y), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)), "w4a16_gemm")
 
@@ -199,6 +249,10 @@ def swiglu_mlp_workspace_bytes(M: int, xt: int, gate: Weight, up: Weight, down: 
 
 def swiglu_mlp(x: torch.Tensor, gate: Weight, up: Weight, down: Weight, y: torch.Tensor,
                ws: torch.Tensor, stream=None):
+    _need_x(x, gate.K)
+    _need(y, "y", torch.float32, (x.shape[0], down.N))
+    _need(ws, "ws", torch.uint8)
+    _on_device(x=x, y=y, ws=ws)
     _check(load_library().w4a16_swiglu_mlp(_ptr(x), _dtype_code(x), x.shape[0], _dref(gate), _dref(up),
                                            _dref(down), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                            _stream(stream)), "w4a16_swiglu_mlp")
@@ -206,13 +260,25 @@ def swiglu_mlp(x: torch.Tensor, gate: Weight, up: Weight, down: Weight, y: torch
 
 def moe_topk(logits: torch.Tensor, top_k: int, topk_ids: torch.Tensor, topk_w: torch.Tensor, stream=None):
     """Top-k experts per token row of float32 logits [M][E] and their softmax gate weights."""
+    _need(logits, "logits", torch.float32)
     M, E = logits.shape
+    _need(topk_ids, "topk_ids", torch.int32, (M, top_k))
+    _need(topk_w, "topk_w", torch.float32, (M, top_k))
+    _on_device(logits=logits, topk_ids=topk_ids, topk_w=topk_w)
     _check(load_library().w4a16_moe_topk(_ptr(logits), M, E, top_k, _ptr(topk_ids), _ptr(topk_w),
                                          _stream(stream)), "w4a16_moe_topk")
 
 
 def moe_route(topk_ids: torch.Tensor, num_experts: int, counts, offsets, sorted_pairs, inv, stream=None):
+    _need(topk_ids, "topk_ids", torch.int32)
     M, k = topk_ids.shape
+    _need(counts, "counts", torch.int32, (num_experts,))
+    _need(offsets, "offsets", torch.int32, (num_experts + 1,))
+    for t, name in ((sorted_pairs, "sorted_pairs"), (inv, "inv")):
+        _need(t, name, torch.int32)
+        if t.numel() < M * k:
+            raise ValueError(f"{name} must hold at least {M * k} entries")
+    _on_device(topk_ids=topk_ids, counts=counts, offsets=offsets, sorted_pairs=sorted_pairs, inv=inv)
     _check(load_library().w4a16_moe_route(_ptr(topk_ids), M, k, num_experts, _ptr(counts), _ptr(offsets),
                                           _ptr(sorted_pairs), _ptr(inv), _stream(stream)), "w4a16_moe_route")
 
@@ -228,10 +294,27 @@ def moe_shared_workspace_bytes(M: int, top_k: int, xt: int, gate: Weight, up: We
                                                            _dref(shared_down))
 
 
+def _check_moe_args(x, topk_ids, topk_w, gate: Weight, down: Weight, y, ws):
+    """topk_ids int32 [M][k] (torch.topk's int64 ids must be converted), topk_w
+    float32 [M][k], x [M][H], y float32 [M][H]; returns (M, k)."""
+    _need(topk_ids, "topk_ids", torch.int32)
+    if topk_ids.dim() != 2:
+        raise ValueError(f"topk_ids must be [M][top_k], got {tuple(topk_ids.shape)}")
+    M, k = topk_ids.shape
+    _need(topk_w, "topk_w", torch.float32, (M, k))
+    _need_x(x, gate.K)
+    if x.shape[0] != M:
+        raise ValueError(f"x has {x.shape[0]} rows, topk_ids {M}")
+    _need(y, "y", torch.float32, (M, down.N))
+    _need(ws, "ws", torch.uint8)
+    _on_device(x=x, topk_ids=topk_ids, topk_w=topk_w, y=y, ws=ws)
+    return M, k
+
+
 def moe_grouped_shared(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate: Weight, up: Weight,
                        down: Weight, shared_gate: Weight, shared_up: Weight, shared_down: Weight, y: torch.Tensor,
                        ws: torch.Tensor, stream=None):
-    M, k = topk_ids.shape
+    M, k = _check_moe_args(x, topk_ids, topk_w, gate, down, y, ws)
     _check(load_library().w4a16_moe_grouped_shared(_ptr(x), _dtype_code(x), M, _ptr(topk_ids), _ptr(topk_w), k,
                                                    _dref(gate), _dref(up), _dref(down), _dref(shared_gate),
                                                    _dref(shared_up), _dref(shared_down), _ptr(y), _ptr(ws),
@@ -241,7 +324,7 @@ def moe_grouped_shared(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Te
 
 def moe_grouped(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor, gate: Weight, up: Weight,
                 down: Weight, y: torch.Tensor, ws: torch.Tensor, stream=None):
-    M, k = topk_ids.shape
+    M, k = _check_moe_args(x, topk_ids, topk_w, gate, down, y, ws)
     _check(load_library().w4a16_moe_grouped(_ptr(x), _dtype_code(x), M, _ptr(topk_ids), _ptr(topk_w), k,
                                             _dref(gate), _dref(up), _dref(down), _ptr(y), _ptr(ws),
                                             ws.numel() * ws.element_size(), _stream(stream)),

@@ -320,7 +320,6 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
     if (st != W4A16_OK) return st;
     MfmaArgs a = mfma_dense_args(p.gu, M, gate, up, 1, apx, rsx, wsb, p.partials_off, p.counters_off);
     a.h = h;
-    a.h_bf16 = 0;
     b = ev.bracket();
     st = launch_mfma(a, p.gu.P, p.gu.tasks * p.gu.S, stream, b.start, b.stop);
     if (st != W4A16_OK) return st;

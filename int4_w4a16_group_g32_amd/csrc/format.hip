@@ -140,31 +140,42 @@ extern "C" w4a16_status_t w4a16_workspace_init(void* ws, size_t bytes, hipStream
 }
 
 extern "C" w4a16_status_t w4a16_quantize_group(const float* w, int32_t K, int32_t N, int32_t E,
-                                               int32_t group_size, int32_t* qw, float* scales,
-                                               hipStream_t stream) {
+                                               int32_t group_size, int32_t* qw, size_t qw_bytes,
+                                               float* scales, size_t scales_bytes, hipStream_t stream) {
   if (w == nullptr || qw == nullptr || scales == nullptr) return W4A16_ERR_INVALID_ARG;
   if (!aligned16(w) || !aligned16(qw) || !aligned16(scales)) return W4A16_ERR_INVALID_ARG;
   if (K < 0 || N < 0 || E < 0) return W4A16_ERR_INVALID_ARG;
   if (group_size != 32 && group_size != 64 && group_size != 128) return W4A16_ERR_UNSUPPORTED;
   if (K % group_size != 0) return W4A16_ERR_UNSUPPORTED;
   const size_t total = static_cast<size_t>(E) * (K / group_size) * N;
+  // the outputs: E * K/8 * N code words and E * K/group_size * N scales
+  if (qw_bytes < static_cast<size_t>(E) * (K / 8) * N * 4 || scales_bytes < total * 4)
+    return W4A16_ERR_INVALID_ARG;
   if (total == 0) return W4A16_OK;
   quantize_kernel<<<grid_for(total, 256), 256, 0, stream>>>(w, K, N, E, group_size, qw, scales);
   return launch_status();
 }
 
 extern "C" w4a16_status_t w4a16_quantize(const float* w, int32_t K, int32_t N, int32_t E,
-                                         int32_t* qw, float* scales, hipStream_t stream) {
-  return w4a16_quantize_group(w, K, N, E, 32, qw, scales, stream);
+                                         int32_t* qw, size_t qw_bytes, float* scales, size_t scales_bytes,
+                                         hipStream_t stream) {
+  return w4a16_quantize_group(w, K, N, E, 32, qw, qw_bytes, scales, scales_bytes, stream);
 }
 
-extern "C" w4a16_status_t w4a16_prepack(const w4a16_weight_t* src, int32_t* dst_qw,
+extern "C" size_t w4a16_prepacked_bytes(const w4a16_weight_t* w) {
+  if (check_weight(w) != W4A16_OK) return 0;
+  // the GROUPED layout is a permutation of the canonical words: same size
+  return static_cast<size_t>(w->num_experts) * (w->K / 8) * w->N * 4;
+}
+
+extern "C" w4a16_status_t w4a16_prepack(const w4a16_weight_t* src, int32_t* dst_qw, size_t dst_bytes,
                                         w4a16_weight_t* out, hipStream_t stream) {
   w4a16_status_t st = check_weight(src);
   if (st != W4A16_OK) return st;
   if (dst_qw == nullptr || out == nullptr || !aligned16(dst_qw)) return W4A16_ERR_INVALID_ARG;
   if (src->layout != W4A16_LAYOUT_CANONICAL) return W4A16_ERR_UNSUPPORTED;
   const size_t words = static_cast<size_t>(src->num_experts) * (src->K / 8) * src->N;
+  if (dst_bytes < words * 4) return W4A16_ERR_INVALID_ARG;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(src->qw), a1 = a0 + words * 4;
   const uintptr_t b0 = reinterpret_cast<uintptr_t>(dst_qw), b1 = b0 + words * 4;
   if (words != 0 && a0 < b1 && b0 < a1) return W4A16_ERR_INVALID_ARG;
@@ -178,11 +189,12 @@ extern "C" w4a16_status_t w4a16_prepack(const w4a16_weight_t* src, int32_t* dst_
   return launch_status();
 }
 
-extern "C" w4a16_status_t w4a16_dequantize(const w4a16_weight_t* w, float* out,
+extern "C" w4a16_status_t w4a16_dequantize(const w4a16_weight_t* w, float* out, size_t out_bytes,
                                            hipStream_t stream) {
   w4a16_status_t st = check_weight(w);
   if (st != W4A16_OK) return st;
   if (out == nullptr || !aligned16(out)) return W4A16_ERR_INVALID_ARG;
+  if (out_bytes < static_cast<size_t>(w->num_experts) * w->K * w->N * 4) return W4A16_ERR_INVALID_ARG;
   const size_t total = static_cast<size_t>(w->num_experts) * (w->K / 8) * w->N;
   if (total == 0) return W4A16_OK;
   dequantize_kernel<<<grid_for(total, 256), 256, 0, stream>>>(

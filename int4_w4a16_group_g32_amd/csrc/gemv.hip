@@ -433,9 +433,11 @@ void gemv_kernel(const GemvArgs a) {
   bool mine = ttile_ok;
   if (a.S > 1) {
     // Partials are written through to the device coherence point (agent-scope
-    // stores), the arrival counter is an agent-scope atomic, and the last
-    // workgroup of the tile reads the partials back with agent-scope loads,
-    // many in flight at once, and sums them in split order.
+    // stores), the arrival counter is an agent-scope acquire-release atomic
+    // (it publishes this workgroup's partials and, for the last arriver,
+    // makes every other split's partials visible), and the last workgroup of
+    // the tile reads the partials back with agent-scope loads, many in flight
+    // at once, and sums them in split order.
     const size_t ct = static_cast<size_t>(item) * a.tiles + (ttile_ok ? ttile : 0);
     const size_t tf = kPartialTileFloats;
     float* base = a.partials + ct * a.S * tf;
@@ -446,10 +448,9 @@ void gemv_kernel(const GemvArgs a) {
           __hip_atomic_store(base + split * tf + r * kGemvCols + t, v[r], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t == 0) {
-      last[tq] = ttile_ok ? (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED,
+      last[tq] = ttile_ok ? (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_ACQ_REL,
                                                     __HIP_MEMORY_SCOPE_AGENT) == a.S - 1)
                           : 0;
     }

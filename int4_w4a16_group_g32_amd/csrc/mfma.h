@@ -69,8 +69,7 @@ struct MfmaArgs {
   const int* n_items;
   int mode;              // 0: plain float32 out[pos][N]; 1: SwiGLU, h[pos][N]
   float* out;
-  void* h;
-  int h_bf16;
+  float* h;              // SwiGLU output h[pos][N], float32
   float* partials;
   int* counters;
 };

@@ -505,10 +505,9 @@ void mfma_kernel(const MfmaArgs a) {
         for (int i = 0; i < 4; ++i)
           __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kMfmaThreads, acc[rb][cb][i],
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0)
-      last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
               a.S - 1);
     __syncthreads();
     if (!last) return;
@@ -563,12 +562,7 @@ void mfma_kernel(const MfmaArgs a) {
         for (int cb = 0; cb < 4; ++cb) {
           const float up = __shfl_xor(acc[rb][cb][i], 8);  // every lane takes part
           if (live && lc < 8) {
-            const float h = silu(acc[rb][cb][i] * f) * (up * f);
-            const size_t hi = prow * a.N + col0 + cb;
-            if (a.h_bf16)
-              static_cast<uint16_t*>(a.h)[hi] = f32_to_bf16(h);
-            else
-              static_cast<float*>(a.h)[hi] = h;
+            a.h[prow * a.N + col0 + cb] = silu(acc[rb][cb][i] * f) * (up * f);
           }
         }
       }

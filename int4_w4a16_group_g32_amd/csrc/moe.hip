@@ -6,6 +6,8 @@
 // the router selects top-k experts per token and each selected expert runs its
 // own gate, up and down projections through the W4A16 path.  Per-expert row
 // counts are produced and consumed on the device only.
+#include <climits>
+
 #include "dispatch.h"
 
 namespace w4 {
@@ -299,6 +301,7 @@ struct MoePlan {
   size_t h_off, o_off;
   size_t apx_off, rsx_off, aph_off, rsh_off;
   bool mfma = false;  // some expert can have more than gemv_expert_rows(xt) rows
+  int expert_rows = 0;  // experts above this many rows run on MFMA items
   size_t bytes = 0;
 };
 
@@ -308,10 +311,18 @@ MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate,
   const int E = gate->num_experts, H = gate->K, I = gate->N;
   p.pairs = static_cast<size_t>(M) * top_k;
   p.positions = p.pairs + (shared ? static_cast<size_t>(M) : 0);
-  // GEMV items of the light experts
-  const int per_expert = (gemv_expert_rows(xt) + gemv_rows(xt) - 1) / gemv_rows(xt);
-  p.max_items = std::min<size_t>(E, p.pairs) * per_expert + 1;
-  p.mfma = M > gemv_expert_rows(xt);  // an expert gets at most M rows
+  // An expert gets at most M rows while a token's ids are distinct.  Without
+  // an MFMA launch every expert is cut into GEMV items, so that ids repeated
+  // within a token (more rows than M for one expert) still have their items.
+  p.mfma = M > gemv_expert_rows(xt);
+  p.expert_rows = p.mfma ? gemv_expert_rows(xt) : INT_MAX;
+  if (p.mfma) {
+    // light experts: at most gemv_expert_rows rows, in items of gemv_rows rows
+    const int per_expert = (gemv_expert_rows(xt) + gemv_rows(xt) - 1) / gemv_rows(xt);
+    p.max_items = std::min<size_t>(E, p.pairs) * per_expert + 1;
+  } else {
+    p.max_items = p.pairs / gemv_rows(xt) + std::min<size_t>(E, p.pairs) + 1;
+  }
   p.max_mitems =
       p.mfma ? p.pairs / kMfmaRows + std::min<size_t>(E, p.pairs / (gemv_expert_rows(xt) + 1)) + 1 : 0;
   if (shared) {  // the shared expert is one more expert with M rows
@@ -454,7 +465,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   // 1. expert grouping and work items
   if ((st = ev.mark(stream)) != W4A16_OK) return st;
   st = launch_route(topk_ids, M, top_k, E, counts, offsets, sorted, inv, items, mitems, n_items,
-                    heavy, shared ? M : 0, gemv_rows(xt), gemv_expert_rows(xt), stream);
+                    heavy, shared ? M : 0, gemv_rows(xt), p.expert_rows, stream);
   if (st != W4A16_OK) return st;
 
   // 2. gate/up with the SwiGLU epilogue: light experts on the GEMV, heavy on MFMA tiles
@@ -525,7 +536,6 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     ma.n_items = n_items + 1;
     ma.mode = 1;
     ma.h = hraw;
-    ma.h_bf16 = 0;
     ma.extra_plus1 = a.extra_plus1;
     ma.qw0x = a.qw0x;
     ma.sc0x = a.sc0x;

@@ -348,10 +348,9 @@ void wide_kernel(const MfmaArgs a) {
         for (int i = 0; i < 4; ++i)
           __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kWideThreads, acc[rb][cb][i],
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t == 0)
-      lds.last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      lds.last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
                   a.S - 1);
     __syncthreads();
     if (!lds.last) return;

@@ -137,14 +137,43 @@ def test_topk_argument_checks(lib):
 
 
 def test_quantize_and_prepack_checks(lib):
-    assert lib.w4a16_quantize(ctypes.c_void_p(0x1000), 48, 64, 1, ctypes.c_void_p(0x2000),
-                              ctypes.c_void_p(0x3000), None) == L.ERR_UNSUPPORTED
-    assert lib.w4a16_quantize(None, 64, 64, 1, ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000),
+    big = 1 << 30
+    assert lib.w4a16_quantize(ctypes.c_void_p(0x1000), 48, 64, 1, ctypes.c_void_p(0x2000), big,
+                              ctypes.c_void_p(0x3000), big, None) == L.ERR_UNSUPPORTED
+    assert lib.w4a16_quantize(None, 64, 64, 1, ctypes.c_void_p(0x2000), big, ctypes.c_void_p(0x3000), big,
                               None) == L.ERR_INVALID_ARG
     src = _desc(layout=L.LAYOUT_GROUPED)
     out = L.WeightDesc()
-    assert lib.w4a16_prepack(ctypes.byref(src), ctypes.c_void_p(0x8000), ctypes.byref(out),
+    assert lib.w4a16_prepack(ctypes.byref(src), ctypes.c_void_p(0x8000), big, ctypes.byref(out),
                              None) == L.ERR_UNSUPPORTED
     src = _desc(layout=L.LAYOUT_CANONICAL, qw=0x1000)
-    assert lib.w4a16_prepack(ctypes.byref(src), ctypes.c_void_p(0x1100), ctypes.byref(out),
+    assert lib.w4a16_prepack(ctypes.byref(src), ctypes.c_void_p(0x1100), big, ctypes.byref(out),
                              None) == L.ERR_INVALID_ARG  # overlapping destination
+
+
+def test_output_sizes_are_checked_before_launch(lib):
+    """Every format entry point takes the size of its output buffer and returns
+    INVALID_ARG, with nothing enqueued (these pointers are not device memory),
+    when the buffer is one byte short."""
+    K, N, E = 256, 128, 3
+    qw_bytes, sc_bytes = E * K // 8 * N * 4, E * K // 32 * N * 4
+    q = lambda qb, sb: lib.w4a16_quantize(ctypes.c_void_p(0x1000), K, N, E, ctypes.c_void_p(0x2000), qb,
+                                          ctypes.c_void_p(0x3000), sb, None)
+    assert q(qw_bytes - 1, sc_bytes) == L.ERR_INVALID_ARG
+    assert q(qw_bytes, sc_bytes - 1) == L.ERR_INVALID_ARG
+    sc64 = E * K // 64 * N * 4
+    qg = lambda sb: lib.w4a16_quantize_group(ctypes.c_void_p(0x1000), K, N, E, 64, ctypes.c_void_p(0x2000),
+                                             qw_bytes, ctypes.c_void_p(0x3000), sb, None)
+    assert qg(sc64 - 1) == L.ERR_INVALID_ARG
+    src = _desc(K=K, N=N, E=E, layout=L.LAYOUT_CANONICAL, qw=0x10000)
+    assert lib.w4a16_prepacked_bytes(ctypes.byref(src)) == qw_bytes
+    out = L.WeightDesc()
+    assert lib.w4a16_prepack(ctypes.byref(src), ctypes.c_void_p(0x100000), qw_bytes - 1, ctypes.byref(out),
+                             None) == L.ERR_INVALID_ARG
+    deq_bytes = E * K * N * 4
+    assert lib.w4a16_dequantize(ctypes.byref(src), ctypes.c_void_p(0x100000), deq_bytes - 1,
+                                None) == L.ERR_INVALID_ARG
+    # the query rejects what prepack rejects
+    assert lib.w4a16_prepacked_bytes(ctypes.byref(_desc(group=96))) == 0
+    assert lib.w4a16_prepacked_bytes(ctypes.byref(_desc(N=96))) == 0
+    assert lib.w4a16_prepacked_bytes(None) == 0
