@@ -489,7 +489,8 @@ void mfma_kernel(const MfmaArgs a) {
 
   // Split-K: write-through partials, an agent-scope arrival counter, and the
   // last workgroup sums the partials in split order (the GEMV kernel's
-  // scheme).  A partial tile is stored element-major, [j][thread] with
+  // scheme, with the same reliance on gfx950's write-through agent-scope
+  // atomics in place of release/acquire ordering).  A partial tile is stored element-major, [j][thread] with
   // j = (rb * 4 + cb) * 4 + i, so every store and load instruction covers 256
   // contiguous bytes, and the readback keeps two splits' worth (128 loads per
   // thread) in flight at a time.
@@ -505,9 +506,10 @@ void mfma_kernel(const MfmaArgs a) {
         for (int i = 0; i < 4; ++i)
           __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kMfmaThreads, acc[rb][cb][i],
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
     __syncthreads();
     if (threadIdx.x == 0)
-      last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+      last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               a.S - 1);
     __syncthreads();
     if (!last) return;

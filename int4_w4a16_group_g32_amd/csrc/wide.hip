@@ -335,7 +335,8 @@ void wide_kernel(const MfmaArgs a) {
 
   // Split-K: write-through partials [j][thread], j = (rb * 4 + cb) * 4 + i, an
   // agent-scope arrival counter, and the last workgroup sums the partials in
-  // split order, 64 loads per thread in flight.
+  // split order, 64 loads per thread in flight (the GEMV kernel's scheme and
+  // its reliance on gfx950's write-through agent-scope atomics).
   if (a.S > 1) {
     const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
     const size_t tf = static_cast<size_t>(kWideRows) * kWideCols;
@@ -348,9 +349,10 @@ void wide_kernel(const MfmaArgs a) {
         for (int i = 0; i < 4; ++i)
           __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kWideThreads, acc[rb][cb][i],
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
     __syncthreads();
     if (t == 0)
-      lds.last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+      lds.last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                   a.S - 1);
     __syncthreads();
     if (!lds.last) return;

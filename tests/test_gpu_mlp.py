@@ -10,6 +10,7 @@ import int4_w4a16_group_g32_amd as L
 import oracle as O
 import workloads as W
 from helpers import canonical_words, rel_err, tol_for, weight_from_codes, x_for_dtype, x_values
+from oracle_pool import TAU, check_elementwise, mlp_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +37,32 @@ def test_mlp_small(M, H, I, dtype):
     y = _mlp_gpu(x, g, u, d)
     ref = O.swiglu_mlp64(x_values(x), *codes)
     err = rel_err(y, ref)
-    print(f"mlp M={M} H={H} I={I} {dtype} relF={err:.3e}", flush=True)
+    worst = check_elementwise(y.cpu().numpy(), ref, mlp_bound(x_values(x), *codes, TAU[dtype]),
+                              f"mlp M={M} H={H} I={I} {dtype}")
+    print(f"mlp M={M} H={H} I={I} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
+    assert err <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [4, 16, 64])
+def test_mlp_random_codes_include_nibble_zero(M, dtype):
+    """Code words with every bit uniform, so q = -8 reaches the gate/up and
+    down kernels of the GEMV (M = 4; 16 with bf16) and the tiles (M = 16
+    with float32, 64)."""
+    H, I, cfg = 1024, 2048, 610 + M
+    rng = np.random.default_rng(cfg)
+    codes = []
+    for K, N in ((H, I), (H, I), (I, H)):
+        qw = rng.integers(0, 2 ** 32, size=(K // 8, N), dtype=np.uint64).astype(np.uint32).view(np.int32)
+        codes.append((qw, (rng.random((K // 32, N)) * 0.005 + 0.004).astype(np.float32)))
+    g, u, d = (weight_from_codes(*c) for c in codes)
+    x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
+    y = _mlp_gpu(x, g, u, d)
+    ref = O.swiglu_mlp64(x_values(x), *codes)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, mlp_bound(x_values(x), *codes, TAU[dtype]),
+                              f"mlp random codes M={M} {dtype}")
+    print(f"mlp random codes M={M} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
     assert err <= tol_for(dtype)
 
 
@@ -72,11 +98,14 @@ def test_mlp_full_size(dense_mlp, name, dtype):
     y = _mlp_gpu(x, g, u, d)
     cols = np.sort(np.random.default_rng(cfg.M).choice(H, size=512, replace=False))
     xv = x_values(x)
-    h = O.silu64(O.gemm64(xv, *gq)) * O.gemm64(xv, *uq)
-    ref = h @ O.dequant64(*_sampled_down(w_down, cols))
-    err = rel_err(y[:, torch.as_tensor(cols, device="cuda")], ref)
-    print(f"{name} relF={err:.3e} (512 sampled columns)", flush=True)
+    dq = _sampled_down(w_down, cols)
+    ref = O.swiglu_mlp64(xv, gq, uq, dq)
+    ys = y[:, torch.as_tensor(cols, device="cuda")]
+    err = rel_err(ys, ref)
+    worst = check_elementwise(ys.cpu().numpy(), ref, mlp_bound(xv, gq, uq, dq, TAU[dtype]), name)
+    print(f"{name} relF={err:.3e} worst/bound={worst:.2e} (512 sampled columns)", flush=True)
     assert err <= tol_for(dtype)
+    assert torch.isfinite(y).all()
     # the library's quantization of the same weights agrees with the oracle's
     qd = canonical_words(d.qw.cpu().numpy(), I, H)[0][:, cols]
     assert np.array_equal(qd, _sampled_down(w_down, cols)[0])

@@ -1,5 +1,6 @@
 """GPU parity of expert routing (bit-exact) and of the routed MoE layer
-(relative Frobenius error vs the oracle's float64 MoE)."""
+against the oracle's float64 MoE: relative Frobenius error and a bound on
+every output element (tests/oracle_pool.py)."""
 import numpy as np
 import pytest
 import torch
@@ -8,6 +9,7 @@ import int4_w4a16_group_g32_amd as L
 import oracle as O
 import workloads as W
 from helpers import oracle_quantize_stack, rel_err, to_dev, tol_for, weight_from_codes, x_for_dtype, x_values
+from oracle_pool import TAU, ExpertPool, check_elementwise, moe_bound_from
 
 pytestmark = pytest.mark.gpu
 
@@ -85,9 +87,72 @@ def test_moe_small(M, E, k, H, I, routing, dtype):
     wts = W.gate_weights(M, k, cfg)
     x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
     y = _moe_gpu(x, to_dev(ids), to_dev(wts), g, u, d)
-    ref = O.moe64(x_values(x), ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E)
+    ref, bound = _moe_ref(x, ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E, dtype)
     err = rel_err(y, ref)
-    print(f"moe M={M} E={E} k={k} H={H} I={I} {dtype} relF={err:.3e}", flush=True)
+    worst = check_elementwise(y.cpu().numpy(), ref, bound, f"moe M={M} E={E} k={k} {dtype}")
+    print(f"moe M={M} E={E} k={k} H={H} I={I} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
+    assert err <= tol_for(dtype)
+
+
+def _moe_ref(x, ids, wts, expert, E, dtype, tokens=None, workers=0):
+    """The oracle's MoE output and the per-element bound for it."""
+    with ExpertPool(TAU[dtype], workers=workers) as pool:
+        ref = O.moe64(x_values(x), ids, wts, expert, E, tokens=tokens, map_fn=pool)
+        bound = moe_bound_from(pool.bounds, ids, wts, tokens)
+    return ref, bound
+
+
+def _random_expert_codes(E, H, I, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for K, N in ((H, I), (H, I), (I, H)):
+        qw = rng.integers(0, 2 ** 32, size=(E, K // 8, N), dtype=np.uint64).astype(np.uint32).view(np.int32)
+        out.append((qw, (rng.random((E, K // 32, N)) * 0.005 + 0.004).astype(np.float32)))
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,E,k,H,I", [(5, 8, 3, 128, 64), (24, 16, 8, 128, 128), (200, 4, 2, 128, 256)])
+def test_moe_random_codes_include_nibble_zero(M, E, k, H, I, dtype):
+    """Code words with every bit uniform (q = -8 included) on the GEMV items,
+    the 64-row tiles and both together."""
+    cfg = 560 + M
+    (gq, gs), (uq, us), (dq, ds) = _random_expert_codes(E, H, I, cfg)
+    g, u, d = weight_from_codes(gq, gs), weight_from_codes(uq, us), weight_from_codes(dq, ds)
+    ids = W.topk_uniform(M, E, k, cfg)
+    wts = W.gate_weights(M, k, cfg)
+    x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
+    y = _moe_gpu(x, to_dev(ids), to_dev(wts), g, u, d)
+    ref, bound = _moe_ref(x, ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E, dtype)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, bound, f"moe random codes M={M} {dtype}")
+    print(f"moe random codes M={M} E={E} k={k} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
+    assert err <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [5, 20])
+def test_moe_repeated_ids_within_a_token(M, dtype):
+    """A token that names one expert in two or three of its slots gets that
+    expert's output once per slot.  At M = 5 the layer has no MFMA launch, yet
+    an expert can collect up to 15 rows (more than the GEMV's item size); at
+    M = 20 with float32 activations such experts take the tiles."""
+    E, k, H, I = 4, 3, 128, 64
+    cfg = 580 + M
+    (gq, gs), (uq, us), (dq, ds) = _experts(E, H, I, cfg)
+    g, u, d = weight_from_codes(gq, gs), weight_from_codes(uq, us), weight_from_codes(dq, ds)
+    rng = np.random.default_rng(cfg)
+    ids = rng.integers(0, E, size=(M, k)).astype(np.int32)
+    ids[:, 0] = ids[:, 1] = 2  # expert 2 twice in every token
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert counts.max() > 2 * M - 1
+    wts = W.gate_weights(M, k, cfg)
+    x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
+    y = _moe_gpu(x, to_dev(ids), to_dev(wts), g, u, d)
+    ref, bound = _moe_ref(x, ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E, dtype)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, bound, f"moe repeated ids M={M} {dtype}")
+    print(f"moe repeated ids M={M} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
     assert err <= tol_for(dtype)
 
 
@@ -105,9 +170,10 @@ def test_moe_all_heavy_bf16(M, E, k, H, I):
     wts = W.gate_weights(M, k, cfg)
     x = x_for_dtype(W.activations(M, H, cfg).cuda(), "bf16")
     y = _moe_gpu(x, to_dev(ids), to_dev(wts), g, u, d)
-    ref = O.moe64(x_values(x), ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E)
+    ref, bound = _moe_ref(x, ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E, "bf16")
     err = rel_err(y, ref)
-    print(f"moe all-heavy M={M} E={E} k={k} H={H} I={I} bf16 relF={err:.3e}", flush=True)
+    worst = check_elementwise(y.cpu().numpy(), ref, bound, f"moe all-heavy M={M}")
+    print(f"moe all-heavy M={M} E={E} k={k} H={H} I={I} bf16 relF={err:.3e} worst/bound={worst:.2e}", flush=True)
     assert err <= tol_for("bf16")
 
 
@@ -163,3 +229,67 @@ def test_moe_prefill_full_size():
     hot = int(np.argmax(counts))
     t_hot = int(np.argwhere((ids == hot).any(axis=1))[0, 0])
     _full_moe("moe_prefill_m2048", [t_hot, 2047])
+
+
+def _random_code_stacks(cfg, E, H, I):
+    """Expert stacks of random code words and scales drawn on the GPU
+    (workloads.code_words / scale_values), kept in both layouts: the GROUPED
+    copy for the library, the canonical one for the oracle's expert slices."""
+    canon, grouped = {}, {}
+    for tag, (K, N) in ((W.TAG_GATE, (H, I)), (W.TAG_UP, (H, I)), (W.TAG_DOWN, (I, H))):
+        qw = torch.empty((E, K // 8, N), dtype=torch.int32, device="cuda")
+        sc = torch.empty((E, K // 32, N), dtype=torch.float32, device="cuda")
+        for e in range(E):
+            qw[e] = W.code_words(K, N, cfg.index, tag, e, device="cuda")
+            sc[e] = W.scale_values(K // 32, N, cfg.index, tag, e, device="cuda")
+        canon[tag] = (qw, sc)
+        grouped[tag] = L.prepack(L.Weight(qw, sc, K, N, E, L.LAYOUT_CANONICAL), torch.empty_like(qw))
+    torch.cuda.synchronize()
+    tags = (W.TAG_GATE, W.TAG_UP, W.TAG_DOWN)
+
+    def expert(e):
+        return tuple((canon[t][0][e].cpu().numpy(), canon[t][1][e].cpu().numpy()) for t in tags)
+
+    return [grouped[t] for t in tags], expert
+
+
+def _full_moe_every_token(name):
+    """Every token of a full-size MoE layer (384 experts of 7168 -> 2048,
+    top-8, bf16) against the oracle, with random code words (q = -8 included)
+    and the element-wise bound; the oracle's experts run in worker processes."""
+    cfg = W.CONFIGS[name]
+    E, H, I, M, k = cfg.experts, cfg.K, cfg.N, cfg.M, cfg.top_k
+    if cfg.routing == "zipf":
+        ids = W.topk_zipf(M, E, k, cfg.zipf_alpha, cfg.index)
+    else:
+        ids = W.topk_uniform(M, E, k, cfg.index)
+    wts = W.gate_weights(M, k, cfg.index)
+    stacks, expert = _random_code_stacks(cfg, E, H, I)
+    x = x_for_dtype(W.activations(M, H, cfg.index).cuda(), cfg.x_dtype)
+    y = _moe_gpu(x, to_dev(ids), to_dev(wts), *stacks)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    print(f"{name}: {int((counts > 0).sum())} experts active, rows per expert {counts.min()}..{counts.max()}",
+          flush=True)
+    ref, bound = _moe_ref(x, ids, wts, expert, E, cfg.x_dtype, workers=16)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, bound, name)
+    print(f"{name} random codes relF={err:.3e} worst/bound={worst:.2e} on all {M} tokens "
+          f"({int((counts > 0).sum())} experts)", flush=True)
+    assert err <= tol_for(cfg.x_dtype)
+    return counts
+
+
+def test_moe_decode_full_size_every_token():
+    _full_moe_every_token("moe_decode_m64")
+
+
+def test_moe_prefill_full_size_every_token():
+    """Zipf(1.1) routing: every item kind at full size, among them the hot
+    expert's tiles, experts of exactly 16 and 17 rows (the bf16 GEMV/tile
+    boundary), experts of 65-127 rows (a ragged second tile) and expert 383."""
+    cfg = W.CONFIGS["moe_prefill_m2048"]
+    ids = W.topk_zipf(cfg.M, cfg.experts, cfg.top_k, cfg.zipf_alpha, cfg.index)
+    counts = np.bincount(ids.ravel(), minlength=cfg.experts)
+    assert (counts == 16).any() and (counts == 17).any() and ((counts > 64) & (counts < 128)).any()
+    assert counts[cfg.experts - 1] > 0
+    _full_moe_every_token("moe_prefill_m2048")

@@ -10,6 +10,7 @@ import int4_w4a16_group_g32_amd as L
 import oracle as O
 import workloads as W
 from helpers import oracle_quantize_stack, rel_err, to_dev, tol_for, weight_from_codes, x_for_dtype, x_values
+from oracle_pool import TAU, ExpertPool, check_elementwise, mlp_bound, moe_bound_from
 
 pytestmark = pytest.mark.gpu
 
@@ -49,11 +50,23 @@ def test_moe_shared_small(M, E, k, H, I, dtype):
     wts = W.gate_weights(M, k, cfg)
     x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
     y = _run_shared(x, to_dev(ids), to_dev(wts), routed, shared)
-    ref = O.moe_shared64(x_values(x), ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E,
-                         ((sgq[0], sgs[0]), (suq[0], sus[0]), (sdq[0], sds[0])))
+    sh = ((sgq[0], sgs[0]), (suq[0], sus[0]), (sdq[0], sds[0]))
+    ref, bound = _shared_ref(x, ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E, sh,
+                             dtype)
     err = rel_err(y, ref)
-    print(f"moe+shared M={M} E={E} k={k} H={H} I={I} {dtype} relF={err:.3e}", flush=True)
+    worst = check_elementwise(y.cpu().numpy(), ref, bound, f"moe+shared M={M} {dtype}")
+    print(f"moe+shared M={M} E={E} k={k} H={H} I={I} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
     assert err <= tol_for(dtype)
+
+
+def _shared_ref(x, ids, wts, expert, E, shared, dtype, tokens=None, workers=0):
+    """The oracle's routed-plus-shared output and its per-element bound."""
+    xv = x_values(x)
+    with ExpertPool(TAU[dtype], workers=workers) as pool:
+        ref = O.moe_shared64(xv, ids, wts, expert, E, shared, tokens=tokens, map_fn=pool)
+        bound = moe_bound_from(pool.bounds, ids, wts, tokens)
+    rows = np.arange(xv.shape[0]) if tokens is None else np.asarray(tokens)
+    return ref, bound + mlp_bound(xv[rows], *shared, TAU[dtype])
 
 
 @pytest.mark.parametrize("M", [4, 64])
@@ -78,7 +91,8 @@ def test_moe_shared_zero_scales_equal_routed_only(M):
 
 def test_moe_shared_decode_full_size():
     """The MoE decode layer (64 tokens, 384 experts of 7168 -> 2048, top-8,
-    bf16) with a shared expert of the same shape; the oracle on sampled tokens."""
+    bf16) with a shared expert of the same shape, quantized on the GPU; the
+    oracle, on two tokens, quantizes the same float32 weights itself."""
     cfg = W.CONFIGS["moe_decode_m64"]
     E, H, I, M, k = cfg.experts, cfg.K, cfg.N, cfg.M, cfg.top_k
     ids = W.topk_uniform(M, E, k, cfg.index)
@@ -112,3 +126,40 @@ def test_moe_shared_decode_full_size():
     print(f"moe_decode_m64 + shared relF={err:.3e} on tokens {tokens}", flush=True)
     assert err <= tol_for(cfg.x_dtype)
     assert torch.isfinite(y).all()
+
+
+def test_moe_shared_decode_full_size_every_token():
+    """The same layer with random code words (q = -8 included) drawn on the
+    GPU: every token against the oracle, with the element-wise bound; the
+    oracle's experts run in worker processes."""
+    cfg = W.CONFIGS["moe_decode_m64"]
+    E, H, I, M, k = cfg.experts, cfg.K, cfg.N, cfg.M, cfg.top_k
+    ids = W.topk_uniform(M, E, k, cfg.index)
+    wts = W.gate_weights(M, k, cfg.index)
+    tags = ((W.TAG_GATE, (H, I)), (W.TAG_UP, (H, I)), (W.TAG_DOWN, (I, H)))
+    canon, stacks, shared_dev, shared_np = {}, [], [], []
+    for tag, (K, N) in tags:
+        qw = torch.empty((E, K // 8, N), dtype=torch.int32, device="cuda")
+        sc = torch.empty((E, K // 32, N), dtype=torch.float32, device="cuda")
+        for e in range(E):
+            qw[e] = W.code_words(K, N, cfg.index, tag, e, device="cuda")
+            sc[e] = W.scale_values(K // 32, N, cfg.index, tag, e, device="cuda")
+        canon[tag] = (qw, sc)
+        stacks.append(L.prepack(L.Weight(qw, sc, K, N, E, L.LAYOUT_CANONICAL), torch.empty_like(qw)))
+        sq = W.code_words(K, N, cfg.index, tag, SHARED_INDEX, device="cuda")[None].contiguous()
+        ss = W.scale_values(K // 32, N, cfg.index, tag, SHARED_INDEX, device="cuda")[None].contiguous()
+        shared_dev.append(L.prepack(L.Weight(sq, ss, K, N, 1, L.LAYOUT_CANONICAL), torch.empty_like(sq)))
+        shared_np.append((sq[0].cpu().numpy(), ss[0].cpu().numpy()))
+    torch.cuda.synchronize()
+    x = x_for_dtype(W.activations(M, H, cfg.index).cuda(), cfg.x_dtype)
+    y = _run_shared(x, to_dev(ids), to_dev(wts), stacks, shared_dev)
+
+    def expert(e):
+        return tuple((canon[t][0][e].cpu().numpy(), canon[t][1][e].cpu().numpy()) for t, _ in tags)
+
+    ref, bound = _shared_ref(x, ids, wts, expert, E, tuple(shared_np), cfg.x_dtype, workers=16)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, bound, "moe_decode_m64 + shared")
+    print(f"moe_decode_m64 + shared random codes relF={err:.3e} worst/bound={worst:.2e} on all {M} tokens",
+          flush=True)
+    assert err <= tol_for(cfg.x_dtype)

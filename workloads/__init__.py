@@ -26,6 +26,8 @@ WEIGHT_STD = 0.02
 
 # tensor tags, so that every (config, tensor) pair has its own stream
 TAG_X, TAG_GATE, TAG_UP, TAG_DOWN, TAG_TOPK, TAG_GATEW, TAG_ZIPF, TAG_LOGITS = range(8)
+# streams of random code words and scales (drawn directly, not quantized)
+TAG_CODES, TAG_SCALES = 8, 9
 
 
 @dataclass(frozen=True)
@@ -134,3 +136,19 @@ def gate_weights(M, k, config, index=0) -> np.ndarray:
     z = rng.standard_normal((M, k))
     z = np.exp(z - z.max(axis=1, keepdims=True))
     return (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+def code_words(K, N, config, tag, index=0, device="cpu") -> torch.Tensor:
+    """Random 32-bit words [K/8][N] as int32, every bit uniform: each nibble is
+    uniform over 0..15, so code 0 (value -8) appears as often as any other.
+    ``tag`` names the matrix (TAG_GATE, TAG_UP, TAG_DOWN)."""
+    g = _gen(device, seed_of(config, TAG_CODES * 16 + tag, index))
+    w = torch.randint(-(2 ** 31), 2 ** 31, (K // 8, N), generator=g, device=device, dtype=torch.int64)
+    return w.to(torch.int32)
+
+
+def scale_values(G, N, config, tag, index=0, lo=0.004, hi=0.009, device="cpu") -> torch.Tensor:
+    """Random float32 scales [G][N], uniform in [lo, hi) (the range that
+    max|w| / 7 takes for 32 draws of N(0, 0.02^2))."""
+    g = _gen(device, seed_of(config, TAG_SCALES * 16 + tag, index))
+    return torch.rand((G, N), generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
