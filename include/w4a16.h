@@ -223,6 +223,30 @@ W4A16_API w4a16_status_t w4a16_swiglu_mlp_timed(const void* x, w4a16_dtype_t xt,
                                                 hipEvent_t* events, int32_t capacity,
                                                 int32_t* recorded);
 
+/* Size of the static scratch array behind w4a16_swiglu_mlp_static (64 MiB per GPU). */
+#define W4A16_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * w4a16_swiglu_mlp without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The same kernels and results as
+ * w4a16_swiglu_mlp (bitwise), with the workspace taken from a static device
+ * array of W4A16_STATIC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends.  The call allocates nothing and frees
+ * nothing; its first call on a device looks up the array's address there and
+ * zeroes its first 64 KiB with a fill kernel on `stream`.  Every call on one
+ * GPU shares that GPU's array, so calls that may overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  The
+ * caller still passes x and y.  Errors as w4a16_swiglu_mlp, plus WORKSPACE
+ * (nothing enqueued) when the call needs more scratch than the array holds
+ * (w4a16_swiglu_mlp_workspace_bytes above W4A16_STATIC_SCRATCH_BYTES; the
+ * hidden 7168 / intermediate 18432 MLP fits up to M = 128) and HIP if the
+ * array's address cannot be looked up.
+ */
+W4A16_API w4a16_status_t w4a16_swiglu_mlp_static(const void* x, w4a16_dtype_t xt, int32_t M,
+                                                 const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                                 const w4a16_weight_t* down, float* y, hipStream_t stream);
+
 /*
  * Router: the top_k experts of every token and their gate weights (page "The
  * Final Wire", section "What the Edit Actually Changes": for each token the

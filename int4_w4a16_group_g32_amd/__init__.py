@@ -35,6 +35,7 @@ EXPORTS = (
     "w4a16_swiglu_mlp_workspace_bytes",
     "w4a16_swiglu_mlp",
     "w4a16_swiglu_mlp_timed",
+    "w4a16_swiglu_mlp_static",
     "w4a16_moe_topk",
     "w4a16_moe_route",
     "w4a16_moe_workspace_bytes",
@@ -89,6 +90,7 @@ def load_library() -> ctypes.CDLL:
             "w4a16_swiglu_mlp": (i32, [vp, i32, i32, dp, dp, dp, vp, vp, sz, vp]),
             "w4a16_swiglu_mlp_timed": (i32, [vp, i32, i32, dp, dp, dp, vp, vp, sz, vp, vp, i32,
                                              ctypes.POINTER(i32)]),
+            "w4a16_swiglu_mlp_static": (i32, [vp, i32, i32, dp, dp, dp, vp, vp]),
             "w4a16_moe_topk": (i32, [vp, i32, i32, i32, vp, vp, vp]),
             "w4a16_moe_route": (i32, [vp, i32, i32, i32, vp, vp, vp, vp, vp]),
             "w4a16_moe_workspace_bytes": (sz, [i32, i32, i32, dp, dp, dp]),
@@ -256,6 +258,15 @@ def swiglu_mlp(x: torch.Tensor, gate: Weight, up: Weight, down: Weight, y: torch
     _check(load_library().w4a16_swiglu_mlp(_ptr(x), _dtype_code(x), x.shape[0], _dref(gate), _dref(up),
                                            _dref(down), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                            _stream(stream)), "w4a16_swiglu_mlp")
+
+
+def swiglu_mlp_static(x: torch.Tensor, gate: Weight, up: Weight, down: Weight, y: torch.Tensor, stream=None):
+    """swiglu_mlp on the library's static per-GPU scratch (no workspace, no allocation)."""
+    _need_x(x, gate.K)
+    _need(y, "y", torch.float32, (x.shape[0], down.N))
+    _on_device(x=x, y=y)
+    _check(load_library().w4a16_swiglu_mlp_static(_ptr(x), _dtype_code(x), x.shape[0], _dref(gate), _dref(up),
+                                                  _dref(down), _ptr(y), _stream(stream)), "w4a16_swiglu_mlp_static")
 
 
 def moe_topk(logits: torch.Tensor, top_k: int, topk_ids: torch.Tensor, topk_w: torch.Tensor, stream=None):

@@ -2,6 +2,7 @@
 // the dense GEMM and the dense SwiGLU MLP.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "dispatch.h"
 
@@ -372,4 +373,56 @@ extern "C" w4a16_status_t w4a16_swiglu_mlp_timed(const void* x, w4a16_dtype_t xt
   w4a16_status_t st = swiglu_mlp_impl(x, xt, M, gate, up, down, y, ws, ws_bytes, stream, ev);
   if (recorded != nullptr) *recorded = ev.recorded;
   return st;
+}
+
+// ---------------------------------------------------------------- allocation-free entry point
+
+namespace w4 {
+namespace {
+
+// The workspace of w4a16_swiglu_mlp_static: a static device array, one copy
+// on every GPU the library runs on, held until the process ends.
+__device__ __align__(256) unsigned char scratch[W4A16_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // the array's device address on each GPU (null: not set up)
+
+// The device address of `scratch` on the current device, set up on the first
+// call there: hipGetSymbolAddress with that device current (each GPU holds
+// its own copy at its own address), then the split-K counters at its start
+// are zeroed by a fill kernel on `stream` (every later call leaves them at
+// zero again).  Host code uses only this address, never the array's name.
+w4a16_status_t static_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return W4A16_ERR_HIP;
+  if (dev >= kMaxDevices) return W4A16_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return W4A16_ERR_HIP;
+    const w4a16_status_t st = w4a16_workspace_init(p, kCounterBytes, stream);
+    if (st != W4A16_OK) return st;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return W4A16_OK;
+}
+
+}  // namespace
+}  // namespace w4
+
+extern "C" w4a16_status_t w4a16_swiglu_mlp_static(const void* x, w4a16_dtype_t xt, int32_t M,
+                                                  const w4a16_weight_t* gate, const w4a16_weight_t* up,
+                                                  const w4a16_weight_t* down, float* y, hipStream_t stream) {
+  w4a16_status_t st = check_mlp(gate, up, down);
+  if (st != W4A16_OK) return st;
+  if (M < 0 || (xt != W4A16_F32 && xt != W4A16_BF16)) return W4A16_ERR_INVALID_ARG;
+  if (M == 0 || gate->K == 0 || gate->N == 0) return W4A16_OK;
+  if (x == nullptr || y == nullptr || !aligned16(x) || !aligned16(y)) return W4A16_ERR_INVALID_ARG;
+  if (plan_mlp(M, xt, gate, down).bytes > W4A16_STATIC_SCRATCH_BYTES) return W4A16_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = static_scratch(stream, &ws)) != W4A16_OK) return st;
+  EventMarks none;
+  return swiglu_mlp_impl(x, xt, M, gate, up, down, y, ws, W4A16_STATIC_SCRATCH_BYTES, stream, none);
 }

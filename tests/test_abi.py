@@ -177,3 +177,18 @@ def test_output_sizes_are_checked_before_launch(lib):
     assert lib.w4a16_prepacked_bytes(ctypes.byref(_desc(group=96))) == 0
     assert lib.w4a16_prepacked_bytes(ctypes.byref(_desc(N=96))) == 0
     assert lib.w4a16_prepacked_bytes(None) == 0
+
+
+def test_static_mlp_size_check_is_host_only(lib):
+    """w4a16_swiglu_mlp_static rejects a call that needs more than its static
+    scratch before touching any device (these pointers are not device memory)."""
+    g, u, dn = _desc(7168, 18432), _desc(7168, 18432), _desc(18432, 7168)
+    need = lib.w4a16_swiglu_mlp_workspace_bytes(512, L.F32, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn))
+    assert need > 64 << 20
+    st = lib.w4a16_swiglu_mlp_static(ctypes.c_void_p(0x100000), L.F32, 512, ctypes.byref(g), ctypes.byref(u),
+                                     ctypes.byref(dn), ctypes.c_void_p(0x200000), None)
+    assert st == L.ERR_WORKSPACE
+    assert lib.w4a16_swiglu_mlp_static(None, L.F32, 0, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), None,
+                                       None) == L.OK  # M == 0: nothing to do
+    assert lib.w4a16_swiglu_mlp_static(None, 7, 4, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), None,
+                                       None) == L.ERR_INVALID_ARG
