@@ -180,6 +180,20 @@ W4A16_API size_t w4a16_gemm_workspace_bytes(int32_t M, const w4a16_weight_t* w, 
 W4A16_API w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M, const w4a16_weight_t* w,
                           float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Measurement variant of w4a16_gemm: identical work and results, and in
+ * addition brackets each kernel it launches with two of the caller's events
+ * (events[2i] at the start and events[2i+1] at the end of kernel i, taken by
+ * the runtime from the kernel's own dispatch), at most `capacity` events;
+ * *recorded (if not NULL) receives how many were used.  Up to 8 rows
+ * (float32) or 16 (bf16) it launches one GEMV kernel; above, the activation
+ * pieces and then the MFMA tiles.  Errors as w4a16_gemm, plus INVALID_ARG for
+ * capacity < 0 or events == NULL with capacity > 0.
+ */
+W4A16_API w4a16_status_t w4a16_gemm_timed(const void* x, w4a16_dtype_t xt, int32_t M, const w4a16_weight_t* w,
+                                          float* y, void* ws, size_t ws_bytes, hipStream_t stream,
+                                          hipEvent_t* events, int32_t capacity, int32_t* recorded);
+
 /* Bytes of workspace w4a16_swiglu_mlp needs. */
 W4A16_API size_t w4a16_swiglu_mlp_workspace_bytes(int32_t M, w4a16_dtype_t xt, const w4a16_weight_t* gate,
                                         const w4a16_weight_t* up, const w4a16_weight_t* down);
@@ -336,14 +350,15 @@ W4A16_API w4a16_status_t w4a16_moe_grouped_shared(const void* x, w4a16_dtype_t x
 
 /*
  * Measurement variant of w4a16_moe_grouped: identical work and results, and in
- * addition records the caller's events on `stream` between the kernels it
- * launches: events[i] just before kernel i and one more after the last (each
- * interval also holds the next kernel's dispatch gap), at most `capacity`
- * events; *recorded (if not NULL) receives how many were recorded.  Kernels in
- * launch order: expert grouping; gate/up GEMV for the light experts (at most
- * 8 rows with float32 activations, 16 with bf16); when some expert can be
- * heavier, activation pieces (one row per token) and gate/up MFMA tiles; down
- * GEMV; then pieces of the intermediate and down MFMA tiles; weighted combine.
+ * addition brackets each kernel it launches with two of the caller's events,
+ * as w4a16_swiglu_mlp_timed does: events[2i] at the start and events[2i+1] at
+ * the end of kernel i, taken by the runtime from the kernel's own dispatch, at
+ * most `capacity` events; *recorded (if not NULL) receives how many were
+ * used.  Kernels in launch order: expert grouping; gate/up GEMV for the light
+ * experts (at most 8 rows with float32 activations, 16 with bf16); when some
+ * expert can be heavier, activation pieces (one row per token) and gate/up
+ * MFMA tiles; down GEMV; then pieces of the intermediate and down MFMA tiles;
+ * weighted combine.
  * Errors as w4a16_moe_grouped, plus INVALID_ARG for capacity < 0 or
  * events == NULL with capacity > 0, and HIP if recording fails.
  */

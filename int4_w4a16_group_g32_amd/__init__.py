@@ -32,6 +32,7 @@ EXPORTS = (
     "w4a16_dequantize",
     "w4a16_gemm_workspace_bytes",
     "w4a16_gemm",
+    "w4a16_gemm_timed",
     "w4a16_swiglu_mlp_workspace_bytes",
     "w4a16_swiglu_mlp",
     "w4a16_swiglu_mlp_timed",
@@ -86,6 +87,7 @@ def load_library() -> ctypes.CDLL:
             "w4a16_dequantize": (i32, [dp, vp, sz, vp]),
             "w4a16_gemm_workspace_bytes": (sz, [i32, dp, i32]),
             "w4a16_gemm": (i32, [vp, i32, i32, dp, vp, vp, sz, vp]),
+            "w4a16_gemm_timed": (i32, [vp, i32, i32, dp, vp, vp, sz, vp, vp, i32, ctypes.POINTER(i32)]),
             "w4a16_swiglu_mlp_workspace_bytes": (sz, [i32, i32, dp, dp, dp]),
             "w4a16_swiglu_mlp": (i32, [vp, i32, i32, dp, dp, dp, vp, vp, sz, vp]),
             "w4a16_swiglu_mlp_timed": (i32, [vp, i32, i32, dp, dp, dp, vp, vp, sz, vp, vp, i32,

@@ -237,9 +237,9 @@ extern "C" size_t w4a16_gemm_workspace_bytes(int32_t M, const w4a16_weight_t* w,
   return plan_gemm(M, w, xt).bytes;
 }
 
-extern "C" w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M,
-                                     const w4a16_weight_t* w, float* y, void* ws, size_t ws_bytes,
-                                     hipStream_t stream) {
+namespace w4 {
+static w4a16_status_t gemm_impl(const void* x, w4a16_dtype_t xt, int32_t M, const w4a16_weight_t* w, float* y,
+                                void* ws, size_t ws_bytes, hipStream_t stream, EventMarks& ev) {
   w4a16_status_t st = check_dense_grouped(w);
   if (st != W4A16_OK) return st;
   if (M < 0 || (xt != W4A16_F32 && xt != W4A16_BF16)) return W4A16_ERR_INVALID_ARG;
@@ -255,18 +255,42 @@ extern "C" w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M,
   if (p.mfma) {
     _Float16* ap = reinterpret_cast<_Float16*>(wsb + p.ap_off);
     float* rs = reinterpret_cast<float*>(wsb + p.rs_off);
-    st = launch_mfma_prep(x, xt, M, p.mf.Mp, w->K, p.mf.P, nullptr, 0, nullptr, ap, rs, stream);
+    EventMarks::Bracket b = ev.bracket();
+    st = launch_mfma_prep(x, xt, M, p.mf.Mp, w->K, p.mf.P, nullptr, 0, nullptr, ap, rs, stream, b.start, b.stop);
     if (st != W4A16_OK) return st;
     MfmaArgs a = mfma_dense_args(p.mf, M, w, nullptr, 0, ap, rs, wsb, p.partials_off, p.counters_off);
     a.out = y;
-    if (p.mf.wide) return launch_wide(a, p.mf.tasks * p.mf.S, stream);
-    return launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream);
+    b = ev.bracket();
+    if (p.mf.wide) return launch_wide(a, p.mf.tasks * p.mf.S, stream, b.start, b.stop);
+    return launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream, b.start, b.stop);
   }
   if (!counters_fit(p.tasks, p.S)) return W4A16_ERR_UNSUPPORTED;
   GemvArgs a = gemv_dense_args(M, w, nullptr, 0, x, xt == W4A16_BF16, gemv_pieces(xt), p.tiles, p.S, p.gps, wsb,
                                p.partials_off, p.counters_off);
   a.out = y;
-  return launch_gemv(a, p.tasks * p.S, stream);
+  EventMarks::Bracket b = ev.bracket();
+  return launch_gemv(a, p.tasks * p.S, stream, b.start, b.stop);
+}
+}  // namespace w4
+
+extern "C" w4a16_status_t w4a16_gemm(const void* x, w4a16_dtype_t xt, int32_t M,
+                                     const w4a16_weight_t* w, float* y, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  EventMarks none;
+  return gemm_impl(x, xt, M, w, y, ws, ws_bytes, stream, none);
+}
+
+extern "C" w4a16_status_t w4a16_gemm_timed(const void* x, w4a16_dtype_t xt, int32_t M,
+                                           const w4a16_weight_t* w, float* y, void* ws, size_t ws_bytes,
+                                           hipStream_t stream, hipEvent_t* events, int32_t capacity,
+                                           int32_t* recorded) {
+  if (capacity < 0 || (capacity > 0 && events == nullptr)) return W4A16_ERR_INVALID_ARG;
+  EventMarks ev;
+  ev.events = events;
+  ev.capacity = capacity;
+  const w4a16_status_t st = gemm_impl(x, xt, M, w, y, ws, ws_bytes, stream, ev);
+  if (recorded != nullptr) *recorded = ev.recorded;
+  return st;
 }
 
 extern "C" size_t w4a16_swiglu_mlp_workspace_bytes(int32_t M, w4a16_dtype_t xt,

@@ -47,16 +47,13 @@ struct MlpPlan {
   size_t bytes = 0;
 };
 
-// Optional measurement hook: records caller events on the stream between the
-// kernels an entry point launches (events[i] before kernel i, one after the last).
+// Optional measurement hook: hands out caller events in pairs, the start and
+// stop of each kernel an entry point launches (taken by the runtime from the
+// kernel's own dispatch).
 struct EventMarks {
   hipEvent_t* events = nullptr;
   int capacity = 0;
   int recorded = 0;
-  w4a16_status_t mark(hipStream_t stream) {
-    if (events == nullptr || recorded >= capacity) return W4A16_OK;
-    return hipEventRecord(events[recorded++], stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
-  }
   // The start and stop events of the next kernel (both null once the caller's
   // array is used up, or without events).
   struct Bracket {

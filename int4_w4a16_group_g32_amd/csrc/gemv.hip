@@ -56,10 +56,13 @@ static_assert(kWin % kRing == 0, "ring slots must stay aligned across windows");
 static_assert(sizeof(uint4) * kWin * kUnitsPerGroup >= sizeof(float) * 4 * kMaxGemvRows * kGemvCols,
               "the tile buffers of a workgroup must fit in the staging buffer");
 
-// k blocks are XOR-swizzled by row so the 16 rows of one k block fall in
-// distinct LDS banks.
+// The low four bits of a unit's index pick one of 16 four-bank groups:
+// 4 * ((r & 3) ^ (g & 3)) + (kb ^ ((r >> 2) & 3) ^ ((g >> 2) & 1)).  A fragment
+// read (16 rows at one g and kb) and a staging store (16 lanes: one row,
+// eight groups, two k blocks) both cover all 16.  Rows are permuted only
+// within blocks of four.
 __device__ __forceinline__ int a_unit(int g, int r, int kb) {
-  return (g * 16 + r) * 4 + (kb ^ ((r >> 2) & 3));
+  return (g * 16 + ((r & ~3) | ((r & 3) ^ (g & 3)))) * 4 + (kb ^ ((r >> 2) & 3) ^ ((g >> 2) & 1));
 }
 
 // Staging of groups [gw, gw + nw) of rows pos0 .. pos0 + nrows - 1 (up to

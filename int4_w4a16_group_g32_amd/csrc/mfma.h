@@ -86,7 +86,8 @@ w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream
                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Wide-tile launch (mode 0, dense rows, Mp a multiple of kWideRows); a.tiles
 // counts 128-column tiles.
-w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stream);
+w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stream, hipEvent_t start = nullptr,
+                           hipEvent_t stop = nullptr);
 
 // Rows of the piece planes for R positions.
 inline int mfma_rows_padded(int R) { return (R + kMfmaRows - 1) / kMfmaRows * kMfmaRows + kMfmaRows; }

@@ -224,8 +224,11 @@ struct MfmaLds {
   uint4 a[2][kWinUnits<P>];  // double buffer
 };
 
-// Thread t loads units t, t + 256, ...: unit u = ((p * 64 + row) * kGw + gl) * 4 + kb,
-// so 16 consecutive threads read one row's four groups (256 contiguous bytes).
+// Thread t loads units t, t + 256, ...: unit u holds k block u & 3 of tile
+// row 4 * (u >> 6) + ((u >> 2) & 3) (in piece plane u >> 10) and window group
+// (u >> 4) & 3, so 16 consecutive threads take four rows' 64 bytes of one
+// group, and their stores (four rows times four k blocks) fall in 16 distinct
+// bank groups.  A thread keeps one window group and one k block throughout.
 // The loads are unconditional (clamped addresses); groups past the split's
 // end are zeroed when the window is stored, so the tail needs no masking.  A
 // load under a branch, or a use of its value before the window's groups are
@@ -233,21 +236,24 @@ struct MfmaLds {
 // The thread's units cover four tile rows, the same in every window and
 // piece plane: srow[j] is the piece row of tile row row_of_unit(j).
 constexpr int kUnitRows = 4;
-__device__ __forceinline__ int row_of_unit(int i) {
+struct WinUnit {
+  int kb, gl, row, p;
+};
+__device__ __forceinline__ WinUnit win_unit(int i) {
   const int u = static_cast<int>(threadIdx.x) + kMfmaThreads * i;
-  return (u >> 2) / kGw % kMfmaRows;
+  return WinUnit{u & 3, (u >> 4) & 3, (4 * (u >> 6) + ((u >> 2) & 3)) % kMfmaRows, u >> 10};
 }
+__device__ __forceinline__ int row_of_unit(int i) { return win_unit(i).row; }
 
 template <int P>
 __device__ __forceinline__ void load_a_window(const MfmaArgs& a, const int srow[kUnitRows], int gw, int g_hi,
                                               uint4 r[kWinUnits<P> / kMfmaThreads]) {
-  static_assert(kMfmaThreads * kUnitRows / 4 / kGw == kMfmaRows, "a thread's units repeat every 4 rows");
+  static_assert(kGw == 4 && kMfmaThreads == 256 && kMfmaRows == 64, "the unit mapping assumes these sizes");
 #pragma unroll
   for (int i = 0; i < kWinUnits<P> / kMfmaThreads; ++i) {
-    const int u = static_cast<int>(threadIdx.x) + kMfmaThreads * i;
-    const int kb = u & 3, gl = (u >> 2) % kGw, p = (u >> 2) / kGw / kMfmaRows;
-    r[i] = *reinterpret_cast<const uint4*>(a.ap + (static_cast<size_t>(p) * a.Mp + srow[i % kUnitRows]) * a.K +
-                                           static_cast<size_t>(min(gw + gl, g_hi - 1)) * kGroup + 8 * kb);
+    const WinUnit w = win_unit(i);
+    r[i] = *reinterpret_cast<const uint4*>(a.ap + (static_cast<size_t>(w.p) * a.Mp + srow[i % kUnitRows]) * a.K +
+                                           static_cast<size_t>(min(gw + w.gl, g_hi - 1)) * kGroup + 8 * w.kb);
   }
 }
 
@@ -256,9 +262,8 @@ __device__ __forceinline__ void store_a_window(uint4* buf, int gw, int g_hi,
                                                const uint4 r[kWinUnits<P> / kMfmaThreads]) {
 #pragma unroll
   for (int i = 0; i < kWinUnits<P> / kMfmaThreads; ++i) {
-    const int u = static_cast<int>(threadIdx.x) + kMfmaThreads * i;
-    const int kb = u & 3, gl = (u >> 2) % kGw, row = (u >> 2) / kGw % kMfmaRows, p = (u >> 2) / kGw / kMfmaRows;
-    buf[a_off(p, gl, row, kb)] = gw + gl < g_hi ? r[i] : make_uint4(0, 0, 0, 0);
+    const WinUnit w = win_unit(i);
+    buf[a_off(w.p, w.gl, w.row, w.kb)] = gw + w.gl < g_hi ? r[i] : make_uint4(0, 0, 0, 0);
   }
 }
 

@@ -10,6 +10,8 @@
 
 #include "dispatch.h"
 
+#include <hip/hip_ext.h>
+
 namespace w4 {
 namespace {
 
@@ -284,12 +286,13 @@ size_t route_lds_bytes(int E) { return static_cast<size_t>(route_waves(E) + 1) *
 w4a16_status_t launch_route(const int32_t* ids, int M, int top_k, int E, int32_t* counts,
                             int32_t* offsets, int32_t* sorted_pairs, int32_t* inv, int4* items_g,
                             int4* items_m, int32_t* n_items, int32_t* heavy, int shared_rows,
-                            int gemv_rows, int expert_rows, hipStream_t stream) {
+                            int gemv_rows, int expert_rows, hipStream_t stream, hipEvent_t start = nullptr,
+                            hipEvent_t stop = nullptr) {
   if (2 * E > kRouteLdsInts) return W4A16_ERR_UNSUPPORTED;
   const size_t lds = route_lds_bytes(E);
-  route_kernel<<<1, kRouteThreads, lds, stream>>>(ids, M, top_k, E, counts, offsets, sorted_pairs,
-                                                   inv, items_g, items_m, n_items, heavy, shared_rows,
-                                                   gemv_rows, expert_rows);
+  hipExtLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, stream, start, stop, 0, ids, M, top_k, E,
+                        counts, offsets, sorted_pairs, inv, items_g, items_m, n_items, heavy, shared_rows, gemv_rows,
+                        expert_rows);
   return launch_status();
 }
 
@@ -463,9 +466,9 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   const int T = static_cast<int>(p.positions);  // routed pairs, then the shared expert's rows
 
   // 1. expert grouping and work items
-  if ((st = ev.mark(stream)) != W4A16_OK) return st;
+  EventMarks::Bracket bk = ev.bracket();
   st = launch_route(topk_ids, M, top_k, E, counts, offsets, sorted, inv, items, mitems, n_items,
-                    heavy, shared ? M : 0, gemv_rows(xt), p.expert_rows, stream);
+                    heavy, shared ? M : 0, gemv_rows(xt), p.expert_rows, stream, bk.start, bk.stop);
   if (st != W4A16_OK) return st;
 
   // 2. gate/up with the SwiGLU epilogue: light experts on the GEMV, heavy on MFMA tiles
@@ -499,8 +502,8 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     a.qw1x = reinterpret_cast<const u32x4*>(su->qw);
     a.sc1x = su->scales;
   }
-  if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(a, p.max_items * a.tiles, stream);
+  bk = ev.bracket();
+  st = launch_gemv(a, p.max_items * a.tiles, stream, bk.start, bk.stop);
   if (st != W4A16_OK) return st;
 
   _Float16* apx = reinterpret_cast<_Float16*>(b + p.apx_off);
@@ -509,9 +512,9 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   float* rsh = reinterpret_cast<float*>(b + p.rsh_off);
   MfmaArgs ma{};
   if (p.mfma) {
-    if ((st = ev.mark(stream)) != W4A16_OK) return st;
+    bk = ev.bracket();
     // pieces once per token; the tiles read position p from token sorted[p] / top_k
-    st = launch_mfma_prep(x, xt, M, M, H, p.P, nullptr, 0, nullptr, apx, rsx, stream);
+    st = launch_mfma_prep(x, xt, M, M, H, p.P, nullptr, 0, nullptr, apx, rsx, stream, bk.start, bk.stop);
     if (st != W4A16_OK) return st;
     ma.ap = apx;
     ma.rs = rsx;
@@ -541,8 +544,8 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     ma.sc0x = a.sc0x;
     ma.qw1x = a.qw1x;
     ma.sc1x = a.sc1x;
-    if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma(ma, p.P, p.max_mitems * ma.tiles, stream);
+    bk = ev.bracket();
+    st = launch_mfma(ma, p.P, p.max_mitems * ma.tiles, stream, bk.start, bk.stop);
     if (st != W4A16_OK) return st;
   }
 
@@ -571,12 +574,12 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     d.qw0x = reinterpret_cast<const u32x4*>(sd->qw);
     d.sc0x = sd->scales;
   }
-  if ((st = ev.mark(stream)) != W4A16_OK) return st;
-  st = launch_gemv(d, p.max_items * d.tiles, stream);
+  bk = ev.bracket();
+  st = launch_gemv(d, p.max_items * d.tiles, stream, bk.start, bk.stop);
   if (st != W4A16_OK) return st;
   if (p.mfma) {
-    if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma_prep(hraw, W4A16_F32, T, p.Mp, I, p.P, nullptr, 0, heavy, aph, rsh, stream);
+    bk = ev.bracket();
+    st = launch_mfma_prep(hraw, W4A16_F32, T, p.Mp, I, p.P, nullptr, 0, heavy, aph, rsh, stream, bk.start, bk.stop);
     if (st != W4A16_OK) return st;
     MfmaArgs md = ma;
     md.ap = aph;
@@ -602,19 +605,17 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     md.sc0x = d.sc0x;
     md.qw1x = nullptr;
     md.sc1x = nullptr;
-    if ((st = ev.mark(stream)) != W4A16_OK) return st;
-    st = launch_mfma(md, p.P, p.max_mitems * md.tiles, stream);
+    bk = ev.bracket();
+    st = launch_mfma(md, p.P, p.max_mitems * md.tiles, stream, bk.start, bk.stop);
     if (st != W4A16_OK) return st;
   }
 
   // 4. weighted combine in slot order
-  if ((st = ev.mark(stream)) != W4A16_OK) return st;
+  bk = ev.bracket();
   const size_t total = static_cast<size_t>(M) * (H / 4);
-  combine_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(o, inv, topk_w, M,
-                                                                                  top_k, H, shared ? R : -1,
-                                                                                  y);
-  if ((st = launch_status()) != W4A16_OK) return st;
-  return ev.mark(stream);
+  hipExtLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, stream,
+                        bk.start, bk.stop, 0, o, inv, topk_w, M, top_k, H, shared ? R : -1, y);
+  return launch_status();
 }
 }  // namespace w4
 

@@ -28,6 +28,8 @@
 #include "mfma.h"
 #include "mfma_ops.h"
 
+#include <hip/hip_ext.h>
+
 namespace w4 {
 namespace {
 
@@ -400,12 +402,14 @@ void wide_kernel(const MfmaArgs a) {
 
 }  // namespace
 
-w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stream) {
+w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stream, hipEvent_t start,
+                           hipEvent_t stop) {
   if (num_tasks == 0) return W4A16_OK;
   if (num_tasks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   if (a.mode != 0 || a.dense_rows <= 0 || a.Mp % kWideRows != 0 || a.G % kWw != 0 || a.gps % kWw != 0)
     return W4A16_ERR_UNSUPPORTED;
-  wide_kernel<<<static_cast<unsigned>(num_tasks), kWideThreads, 0, stream>>>(a);
+  hipExtLaunchKernelGGL(wide_kernel, dim3(static_cast<unsigned>(num_tasks)), dim3(kWideThreads), 0, stream, start,
+                        stop, 0, a);
   return launch_status();
 }
 
