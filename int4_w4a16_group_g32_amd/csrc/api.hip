@@ -76,6 +76,9 @@ MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt, bool allo
       S = s;
     }
   }
+  // the tile kernel addresses a split's codes with 32-bit buffer offsets
+  const size_t row_bytes = static_cast<size_t>(N) * 16;
+  while (S < G && static_cast<size_t>((G + S - 1) / S) * row_bytes > 0x7fffffffu) ++S;
   m.S = S;
   m.gps = (G + S - 1) / S;
   return m;

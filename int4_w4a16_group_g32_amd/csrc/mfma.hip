@@ -272,11 +272,33 @@ struct TileCodes {
   f32x4 s;  // their scales
 };
 
-__device__ __forceinline__ void load_tile_codes(const u32x4* wp, const float* sp, size_t gstride, int g,
-                                                int g_last, int gshift, TileCodes& c) {
-  const size_t gg = static_cast<size_t>(min(g, g_last));
-  c.w = __builtin_nontemporal_load(wp + gg * gstride);
-  c.s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (gg >> gshift) * gstride));
+// Raw buffer resources: a wave-uniform base and size in scalar registers, so
+// a load takes one 32-bit lane offset and a scalar offset for the group (no
+// 64-bit address arithmetic per load).  The hardware's size check covers the
+// lane offset only, so the scalar offsets stay inside the buffer by
+// construction (groups are clamped to the split's last one).
+constexpr int kBufFlags = 0x00020000;  // dword 3 of a raw buffer resource on gfx9
+constexpr int kNt = 2;                 // nontemporal: the codes and scales are read once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufFlags);
+}
+
+// The codes and scales of split-relative group gr (clamped to the split's last
+// group gr_last): the code buffer starts at the split's first group, the scale
+// buffer at its first scale row s_lo.
+struct CodeSrc {
+  __amdgpu_buffer_rsrc_t w, s;
+  int wvoff, svoff;  // lane offsets (bytes)
+  int wstep, sstep;  // bytes per group row of codes, per scale row
+  int g_lo, s_lo, gshift;
+};
+
+__device__ __forceinline__ void load_tile_codes(const CodeSrc& c, int gr, int gr_last, TileCodes& t) {
+  const int g = min(gr, gr_last);
+  t.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.w, c.wvoff, g * c.wstep, kNt));
+  t.s = __builtin_bit_cast(
+      f32x4, __builtin_amdgcn_raw_buffer_load_b128(c.s, c.svoff, (((c.g_lo + g) >> c.gshift) - c.s_lo) * c.sstep, kNt));
 }
 
 // One group of the tile: the live row blocks (nrb of 4, wave-uniform) x 4
@@ -373,45 +395,33 @@ void mfma_kernel(const MfmaArgs a) {
     pos0 = item * kMfmaRows;
     nrows = min(kMfmaRows, a.dense_rows - pos0);
   } else {
-    if (item >= *a.n_items) return;
+    if (item >= __builtin_amdgcn_readfirstlane(*a.n_items)) return;
     const int4 it = a.items[item];
-    expert = it.x;
-    pos0 = it.y;
-    nrows = it.z;
+    // the item is the same for the whole workgroup: keep it in scalar registers
+    expert = __builtin_amdgcn_readfirstlane(it.x);
+    pos0 = __builtin_amdgcn_readfirstlane(it.y);
+    nrows = __builtin_amdgcn_readfirstlane(it.z);
   }
-  const int wv = wave_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const int lane = lane_id();
   const int lc = lane & 15, kb = lane >> 4;
   const uint32_t magic = magic_vgpr();
 
   // The lane reads one 16-byte GROUPED slot per group: word kb of four
   // adjacent columns col0 .. col0 + 3, which are column lc of MFMA blocks
-  // cb = 0..3.  Plain: the wave's 64-column block, slot 16kb + lc.  SwiGLU:
-  // the wave's 32 h columns h0 .. h0 + 31, lanes lc < 8 from gate and lanes
-  // lc >= 8 from up (the same h columns), so a lane pair (lc, lc + 8) holds
-  // gate and up of one output.
-  int mat, col0, chunk;
-  bool wave_ok;
-  if (a.mode == 1) {
-    const int h0 = tile * 128 + wv * 32;
-    wave_ok = h0 < a.N;
-    mat = lc >> 3;
-    col0 = h0 + 4 * (lc & 7);
-    chunk = (h0 >> 6) * 64 + 16 * kb + ((h0 >> 5) & 1) * 8 + (lc & 7);
-  } else {
-    const int c0 = tile * kMfmaCols + wv * 64;
-    wave_ok = c0 < a.N;
-    mat = 0;
-    col0 = c0 + 4 * lc;
-    chunk = c0 + 16 * kb + lc;
-  }
+  // cb = 0..3, so a wave load is one contiguous kilobyte of its 64-column
+  // block.  Plain: wave wv streams columns c0 = 256 tile + 64 wv.  SwiGLU: the
+  // tile is 128 h columns; waves 0 and 1 stream gate columns c0 = 128 tile +
+  // 64 (wv & 1), waves 2 and 3 the same columns of up, and the epilogue pairs
+  // them through LDS.
+  const int mat = a.mode == 1 ? wv >> 1 : 0;
+  const int c0 = a.mode == 1 ? tile * (kMfmaCols / 2) + (wv & 1) * 64 : tile * kMfmaCols + wv * 64;
+  const bool wave_ok = c0 < a.N;
+  const int col0 = c0 + 4 * lc;
   const size_t ebase = static_cast<size_t>(expert) * a.expert_stride;
   const bool xe = expert + 1 == a.extra_plus1;
   const u32x4* qb = xe ? (mat ? a.qw1x : a.qw0x) : (mat ? a.qw1 : a.qw0) + ebase;
   const float* sb = xe ? (mat ? a.sc1x : a.sc0x) : (mat ? a.sc1 : a.sc0) + (ebase >> a.gshift);
-  const u32x4* wp = qb + (wave_ok ? chunk : 0);
-  const float* sp = sb + (wave_ok ? col0 : 0);
-  const size_t gstride = static_cast<size_t>(a.N);  // chunks (and scales) per group row
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -423,13 +433,29 @@ void mfma_kernel(const MfmaArgs a) {
   const int g_hi = min(a.G, g_lo + a.gps);
   const int g_last = g_hi - 1;
   const int nwin = (g_hi - g_lo + kGw - 1) / kGw;
+  // Codes and scales of the split.  A wave past the matrix's last column
+  // streams column block 0 and stores nothing, so every load below is
+  // unconditional.
+  CodeSrc cs;
+  {
+    const size_t row_bytes = static_cast<size_t>(a.N) * 16;  // one group row of GROUPED slots
+    const int s_lo = g_lo >> a.gshift, s_hi = g_last >> a.gshift;
+    cs.w = tile_rsrc(qb + static_cast<size_t>(g_lo) * a.N, static_cast<size_t>(g_hi - g_lo) * row_bytes);
+    cs.s = tile_rsrc(sb + static_cast<size_t>(s_lo) * a.N, static_cast<size_t>(s_hi - s_lo + 1) * a.N * 4);
+    cs.wvoff = (wave_ok ? c0 + 16 * kb + lc : 16 * kb + lc) * 16;
+    cs.svoff = (wave_ok ? col0 : 4 * lc) * 4;
+    cs.wstep = a.N * 16;
+    cs.sstep = a.N * 4;
+    cs.g_lo = g_lo;
+    cs.s_lo = s_lo;
+    cs.gshift = a.gshift;
+  }
+  const int gr_last = g_last - g_lo;
   uint4 ra[kWinUnits<P> / kMfmaThreads];
   // ring of R groups of codes in flight (one or two windows): group g_lo + i
   // sits in slot i % R, so a window always uses the same slots
   static_assert(R == kGw || R == 2 * kGw, "ring of one or two windows");
   TileCodes ring[R];
-  // A wave past the matrix's last column streams column block 0 and stores
-  // nothing, so every load below is unconditional.
   int srow[kUnitRows];
 #pragma unroll
   for (int j = 0; j < kUnitRows; ++j) {
@@ -439,11 +465,11 @@ void mfma_kernel(const MfmaArgs a) {
   load_a_window<P>(a, srow, g_lo, g_hi, ra);
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    load_tile_codes(wp, sp, gstride, g_lo + j, g_last, a.gshift, ring[j]);
+    load_tile_codes(cs, j, gr_last, ring[j]);
     __builtin_amdgcn_sched_barrier(0);  // issue order = use order
   }
-  // live 16-row blocks of the tile (items hold 1 .. 64 rows)
-  const int nrb = (nrows + 15) >> 4;
+  // live 16-row blocks of the tile (items hold 1 .. 64 rows), a scalar
+  const int nrb = __builtin_amdgcn_readfirstlane((nrows + 15) >> 4);
   // one piece: the per-column-block anchors (see mma_tile_group)
   int cexp[4] = {0, 0, 0, 0};
   if (P == 1) {
@@ -470,7 +496,7 @@ void mfma_kernel(const MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < kGw; ++j) {
       mma_tile_group<P>(lds.a[h], j, lc, kb, magic, ring[(kGw * h + j) % R], nrb, cexp, acc);
-      load_tile_codes(wp, sp, gstride, gw + j + R, g_last, a.gshift, ring[(kGw * h + j) % R]);
+      load_tile_codes(cs, gw - g_lo + j + R, gr_last, ring[(kGw * h + j) % R]);
       __builtin_amdgcn_sched_barrier(0);
     }
     store_a_window<P>(lds.a[1 - h], gw + kGw, g_hi, ra);
@@ -495,10 +521,10 @@ void mfma_kernel(const MfmaArgs a) {
   // Split-K: write-through partials, an agent-scope arrival counter, and the
   // last workgroup sums the partials in split order (the GEMV kernel's
   // scheme, with the same reliance on gfx950's write-through agent-scope
-  // atomics in place of release/acquire ordering).  A partial tile is stored element-major, [j][thread] with
-  // j = (rb * 4 + cb) * 4 + i, so every store and load instruction covers 256
-  // contiguous bytes, and the readback keeps two splits' worth (128 loads per
-  // thread) in flight at a time.
+  // atomics in place of release/acquire ordering).  A partial tile is stored
+  // element-major, [j][thread] with j = (rb * 4 + cb) * 4 + i, so every store
+  // and load instruction covers 256 contiguous bytes, and the readback keeps
+  // two splits' worth (128 loads per thread) in flight at a time.
   if (a.S > 1) {
     const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
     const size_t tf = static_cast<size_t>(kMfmaRows) * kMfmaCols;
@@ -549,29 +575,52 @@ void mfma_kernel(const MfmaArgs a) {
     if (threadIdx.x == 0)
       __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (!wave_ok) return;
 
+  if (a.mode == 1) {
+    // The up waves hand their sums to the gate waves of the same columns
+    // through LDS (the window buffers are free now), element-major like the
+    // partial tiles.
+    float* xu = reinterpret_cast<float*>(&lds.a[0][0]);
+    static_assert(sizeof(MfmaLds<P>) >= 2 * 64 * 64 * sizeof(float), "the up sums must fit in the windows");
+    __syncthreads();  // every wave is done with the windows
+    if (wv >= 2) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xu[(((wv & 1) * 64 + (rb * 4 + cb) * 4 + i) << 6) + lane] = acc[rb][cb][i];
+    }
+    __syncthreads();
+    if (wv >= 2 || !wave_ok) return;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb * 16 + 4 * kb + i;
+        if (r < nrows) {
+          const size_t prow = static_cast<size_t>(pos0 + r);
+          const float f = a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const float up = xu[(((wv & 1) * 64 + (rb * 4 + cb) * 4 + i) << 6) + lane];
+            a.h[prow * a.N + col0 + cb] = silu(acc[rb][cb][i] * f) * (up * f);
+          }
+        }
+      }
+    return;
+  }
+  if (!wave_ok) return;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rb * 16 + 4 * kb + i;
-      const bool live = r < nrows;
-      const size_t prow = static_cast<size_t>(pos0 + (live ? r : 0));
-      const float f = live ? a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow] : 0.0f;
-      if (a.mode == 0) {
-        if (live) {
+      if (r < nrows) {
+        const size_t prow = static_cast<size_t>(pos0 + r);
+        const float f = a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow];
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) a.out[prow * a.N + col0 + cb] = acc[rb][cb][i] * f;
-        }
-      } else {
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const float up = __shfl_xor(acc[rb][cb][i], 8);  // every lane takes part
-          if (live && lc < 8) {
-            a.h[prow * a.N + col0 + cb] = silu(acc[rb][cb][i] * f) * (up * f);
-          }
-        }
+        for (int cb = 0; cb < 4; ++cb) a.out[prow * a.N + col0 + cb] = acc[rb][cb][i] * f;
       }
     }
 }
@@ -623,6 +672,8 @@ w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream
                            hipEvent_t stop) {
   if (num_tasks == 0) return W4A16_OK;
   if (num_tasks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
+  // a split's codes must stay within the kernel's 32-bit buffer offsets
+  if (static_cast<size_t>(a.gps) * a.N * 16 > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   const unsigned grid = static_cast<unsigned>(num_tasks);
   if (P == 2)
     hipExtLaunchKernelGGL(mfma_kernel<2, kTileRing, 2>, dim3(grid), dim3(kMfmaThreads), 0, stream, start, stop,
