@@ -211,13 +211,13 @@ KERNEL_OF = {"gate_up": "gemv", "gemv": "gemv", "mfma_gate_up": "mfma", "wide": 
 DOMINANT = {
     "gemm_m1": ("gemv", "gemv_kernel", lambda n: "gemv_kernel" in n, None),
     "mlp_decode_m4": ("gate_up", "gemv_kernel<4, 2>", lambda n: "gemv_kernel<4, 2>" in n, None),
-    "mlp_verify_m64_f32": ("mfma_gate_up", "mfma_kernel<2, 8, 2> (gate/up)", lambda n: "mfma_kernel<2, 8, 2>" in n,
-                           (0, 2)),
-    "mlp_verify_m64_bf16": ("mfma_gate_up", "mfma_kernel<1, 8, 2> (gate/up)", lambda n: "mfma_kernel<1, 8, 2>" in n,
-                            (0, 2)),
+    "mlp_verify_m64_f32": ("mfma_gate_up", "mfma_kernel<2, 8, 2, true> (gate/up)",
+                           lambda n: "mfma_kernel<2, 8, 2, true>" in n, (0, 2)),
+    "mlp_verify_m64_bf16": ("mfma_gate_up", "mfma_kernel<1, 8, 2, true> (gate/up)",
+                            lambda n: "mfma_kernel<1, 8, 2, true>" in n, (0, 2)),
     "moe_decode_m64": ("gate_up", "gemv_kernel<1, 1> (gate/up)", lambda n: "gemv_kernel<1, 1>" in n, (0, 2)),
-    "moe_prefill_m2048": ("mfma_gate_up", "mfma_kernel<1, 4, 3> (gate/up)", lambda n: "mfma_kernel<1, 4, 3>" in n,
-                          (0, 2)),
+    "moe_prefill_m2048": ("mfma_gate_up", "mfma_kernel<1, 4, 3, false> (gate/up)",
+                          lambda n: "mfma_kernel<1, 4, 3, false>" in n, (0, 2)),
     "gemm_m2048_hot_expert": ("wide", "wide_kernel", lambda n: "wide_kernel" in n, None),
 }
 
@@ -392,7 +392,7 @@ def run_mlp(args, cfg):
     ws = L.new_workspace(L.swiglu_mlp_workspace_bytes(M, xt, *base))
     lib = L.load_library()
     sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    cap = 8
+    cap = 10
 
     def step(i, evs=None):
         g, u, d = copies[i % len(copies)]
@@ -407,7 +407,9 @@ def run_mlp(args, cfg):
     # decode sizes: fused gate/up + SwiGLU GEMV, then the down GEMV; larger M:
     # activation pieces, gate/up MFMA tiles, pieces of h, down MFMA tiles
     gemv = M <= (16 if xt == L.BF16 else 8)
-    names = ["gate_up", "down"] if gemv else ["prep_x", "gate_up", "prep_h", "down"]
+    # (with K splits the tiles leave per-split sums: h is formed in prep_h, and
+    # a last kernel sums the down projection's splits)
+    names = ["gate_up", "down"] if gemv else ["prep_x", "gate_up", "prep_h", "down", "down_sum"]
     for i in range(args.warmup):
         step(i)
     ms_step = timed_steps_ms(args.steps, step)
@@ -602,7 +604,7 @@ def run_gemm(args, cfg, cold=None):
     ws = L.new_workspace(L.gemm_workspace_bytes(M, first, xt))
     lib = L.load_library()
     sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    cap = 4
+    cap = 6
 
     def run(rotate):
         def step(i, evs=None):
@@ -617,7 +619,7 @@ def run_gemm(args, cfg, cold=None):
             step(i)
         ms = timed_steps_ms(args.steps, step)
         pct = step_percentiles(args.steps, step)
-        names = ["gemv"] if M <= (16 if xt == L.BF16 else 8) else ["prep_x", "tiles"]
+        names = ["gemv"] if M <= (16 if xt == L.BF16 else 8) else ["prep_x", "tiles", "split_sum"]
         return ms, pct, kernel_ms(args.steps, names, step, cap)
 
     ms_step, pct, kern = run(True)

@@ -116,6 +116,15 @@ MfmaArgs mfma_dense_args(const MfmaPlan& m, int rows, const w4a16_weight_t* w0,
   return a;
 }
 
+// Deferred split-K for a dense tile launch with S > 1: the split sums go to
+// planes in the partials region (the same bytes as the partial tiles) and the
+// next kernel reduces them in split order.
+void defer_split_k(MfmaArgs& a, const MfmaPlan& m) {
+  a.planes = a.partials;
+  a.plane_rows = static_cast<int>(m.items) * kMfmaRows;
+  a.plane_ld = m.tiles * (a.mode == 1 ? kMfmaCols / 2 : kMfmaCols);
+}
+
 GemmPlan plan_gemm(int M, const w4a16_weight_t* w, w4a16_dtype_t xt) {
   GemmPlan p;
   if (M > gemv_rows(xt)) {
@@ -265,7 +274,12 @@ static w4a16_status_t gemm_impl(const void* x, w4a16_dtype_t xt, int32_t M, cons
     a.out = y;
     b = ev.bracket();
     if (p.mf.wide) return launch_wide(a, p.mf.tasks * p.mf.S, stream, b.start, b.stop);
-    return launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream, b.start, b.stop);
+    if (p.mf.S == 1) return launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream, b.start, b.stop);
+    defer_split_k(a, p.mf);
+    st = launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream, b.start, b.stop);
+    if (st != W4A16_OK) return st;
+    b = ev.bracket();
+    return launch_plane_sum(a.planes, a.S, a.plane_rows, a.plane_ld, rs, M, w->N, y, stream, b.start, b.stop);
   }
   if (!counters_fit(p.tasks, p.S)) return W4A16_ERR_UNSUPPORTED;
   GemvArgs a = gemv_dense_args(M, w, nullptr, 0, x, xt == W4A16_BF16, gemv_pieces(xt), p.tiles, p.S, p.gps, wsb,
@@ -348,18 +362,28 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
     if (st != W4A16_OK) return st;
     MfmaArgs a = mfma_dense_args(p.gu, M, gate, up, 1, apx, rsx, wsb, p.partials_off, p.counters_off);
     a.h = h;
+    if (p.gu.S > 1) defer_split_k(a, p.gu);
     b = ev.bracket();
     st = launch_mfma(a, p.gu.P, p.gu.tasks * p.gu.S, stream, b.start, b.stop);
     if (st != W4A16_OK) return st;
     b = ev.bracket();
-    st = launch_mfma_prep(h, W4A16_F32, M, p.dn.Mp, I, p.dn.P, nullptr, 0, nullptr, aph, rsh, stream, b.start,
-                          b.stop);
+    if (p.gu.S > 1)  // h from the gate/up split sums, then its pieces
+      st = launch_prep_planes(a.planes, a.S, a.plane_rows, a.plane_ld, rsx, M, p.dn.Mp, I, p.dn.P, h, aph, rsh,
+                              stream, b.start, b.stop);
+    else
+      st = launch_mfma_prep(h, W4A16_F32, M, p.dn.Mp, I, p.dn.P, nullptr, 0, nullptr, aph, rsh, stream, b.start,
+                            b.stop);
     if (st != W4A16_OK) return st;
     MfmaArgs d = mfma_dense_args(p.dn, M, down, nullptr, 0, aph, rsh, wsb, p.partials_off,
                                  p.counters_off);
     d.out = y;
     b = ev.bracket();
-    return launch_mfma(d, p.dn.P, p.dn.tasks * p.dn.S, stream, b.start, b.stop);
+    if (p.dn.S == 1) return launch_mfma(d, p.dn.P, p.dn.tasks * p.dn.S, stream, b.start, b.stop);
+    defer_split_k(d, p.dn);
+    st = launch_mfma(d, p.dn.P, p.dn.tasks * p.dn.S, stream, b.start, b.stop);
+    if (st != W4A16_OK) return st;
+    b = ev.bracket();
+    return launch_plane_sum(d.planes, d.S, d.plane_rows, d.plane_ld, rsh, M, down->N, y, stream, b.start, b.stop);
   }
   if (!counters_fit(p.tasks_gu, p.S_gu) || !counters_fit(p.tasks_d, p.S_d))
     return W4A16_ERR_UNSUPPORTED;

@@ -72,6 +72,12 @@ struct MfmaArgs {
   float* h;              // SwiGLU output h[pos][N], float32
   float* partials;
   int* counters;
+  // Deferred split-K (dense launches with S > 1): with `planes` set, each
+  // workgroup stores its sums to planes[split][m][row][plane_ld] (m: 0 plain
+  // or gate, 1 up; rows of the item plane) and the reduction runs in the
+  // next kernel (launch_plane_sum, or the h pieces of launch_prep_planes).
+  float* planes;
+  int plane_rows, plane_ld;
 };
 
 // Pieces of R positions (rows of x, or gathered rows gather[p] / top_k); rows
@@ -88,6 +94,19 @@ w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream
 // counts 128-column tiles.
 w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stream, hipEvent_t start = nullptr,
                            hipEvent_t stop = nullptr);
+
+// Deferred split-K, plain output: out[m][n] = (sum over splits, in split
+// order, of planes[s][0][m][n]) * rs[m] for m < M, n < N (N a multiple of 4).
+w4a16_status_t launch_plane_sum(const float* planes, int S, int plane_rows, int plane_ld, const float* rs, int M,
+                                int N, float* out, hipStream_t stream, hipEvent_t start = nullptr,
+                                hipEvent_t stop = nullptr);
+// Deferred split-K, SwiGLU: h[m][n] = silu(g * f) * (u * f) with g, u the
+// split-order sums of planes[s][0] and planes[s][1] and f = rsx[m], written
+// to h[M][I], then the f16 pieces of h as launch_mfma_prep makes them
+// (rows M .. Mp-1 zero-filled).
+w4a16_status_t launch_prep_planes(const float* planes, int S, int plane_rows, int plane_ld, const float* rsx,
+                                  int M, int Mp, int I, int P, float* h, _Float16* ap, float* rs,
+                                  hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // Rows of the piece planes for R positions.
 inline int mfma_rows_padded(int R) { return (R + kMfmaRows - 1) / kMfmaRows * kMfmaRows + kMfmaRows; }

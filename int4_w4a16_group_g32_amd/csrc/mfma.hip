@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "mfma.h"
+#include "gemv.h"  // kMaxSplits
 
 #include <hip/hip_ext.h>
 #include "mfma_ops.h"
@@ -380,7 +381,140 @@ __device__ __forceinline__ void mma_tile_group(const uint4* buf, int gl, int lc,
   }
 }
 
-template <int P, int R, int kWaves>
+// The end of a tile task: the split-K sum (write-through partials, an
+// agent-scope arrival counter, and the last workgroup sums the partials in
+// split order), then the plain or SwiGLU output.  Every thread of the
+// workgroup calls it.
+template <int P, int kWaves, bool kDefer>
+__device__ __forceinline__ void tile_finish(const MfmaArgs& a, MfmaLds<P>& lds, int* last, f32x4 acc[4][4],
+                                            int item, int tile, int split, int pos0, int nrows, int wv, int lane,
+                                            int kb, bool wave_ok, int col0) {
+  if (kDefer) {
+    // deferred split-K: this split's sums
+    if (!wave_ok) return;
+    const int mat = a.mode == 1 ? wv >> 1 : 0;
+    float* base = a.planes + (static_cast<size_t>(split * (a.mode == 1 ? 2 : 1) + mat) * a.plane_rows + pos0) *
+                                 a.plane_ld + col0;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb * 16 + 4 * kb + i;
+        if (r < nrows) {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) base[static_cast<size_t>(r) * a.plane_ld + cb] = acc[rb][cb][i];
+        }
+      }
+    return;
+  }
+  // Split-K: write-through partials, an agent-scope arrival counter, and the
+  // last workgroup sums the partials in split order (the GEMV kernel's
+  // scheme, with the same reliance on gfx950's write-through agent-scope
+  // atomics in place of release/acquire ordering).  A partial tile is stored
+  // element-major, [j][thread] with j = (rb * 4 + cb) * 4 + i, so every store
+  // and load instruction covers 256 contiguous bytes, and the readback keeps
+  // two splits' worth (128 loads per thread) in flight at a time.
+  if (a.S > 1) {
+    const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
+    const size_t tf = static_cast<size_t>(kMfmaRows) * kMfmaCols;
+    float* base = a.partials + ct * a.S * tf + threadIdx.x;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kMfmaThreads, acc[rb][cb][i],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0)
+      *last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              a.S - 1);
+    __syncthreads();
+    if (!*last) return;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // partials in flight per round: two (128 loads per thread) at two waves
+    // per SIMD, one at three (its register budget)
+    constexpr int kB = kWaves >= 3 ? 1 : 2;
+    for (int s0 = 0; s0 < a.S; s0 += kB) {
+      float p[kB][64];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const float* ps = base + static_cast<size_t>(min(s0 + b, a.S - 1)) * tf;
+#pragma unroll
+        for (int e = 0; e < 64; ++e)
+          p[b][e] = __hip_atomic_load(ps + e * kMfmaThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        if (s0 + b < a.S) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[rb][cb][i] += p[b][(rb * 4 + cb) * 4 + i];
+        }
+      }
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  if (a.mode == 1) {
+    // The up waves hand their sums to the gate waves of the same columns
+    // through LDS (the window buffers are free now), element-major like the
+    // partial tiles.
+    float* xu = reinterpret_cast<float*>(&lds.a[0][0]);
+    static_assert(sizeof(MfmaLds<P>) >= 2 * 64 * 64 * sizeof(float), "the up sums must fit in the windows");
+    __syncthreads();  // every wave is done with the windows
+    if (wv >= 2) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xu[(((wv & 1) * 64 + (rb * 4 + cb) * 4 + i) << 6) + lane] = acc[rb][cb][i];
+    }
+    __syncthreads();
+    if (wv >= 2 || !wave_ok) return;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb * 16 + 4 * kb + i;
+        if (r < nrows) {
+          const size_t prow = static_cast<size_t>(pos0 + r);
+          const float f = a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const float up = xu[(((wv & 1) * 64 + (rb * 4 + cb) * 4 + i) << 6) + lane];
+            a.h[prow * a.N + col0 + cb] = silu(acc[rb][cb][i] * f) * (up * f);
+          }
+        }
+      }
+    return;
+  }
+  if (!wave_ok) return;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rb * 16 + 4 * kb + i;
+      if (r < nrows) {
+        const size_t prow = static_cast<size_t>(pos0 + r);
+        const float f = a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) a.out[prow * a.N + col0 + cb] = acc[rb][cb][i] * f;
+      }
+    }
+}
+
+template <int P, int R, int kWaves, bool kDefer = false>
 __global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(kWaves, kWaves)))
 void mfma_kernel(const MfmaArgs a) {
   __shared__ MfmaLds<P> lds;
@@ -518,114 +652,138 @@ void mfma_kernel(const MfmaArgs a) {
         for (int i = 0; i < 4; ++i) acc[rb][cb][i] = ldexpf(acc[rb][cb][i], -cexp[cb]);
   }
 
-  // Split-K: write-through partials, an agent-scope arrival counter, and the
-  // last workgroup sums the partials in split order (the GEMV kernel's
-  // scheme, with the same reliance on gfx950's write-through agent-scope
-  // atomics in place of release/acquire ordering).  A partial tile is stored
-  // element-major, [j][thread] with j = (rb * 4 + cb) * 4 + i, so every store
-  // and load instruction covers 256 contiguous bytes, and the readback keeps
-  // two splits' worth (128 loads per thread) in flight at a time.
-  if (a.S > 1) {
-    const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
-    const size_t tf = static_cast<size_t>(kMfmaRows) * kMfmaCols;
-    float* base = a.partials + ct * a.S * tf + threadIdx.x;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kMfmaThreads, acc[rb][cb][i],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
-    __syncthreads();
-    if (threadIdx.x == 0)
-      last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              a.S - 1);
-    __syncthreads();
-    if (!last) return;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // partials in flight per round: two (128 loads per thread) at two waves
-    // per SIMD, one at three (its register budget)
-    constexpr int kB = kWaves >= 3 ? 1 : 2;
-    for (int s0 = 0; s0 < a.S; s0 += kB) {
-      float p[kB][64];
-#pragma unroll
-      for (int b = 0; b < kB; ++b) {
-        const float* ps = base + static_cast<size_t>(min(s0 + b, a.S - 1)) * tf;
-#pragma unroll
-        for (int e = 0; e < 64; ++e)
-          p[b][e] = __hip_atomic_load(ps + e * kMfmaThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int b = 0; b < kB; ++b) {
-        if (s0 + b < a.S) {
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[rb][cb][i] += p[b][(rb * 4 + cb) * 4 + i];
-        }
-      }
-    }
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  tile_finish<P, kWaves, kDefer>(a, lds, &last, acc, item, tile, split, pos0, nrows, wv, lane, kb, wave_ok, col0);
+}
 
-  if (a.mode == 1) {
-    // The up waves hand their sums to the gate waves of the same columns
-    // through LDS (the window buffers are free now), element-major like the
-    // partial tiles.
-    float* xu = reinterpret_cast<float*>(&lds.a[0][0]);
-    static_assert(sizeof(MfmaLds<P>) >= 2 * 64 * 64 * sizeof(float), "the up sums must fit in the windows");
-    __syncthreads();  // every wave is done with the windows
-    if (wv >= 2) {
+// ------------------------------------------------------- deferred split-K
+
+// out[m][n..n+3] = (sum of the split planes, split order) * rs[m]: one thread
+// per four columns, every split's load in flight before the sum.
+__global__ __launch_bounds__(256) void plane_sum_kernel(const float* __restrict__ planes, int S, int plane_rows,
+                                                        int plane_ld, const float* __restrict__ rs, int M, int N,
+                                                        float* __restrict__ out) {
+  const int n4 = N / 4;
+  const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<size_t>(M) * n4) return;
+  const int m = static_cast<int>(idx / n4), n = static_cast<int>(idx % n4) * 4;
+  const size_t sstride = static_cast<size_t>(plane_rows) * plane_ld;
+  const float* p = planes + static_cast<size_t>(m) * plane_ld + n;
+  f32x4 v[kMaxSplits];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < S) v[s] = *reinterpret_cast<const f32x4*>(p + s * sstride);
+  f32x4 t = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) xu[(((wv & 1) * 64 + (rb * 4 + cb) * 4 + i) << 6) + lane] = acc[rb][cb][i];
-    }
-    __syncthreads();
-    if (wv >= 2 || !wave_ok) return;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < S) t += v[s];
+  const float f = rs[m];
+  *reinterpret_cast<f32x4*>(out + static_cast<size_t>(m) * N + n) = t * f;
+}
+
+// The pieces of h from the gate/up split planes, one workgroup per row:
+// pass 1 sums the splits in order, forms h = silu(g * f) * (u * f), stores
+// it to h and takes the row's largest magnitude; pass 2 reads the row back
+// and writes its pieces (as mfma_prep_kernel).
+template <int P>
+__global__ __launch_bounds__(kPrepThreads) void prep_planes_kernel(const float* __restrict__ planes, int S,
+                                                                   int plane_rows, int plane_ld,
+                                                                   const float* __restrict__ rsx, int M, int Mp,
+                                                                   int I, float* __restrict__ h,
+                                                                   _Float16* __restrict__ ap,
+                                                                   float* __restrict__ rs) {
+  __shared__ float red[kPrepThreads / kWave];
+  const int row = blockIdx.x;
+  const int nb = I / 8;
+  float amax = 0.0f;
+  const size_t sstride = static_cast<size_t>(2) * plane_rows * plane_ld;  // one split: gate plane + up plane
+  float* hr = h + static_cast<size_t>(row < M ? row : 0) * I;
+  if (row < M) {
+    const float f = rsx[row];
+    const float* gp = planes + static_cast<size_t>(row) * plane_ld;
+    const float* up = gp + static_cast<size_t>(plane_rows) * plane_ld;
+    for (int b = threadIdx.x; b < nb; b += kPrepThreads) {
+      f32x4 g0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, g1 = g0, u0 = g0, u1 = g0;
+      for (int s = 0; s < S; ++s) {
+        const size_t o = s * sstride + 8 * static_cast<size_t>(b);
+        g0 += *reinterpret_cast<const f32x4*>(gp + o);
+        g1 += *reinterpret_cast<const f32x4*>(gp + o + 4);
+        u0 += *reinterpret_cast<const f32x4*>(up + o);
+        u1 += *reinterpret_cast<const f32x4*>(up + o + 4);
+      }
+      f32x4 h0, h1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = rb * 16 + 4 * kb + i;
-        if (r < nrows) {
-          const size_t prow = static_cast<size_t>(pos0 + r);
-          const float f = a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow];
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb) {
-            const float up = xu[(((wv & 1) * 64 + (rb * 4 + cb) * 4 + i) << 6) + lane];
-            a.h[prow * a.N + col0 + cb] = silu(acc[rb][cb][i] * f) * (up * f);
-          }
-        }
+        h0[i] = silu(g0[i] * f) * (u0[i] * f);
+        h1[i] = silu(g1[i] * f) * (u1[i] * f);
+        amax = fmaxf(amax, fmaxf(fabsf(h0[i]), fabsf(h1[i])));
       }
-    return;
-  }
-  if (!wave_ok) return;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rb * 16 + 4 * kb + i;
-      if (r < nrows) {
-        const size_t prow = static_cast<size_t>(pos0 + r);
-        const float f = a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) a.out[prow * a.N + col0 + cb] = acc[rb][cb][i] * f;
-      }
+      *reinterpret_cast<f32x4*>(hr + 8 * b) = h0;
+      *reinterpret_cast<f32x4*>(hr + 8 * b + 4) = h1;
     }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if (lane_id() == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();  // (also orders this workgroup's h stores before pass 2 reads them)
+  amax = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kPrepThreads / kWave; ++w) amax = fmaxf(amax, red[w]);
+  int e = 0;
+  if (amax > 0.0f) {
+    int lg = ilogbf(amax);
+    lg = lg > 120 ? 120 : (lg < -120 ? -120 : lg);
+    e = 14 - lg;
+  }
+  const float scale = (row < M && amax > 0.0f) ? ldexpf(1.0f, e) : 0.0f;
+  if (threadIdx.x == 0) rs[row] = scale > 0.0f ? ldexpf(1.0f, -e) : 0.0f;
+  for (int b = threadIdx.x; b < nb; b += kPrepThreads) {
+    float v[8];
+    if (scale != 0.0f) {
+      load8<float>(hr, b, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    half8 h0, h1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float t = v[kCodeOrder[i]] * scale;
+      const _Float16 hi = static_cast<_Float16>(t);
+      h0[i] = hi;
+      if (P == 2) h1[i] = static_cast<_Float16>(t - static_cast<float>(hi));
+    }
+    *reinterpret_cast<half8*>(ap + static_cast<size_t>(row) * I + 8 * b) = h0;
+    if (P == 2) *reinterpret_cast<half8*>(ap + (static_cast<size_t>(Mp) + row) * I + 8 * b) = h1;
+  }
 }
 
 }  // namespace
+
+w4a16_status_t launch_plane_sum(const float* planes, int S, int plane_rows, int plane_ld, const float* rs, int M,
+                                int N, float* out, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (M == 0 || N == 0) return W4A16_OK;
+  if (S < 1 || S > kMaxSplits || N % 4 != 0 || plane_ld < N || plane_rows < M) return W4A16_ERR_INVALID_ARG;
+  const size_t n = static_cast<size_t>(M) * (N / 4);
+  const size_t blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
+  hipExtLaunchKernelGGL(plane_sum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, start, stop,
+                        0, planes, S, plane_rows, plane_ld, rs, M, N, out);
+  return launch_status();
+}
+
+w4a16_status_t launch_prep_planes(const float* planes, int S, int plane_rows, int plane_ld, const float* rsx,
+                                  int M, int Mp, int I, int P, float* h, _Float16* ap, float* rs,
+                                  hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (Mp == 0) return W4A16_OK;
+  if (S < 1 || I % 8 != 0 || plane_ld < I || plane_rows < M || Mp < M) return W4A16_ERR_INVALID_ARG;
+  if (P == 2)
+    hipExtLaunchKernelGGL(prep_planes_kernel<2>, dim3(Mp), dim3(kPrepThreads), 0, stream, start, stop, 0, planes,
+                          S, plane_rows, plane_ld, rsx, M, Mp, I, h, ap, rs);
+  else
+    hipExtLaunchKernelGGL(prep_planes_kernel<1>, dim3(Mp), dim3(kPrepThreads), 0, stream, start, stop, 0, planes,
+                          S, plane_rows, plane_ld, rsx, M, Mp, I, h, ap, rs);
+  return launch_status();
+}
 
 w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, int K, int P,
                                 const int* gather, int top_k, const int* need, _Float16* ap,
@@ -659,7 +817,10 @@ w4a16_status_t launch_mfma_prep(const void* x, w4a16_dtype_t xt, int R, int Mp, 
 
 namespace {
 void launch_one_piece(const MfmaArgs& a, unsigned grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  if (a.dense_rows > 0)
+  if (a.dense_rows > 0 && a.planes != nullptr && a.S > 1)
+    hipExtLaunchKernelGGL((mfma_kernel<1, kTileRing, 2, true>), dim3(grid), dim3(kMfmaThreads), 0, stream, start,
+                          stop, 0, a);
+  else if (a.dense_rows > 0)
     hipExtLaunchKernelGGL(mfma_kernel<1, kTileRing, 2>, dim3(grid), dim3(kMfmaThreads), 0, stream, start, stop,
                           0, a);
   else
@@ -675,7 +836,11 @@ w4a16_status_t launch_mfma(const MfmaArgs& a, int P, size_t num_tasks, hipStream
   // a split's codes must stay within the kernel's 32-bit buffer offsets
   if (static_cast<size_t>(a.gps) * a.N * 16 > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   const unsigned grid = static_cast<unsigned>(num_tasks);
-  if (P == 2)
+  if (a.planes != nullptr && a.S > 1 && a.dense_rows <= 0) return W4A16_ERR_INVALID_ARG;  // dense rows only
+  if (P == 2 && a.planes != nullptr && a.S > 1)
+    hipExtLaunchKernelGGL((mfma_kernel<2, kTileRing, 2, true>), dim3(grid), dim3(kMfmaThreads), 0, stream, start,
+                          stop, 0, a);
+  else if (P == 2)
     hipExtLaunchKernelGGL(mfma_kernel<2, kTileRing, 2>, dim3(grid), dim3(kMfmaThreads), 0, stream, start, stop,
                           0, a);
   else
