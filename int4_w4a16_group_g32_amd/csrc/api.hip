@@ -58,8 +58,8 @@ MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt, bool allo
   // two workgroups per CU (its registers allow two waves per SIMD), 512 on
   // the chip, and every workgroup of a launch streams the same number of
   // groups, so a launch takes about ceil(tasks * S / 512) rounds of
-  // (G / S + a fixed per-workgroup cost) group steps.  The partial tiles'
-  // write + read traffic stays under half the weight bytes.
+  // (G / S + a fixed per-workgroup cost) group steps.  The split sums' write
+  // + read traffic stays under the weight bytes.
   const double wbytes_per_col = K * 0.625;
   const double part_per_col_per_split = 8.0 * static_cast<double>(m.items) * kMfmaRows;
   int s_max = static_cast<int>(W4_MFMA_PARTIAL_CAP * wbytes_per_col / part_per_col_per_split);

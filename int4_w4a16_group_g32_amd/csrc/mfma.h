@@ -18,13 +18,14 @@ constexpr int kMfmaRows = 64;     // rows per tile
 constexpr int kMfmaCols = 256;    // weight columns per tile (4 waves x 4 blocks of 16)
 constexpr int kMfmaThreads = 256;
 // Workgroups of the tile kernel resident at once (two per CU on 256 CUs) and
-// the fixed cost of one workgroup (staging, split-K tail, epilogue) in units
-// of one group step; the split planner balances launches with them.
+// the fixed cost of one workgroup (staging, the store of its 64 KiB of split
+// sums and their later read, epilogue) in units of one group step (about 5 KiB
+// of weights); the split planner balances launches with them.
 #ifndef W4_MFMA_WG_OVERHEAD_GROUPS
-#define W4_MFMA_WG_OVERHEAD_GROUPS 4
+#define W4_MFMA_WG_OVERHEAD_GROUPS 16
 #endif
 #ifndef W4_MFMA_PARTIAL_CAP
-#define W4_MFMA_PARTIAL_CAP 0.5  // partial-tile traffic cap, a fraction of the weight bytes
+#define W4_MFMA_PARTIAL_CAP 1.0  // split-sum traffic cap, a fraction of the weight bytes
 #endif
 constexpr int kMfmaResidentWgs = 512;
 
