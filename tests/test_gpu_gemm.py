@@ -318,3 +318,22 @@ def test_gemv_running_power_of_two_across_windows(pattern, dtype):
     err = rel_err(y, O.gemm64(x_values(x), qw, sc))
     print(f"gemv running 2^e {pattern} {dtype} relF={err:.3e}", flush=True)
     assert err <= tol_for(dtype)
+
+
+# The 64-row tiles split K across workgroups when the row and column tiles are
+# few; each split stores its sums to split planes and a last kernel adds the
+# splits in order.  Ragged row counts (the last item's rows past M are never
+# stored), both piece counts.
+@pytest.mark.parametrize("M,dtype", [(17, "bf16"), (40, "f32"), (100, "bf16"), (130, "f32")])
+def test_gemm_tiles_split_k_ragged_rows(M, dtype):
+    K, N = 7168, 1024
+    qw, sc = _random_codes(K, N, 900 + M)
+    w = weight_from_codes(qw, sc)
+    x = x_for_dtype(W.activations(M, K, 901 + M).cuda(), dtype)
+    y, _ = _run_gemm(x, w, N)
+    ref = O.gemm64(x_values(x), qw, sc)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, gemm_bound(x_values(x), qw, sc, TAU[dtype]),
+                              f"split tiles M={M} {dtype}")
+    print(f"split tiles M={M} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
+    assert err <= tol_for(dtype)

@@ -111,13 +111,19 @@ def test_mlp_full_size(dense_mlp, name, dtype):
     assert np.array_equal(qd, _sampled_down(w_down, cols)[0])
 
 
-@pytest.mark.parametrize("M,dtype,kernels", [(4, "f32", 2), (100, "bf16", 4)])
-def test_mlp_timed_brackets_each_kernel(M, dtype, kernels):
+@pytest.mark.parametrize("M,dtype,H,I,kernels", [(4, "f32", 256, 512, 2), (100, "bf16", 256, 512, 4),
+                                                 (64, "bf16", 2048, 4096, 5), (40, "f32", 2048, 4096, 5)])
+def test_mlp_timed_brackets_each_kernel(M, dtype, H, I, kernels):
     """w4a16_swiglu_mlp_timed does the same work as w4a16_swiglu_mlp (same
-    output bits) and brackets each of its kernels with a start and a stop event."""
+    output bits) and brackets each of its kernels with a start and a stop
+    event.  From M = 9 (float32) or 17 (bf16): the activation pieces, the
+    gate/up tiles, the pieces of h and the down tiles; with K split across
+    workgroups (hidden 2048, intermediate 4096) the pieces of h are formed
+    from the gate/up split sums and a fifth kernel adds the down projection's
+    splits."""
     import ctypes
 
-    H, I, cfg = 256, 512, 470
+    cfg = 470
     codes = [O.quantize_w4a16(w.numpy()) for w in (W.weights(H, I, cfg, W.TAG_GATE), W.weights(H, I, cfg, W.TAG_UP),
                                                    W.weights(I, H, cfg, W.TAG_DOWN))]
     g, u, d = (weight_from_codes(*c) for c in codes)
@@ -126,21 +132,23 @@ def test_mlp_timed_brackets_each_kernel(M, dtype, kernels):
     xt = L.F32 if dtype == "f32" else L.BF16
     ws = L.new_workspace(L.swiglu_mlp_workspace_bytes(M, xt, g, u, d))
     y = torch.full((M, H), float("nan"), dtype=torch.float32, device="cuda")
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
     for e in evs:  # torch creates the HIP event on its first record
         e.record()
     torch.cuda.synchronize()
-    handles = (ctypes.c_void_p * 8)(*[e.cuda_event for e in evs])
+    handles = (ctypes.c_void_p * 10)(*[e.cuda_event for e in evs])
     rec = ctypes.c_int32(-1)
     lib = L.load_library()
     st = lib.w4a16_swiglu_mlp_timed(L._ptr(x), xt, M, ctypes.byref(g.desc()), ctypes.byref(u.desc()),
                                     ctypes.byref(d.desc()), L._ptr(y), L._ptr(ws), ws.numel(),
-                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), handles, 8,
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), handles, 10,
                                     ctypes.byref(rec))
     assert st == 0
     torch.cuda.synchronize()
     assert rec.value == 2 * kernels
     assert torch.equal(y, y_plain)
+    ref = O.swiglu_mlp64(x_values(x), *codes)
+    assert rel_err(y, ref) <= tol_for(dtype)
     for j in range(kernels):
         assert evs[2 * j].elapsed_time(evs[2 * j + 1]) > 0.0
         if j > 0:  # kernels run in launch order on the stream
