@@ -12,13 +12,18 @@
 // scales over all of K and puts the largest in [1/2, 1), so no product can
 // leave the f16 range and no accumulator ever needs rescaling.
 //
-// A workgroup computes 256 rows x 128 columns.  Wave (wr, wc) = (wv >> 1,
-// wv & 1) owns rows 128wr .. +127 and columns 64wc .. +63: 8 x 4 MFMA blocks
-// of 16 x 16, so every expanded weight feeds 8 MFMAs, twice the 64-row tile's
-// reuse, and the vector work per matrix-core instruction halves.  The 256 x 64
-// activation window (two groups) is staged once in LDS and read by the two
-// waves of each row half; each wave streams its own 64 columns of codes, one
-// 16-byte GROUPED slot per lane and group.
+// A workgroup computes 256 rows x 128 columns with eight waves, two per SIMD:
+// wave (kh, wr, wc) = (wv >> 2, (wv >> 1) & 1, wv & 1) owns rows 128wr ..
+// +127 and columns 64wc .. +63, and the K half kh: of each window's two
+// groups it takes group kh.  Per group a wave runs 8 x 4 MFMA blocks of
+// 16 x 16, so every expanded weight feeds 8 MFMAs, twice the 64-row tile's
+// reuse, and the vector work per matrix-core instruction halves.  The
+// 256 x 64 activation window (two groups) is staged once in LDS; each wave
+// streams its own 64 columns of codes of its own groups, one 16-byte GROUPED
+// slot per lane and group.  After the loop the second K half's sums are added
+// to the first half's through LDS, in that order.  (With one wave per SIMD and
+// every wave on both groups of a window, the 2048 x 7168 x 4096 GEMM took
+// 138-142 against 133 us here.)
 //
 // Workgroups are numbered so that each XCD (the hardware deals workgroup b to
 // XCD b mod 8) takes a contiguous run of tiles, row tile major: the column
@@ -33,13 +38,15 @@
 namespace w4 {
 namespace {
 
-constexpr int kWw = 2;                                     // groups per staged activation window
-constexpr int kWideRing = 2 * kWw;                         // groups of codes in flight per wave
+constexpr int kWw = 2;                                     // groups per staged activation window (one per K half)
+constexpr int kWideWgThreads = 2 * kWideThreads;           // two K halves of four waves
+constexpr int kWideRing = 2;                               // own groups of codes in flight per wave (two windows)
 constexpr int kWideWinUnits = kWw * kWideRows * 4;         // 16-byte units per window
-constexpr int kWideUnitsPerThread = kWideWinUnits / kWideThreads;
-constexpr int kAnchorBatch = 16;                           // scale loads in flight per thread
+constexpr int kWideUnitsPerThread = kWideWinUnits / kWideWgThreads;
+constexpr int kAnchorBatch = 8;                            // scale loads in flight per thread
+constexpr int kAnchorPhases = kWideWgThreads / 32;         // scale rows read at once (32 column quads)
 constexpr int kXcds = 8;
-constexpr int kAhead = 3;                                  // A fragments read ahead of their MFMAs
+constexpr int kAhead = 1;                                  // A fragments read ahead of their MFMAs
 
 // Raw buffer resources: a wave-uniform base and size in scalar registers, so a
 // load takes one 32-bit lane offset and a scalar offset (no 64-bit address
@@ -65,34 +72,40 @@ __device__ __forceinline__ int w_off(int gl, int row, int kb) {
 
 struct WideLds {
   uint4 a[2][kWideWinUnits];  // double buffer, 2 x 32 KiB
-  float red[8][kWideCols];    // anchor reduction
+  float red[kAnchorPhases][kWideCols];  // anchor reduction
   int cexp[kWideCols];
   int last;
 };
 
-// Staging: thread t handles units u = t + 256 i, k block u & 3, row
+// Staging: thread t handles units u = t + 512 i, k block u & 3, row
 // 8 (u >> 6) + ((u >> 2) & 7), group (u >> 5) & 1: each 8 lanes two rows of
 // one group, each wave 8 rows x both groups.  The lane offset holds t's row,
-// group and k block; the scalar offset the window's first group and 32 i
+// group and k block; the scalar offset the window's first group and 64 i
 // rows.  The prefetch after a split's last window reads the next split's
 // activations, or past the end of the row (at most 128 bytes past the last
 // row of the plane, which the workspace pads), and is never used.
 __device__ __forceinline__ int stage_row(int u) { return 8 * (u >> 6) + ((u >> 2) & 7); }
 
-__device__ __forceinline__ void wide_load_a(__amdgpu_buffer_rsrc_t ra_src, int voff, int K, int gw,
-                                            uint4 r[kWideUnitsPerThread]) {
+// A window is staged in two halves of kHalfUnits units per thread, so that
+// only one half is held in registers at a time.
+constexpr int kHalfUnits = kWideUnitsPerThread / 2;
+__device__ __forceinline__ void wide_load_a(__amdgpu_buffer_rsrc_t ra_src, int voff, int K, int gw, int hf,
+                                            uint4 r[kHalfUnits]) {
 #pragma unroll
-  for (int i = 0; i < kWideUnitsPerThread; ++i)
-    r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, voff, (gw * kGroup + 32 * i * K) * 2, 0));
+  for (int j = 0; j < kHalfUnits; ++j) {
+    const int i = hf * kHalfUnits + j;
+    r[j] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, voff, (gw * kGroup + kWideWgThreads / 8 * i * K) * 2, 0));
+  }
 }
 
 // Every split holds an even number of groups (the launch checks it), so a
 // window is always whole.
-__device__ __forceinline__ void wide_store_a(uint4* buf, const uint4 r[kWideUnitsPerThread]) {
+__device__ __forceinline__ void wide_store_a(uint4* buf, int hf, const uint4 r[kHalfUnits]) {
 #pragma unroll
-  for (int i = 0; i < kWideUnitsPerThread; ++i) {
-    const int u = static_cast<int>(threadIdx.x) + kWideThreads * i;
-    buf[w_off((u >> 5) & 1, stage_row(u), u & 3)] = r[i];
+  for (int j = 0; j < kHalfUnits; ++j) {
+    const int u = static_cast<int>(threadIdx.x) + kWideWgThreads * (hf * kHalfUnits + j);
+    buf[w_off((u >> 5) & 1, stage_row(u), u & 3)] = r[j];
   }
 }
 
@@ -159,7 +172,7 @@ __device__ __forceinline__ void expand_step(uint32_t w, float s, int ce, uint32_
   }
 }
 
-__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kWideWgThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void wide_kernel(const MfmaArgs a) {
   __shared__ WideLds lds;
   const int t = static_cast<int>(threadIdx.x);
@@ -176,10 +189,10 @@ void wide_kernel(const MfmaArgs a) {
   const int item = rest / a.tiles;
   const int row0 = item * kWideRows;
 
-  const int wv = wave_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const int lane = lane_id();
   const int lc = lane & 15, kb = lane >> 4;
-  const int wr = wv >> 1, wc = wv & 1;
+  const int kh = wv >> 2, wr = (wv >> 1) & 1, wc = wv & 1;  // K half, row half, column half
   const uint32_t magic = magic_vgpr();
 
   const int c0 = tile * kWideCols + wc * 64;
@@ -196,18 +209,20 @@ void wide_kernel(const MfmaArgs a) {
   const int g_lo = split * a.gps;
   const int g_hi = min(a.G, g_lo + a.gps);
   const int nwin = (g_hi - g_lo + kWw - 1) / kWw;
+  // this wave's own groups: g_lo + kh + kWw * j, one per window
+  auto own = [&](int j) { return g_lo + kh + kWw * j; };
 
-  uint4 ra[kWideUnitsPerThread];
-  WideCodes ring[kWideRing];
-  wide_load_a(asrc, avoff, a.K, g_lo, ra);
+  uint4 ra[kHalfUnits];
+  WideCodes ring[kWideRing];  // own group j sits in slot j % kWideRing
+  wide_load_a(asrc, avoff, a.K, g_lo, 0, ra);
 #pragma unroll
   for (int j = 0; j < kWideRing; ++j) {
-    wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, g_lo + j, a.G - 1, a.gshift, ring[j]);
+    wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, own(j), a.G - 1, a.gshift, ring[j]);
     __builtin_amdgcn_sched_barrier(0);  // issue order = use order
   }
 
   // Column anchors over every scale row of K: thread t reads columns
-  // 4(t & 31) .. +3 of the tile at scale rows t >> 5, + 8, ... (rows past the
+  // 4(t & 31) .. +3 of the tile at scale rows t >> 5, + 16, ... (rows past the
   // end are clamped to the last one; a repeated row leaves a maximum as it is).
   {
     const int cq = t & 31, r0 = t >> 5;
@@ -215,13 +230,12 @@ void wide_kernel(const MfmaArgs a) {
     const int ccl = ccol < a.N ? ccol : 0;
     const int rows = a.G >> a.gshift;
     f32x4 mx = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int r = r0; r < rows; r += 8 * kAnchorBatch) {
+    for (int r = r0; r < rows; r += kAnchorPhases * kAnchorBatch) {
       f32x4 v[kAnchorBatch];
-      // rows past the end are clamped to the last one, which leaves a maximum as it is
 #pragma unroll
       for (int j = 0; j < kAnchorBatch; ++j)
         v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             ssrc, (min(r + 8 * j, rows - 1) * a.N + ccl) * 4, 0, 0));
+                                             ssrc, (min(r + kAnchorPhases * j, rows - 1) * a.N + ccl) * 4, 0, 0));
 #pragma unroll
       for (int j = 0; j < kAnchorBatch; ++j)
 #pragma unroll
@@ -233,11 +247,13 @@ void wide_kernel(const MfmaArgs a) {
     if (t < kWideCols) {
       float m = lds.red[0][t];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) m = fmaxf(m, lds.red[j][t]);
+      for (int j = 1; j < kAnchorPhases; ++j) m = fmaxf(m, lds.red[j][t]);
       lds.cexp[t] = m > 0.0f ? -__builtin_amdgcn_frexp_expf(m) : 0;
     }
   }
-  wide_store_a(lds.a[0], ra);
+  wide_store_a(lds.a[0], 0, ra);
+  wide_load_a(asrc, avoff, a.K, g_lo, 1, ra);
+  wide_store_a(lds.a[0], 1, ra);
   __syncthreads();
   int cexp[4];
 #pragma unroll
@@ -249,15 +265,15 @@ void wide_kernel(const MfmaArgs a) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Window wi uses LDS buffer and ring half h = wi % 2; the loop body is two
-  // whole windows and an odd last window runs after it, so every path into
-  // the loop header has the same loads outstanding.  A window is a run of 16
-  // row-block steps (two groups x 8 row blocks), each one A fragment read
-  // (kAhead steps ahead) and 4 MFMAs; between the MFMAs run the steps of the
-  // next group's expansion (its codes are consumed one group early, and the
-  // slot is refilled with group g + kWideRing when the group ends).  The
-  // schedule is pinned with scheduling barriers.
-  half8 bq[2][4];  // expanded weights, by group parity (the loop body holds an even number of groups)
+  // Window wi uses LDS buffer h = wi % 2 and this wave's own group wi (ring
+  // slot wi % 2); the loop body is two whole windows and an odd last window
+  // runs after it, so every path into the loop header has the same loads
+  // outstanding.  A window is a run of 8 row-block steps, each one A fragment
+  // read (kAhead steps ahead) and 4 MFMAs; between the MFMAs run the steps of
+  // the expansion of the wave's next own group, whose slot is then refilled
+  // with own group wi + 1 + kWideRing.  The schedule is pinned with
+  // scheduling barriers.
+  half8 bq[2][4];  // expanded weights, by window parity
   {
     WordExp e;
 #pragma unroll
@@ -272,58 +288,58 @@ void wide_kernel(const MfmaArgs a) {
       expand_step<7>(ring[0].w[cb], ring[0].s[cb], cexp[cb], magic, e, bq[0][cb]);
     }
   }
-  wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, g_lo + kWideRing, a.G - 1, a.gshift, ring[0]);
+  wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, own(kWideRing), a.G - 1, a.gshift, ring[0]);
   // the accumulators were just written by vector instructions: pad before
   // the first (opaque) MFMA reads them
   asm volatile("s_nop 7\n\ts_nop 7");
   auto window = [&](int wi, auto hc) {
     constexpr int h = decltype(hc)::value;
     const int gw = g_lo + wi * kWw;
-    wide_load_a(asrc, avoff, a.K, gw + kWw, ra);  // the next window, in flight
+    wide_load_a(asrc, avoff, a.K, gw + kWw, 0, ra);  // the next window's first half, in flight
     const uint4* buf = lds.a[h];
     auto rd = [&](int st) {
-      return __builtin_bit_cast(half8, buf[w_off(st >> 3, wr * 128 + (st & 7) * 16 + lc, kb)]);
+      return __builtin_bit_cast(half8, buf[w_off(kh, wr * 128 + st * 16 + lc, kb)]);
     };
     half8 af[4];
 #pragma unroll
     for (int st = 0; st < kAhead; ++st) af[st] = rd(st);
     __builtin_amdgcn_sched_barrier(0);
+    static_assert(2 % kWideRing == 0, "ring slots repeat with the loop body");
+    constexpr int cur = h;                      // this window's expanded weights
+    constexpr int nslot = (h + 1) % kWideRing;  // ring slot of the next own group
+    WordExp e;
 #pragma unroll
-    for (int j = 0; j < kWw; ++j) {
-      constexpr int kBody = 2 * kWw;  // groups per loop body
-      const int cur = (kWw * h + j) & 1;
-      const int nslot = (kWw * h + j + 1) % kWideRing;
-      static_assert(kBody % kWideRing == 0, "ring slots repeat with the loop body");
-      WordExp e;
-#pragma unroll
-      for (int rb = 0; rb < 8; ++rb) {
-        const int st = 8 * j + rb;
-        if (st + kAhead < 8 * kWw) af[(st + kAhead) & 3] = rd(st + kAhead);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          mfma_tied(acc[rb][cb], af[st & 3], bq[cur][cb]);
-          // expansion step (rb * 4 + cb) % 8 of word (rb * 4 + cb) / 8
-          const int x = rb * 4 + cb, word = x >> 3;
-          const uint32_t wd = ring[nslot].w[word];
-          const float sc = ring[nslot].s[word];
-          half8& o = bq[cur ^ 1][word];
-          switch (x & 7) {
-            case 0: expand_step<0>(wd, sc, cexp[word], magic, e, o); break;
-            case 1: expand_step<1>(wd, sc, cexp[word], magic, e, o); break;
-            case 2: expand_step<2>(wd, sc, cexp[word], magic, e, o); break;
-            case 3: expand_step<3>(wd, sc, cexp[word], magic, e, o); break;
-            case 4: expand_step<4>(wd, sc, cexp[word], magic, e, o); break;
-            case 5: expand_step<5>(wd, sc, cexp[word], magic, e, o); break;
-            case 6: expand_step<6>(wd, sc, cexp[word], magic, e, o); break;
-            default: expand_step<7>(wd, sc, cexp[word], magic, e, o); break;
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
+    for (int rb = 0; rb < 8; ++rb) {
+      if (rb == 4) {  // the first half is in: store it (buffer 1 - h is free) and fetch the second
+        wide_store_a(lds.a[1 - h], 0, ra);
+        wide_load_a(asrc, avoff, a.K, gw + kWw, 1, ra);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, gw + j + 1 + kWideRing, a.G - 1, a.gshift, ring[nslot]);
-      __builtin_amdgcn_sched_barrier(0);
+      if (rb + kAhead < 8) af[(rb + kAhead) & 3] = rd(rb + kAhead);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        mfma_tied(acc[rb][cb], af[rb & 3], bq[cur][cb]);
+        // expansion step (rb * 4 + cb) % 8 of word (rb * 4 + cb) / 8
+        const int x = rb * 4 + cb, word = x >> 3;
+        const uint32_t wd = ring[nslot].w[word];
+        const float sc = ring[nslot].s[word];
+        half8& o = bq[cur ^ 1][word];
+        switch (x & 7) {
+          case 0: expand_step<0>(wd, sc, cexp[word], magic, e, o); break;
+          case 1: expand_step<1>(wd, sc, cexp[word], magic, e, o); break;
+          case 2: expand_step<2>(wd, sc, cexp[word], magic, e, o); break;
+          case 3: expand_step<3>(wd, sc, cexp[word], magic, e, o); break;
+          case 4: expand_step<4>(wd, sc, cexp[word], magic, e, o); break;
+          case 5: expand_step<5>(wd, sc, cexp[word], magic, e, o); break;
+          case 6: expand_step<6>(wd, sc, cexp[word], magic, e, o); break;
+          default: expand_step<7>(wd, sc, cexp[word], magic, e, o); break;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    wide_store_a(lds.a[1 - h], ra);
+    wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, own(wi + 1 + kWideRing), a.G - 1, a.gshift, ring[nslot]);
+    __builtin_amdgcn_sched_barrier(0);
+    wide_store_a(lds.a[1 - h], 1, ra);
     __syncthreads();
   };
   int w = 0;
@@ -335,29 +351,62 @@ void wide_kernel(const MfmaArgs a) {
   // the last (opaque) MFMAs' results are read by vector instructions below
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 
-  // Split-K: write-through partials [j][thread], j = (rb * 4 + cb) * 4 + i, an
-  // agent-scope arrival counter, and the last workgroup sums the partials in
-  // split order, 64 loads per thread in flight (the GEMV kernel's scheme and
-  // its reliance on gfx950's write-through agent-scope atomics).
+  // The two K halves meet in LDS (the window buffers are free after the loop's
+  // last barrier), one row half at a time: the second half's waves store
+  // their sums, the first half's add them, in that order.
+  {
+    float* red = reinterpret_cast<float*>(&lds.a[0][0]);
+    static_assert(sizeof(lds.a) >= 2 * 128 * 64 * sizeof(float), "a row half of sums must fit in the windows");
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (kh == 1 && wr == p) {
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[((wc * 128 + (rb * 4 + cb) * 4 + i) << 6) + lane] = acc[rb][cb][i];
+      }
+      __syncthreads();
+      if (kh == 0 && wr == p) {
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rb][cb][i] += red[((wc * 128 + (rb * 4 + cb) * 4 + i) << 6) + lane];
+      }
+      __syncthreads();
+    }
+  }
+
+  // Split-K across workgroups (first K half's threads t < kWideThreads hold
+  // the tile): write-through partials [j][thread], j = (rb * 4 + cb) * 4 + i,
+  // an agent-scope arrival counter, and the last workgroup sums the partials
+  // in split order, 32 loads per thread in flight (the GEMV kernel's scheme
+  // and its reliance on gfx950's write-through agent-scope atomics).  Every
+  // thread reaches the barriers.
   if (a.S > 1) {
     const size_t ct = static_cast<size_t>(item) * a.tiles + tile;
     const size_t tf = static_cast<size_t>(kWideRows) * kWideCols;
-    float* base = a.partials + ct * a.S * tf + t;
+    float* base = a.partials + ct * a.S * tf + (kh == 0 ? t : 0);
+    if (kh == 0) {
 #pragma unroll
-    for (int rb = 0; rb < 8; ++rb)
+      for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kWideThreads, acc[rb][cb][i],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(base + split * tf + ((rb * 4 + cb) * 4 + i) * kWideThreads, acc[rb][cb][i],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
     __syncthreads();
     if (t == 0)
       lds.last = (__hip_atomic_fetch_add(&a.counters[ct], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                   a.S - 1);
     __syncthreads();
-    if (!lds.last) return;
+    if (!lds.last || kh != 0) return;
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb)
 #pragma unroll
@@ -365,21 +414,21 @@ void wide_kernel(const MfmaArgs a) {
     for (int s = 0; s < a.S; ++s) {
       const float* ps = base + static_cast<size_t>(s) * tf;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float p[64];
+      for (int hh = 0; hh < 4; ++hh) {
+        float p[32];
 #pragma unroll
-        for (int e = 0; e < 64; ++e)
-          p[e] = __hip_atomic_load(ps + (hh * 64 + e) * kWideThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int e = 0; e < 32; ++e)
+          p[e] = __hip_atomic_load(ps + (hh * 32 + e) * kWideThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int e = 0; e < 64; ++e) {
-          const int j = hh * 64 + e;
+        for (int e = 0; e < 32; ++e) {
+          const int j = hh * 32 + e;
           acc[j >> 4][(j >> 2) & 3][j & 3] += p[e];
         }
       }
     }
     if (t == 0) __hip_atomic_store(&a.counters[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (!wave_ok) return;
+  if (!wave_ok || kh != 0) return;
 
   // lane (lc, kb) holds rows rb*16 + 4kb + i of columns col0 .. col0 + 3 (the
   // four column blocks): one 16-byte store per row
@@ -408,7 +457,7 @@ w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stre
   if (num_tasks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   if (a.mode != 0 || a.dense_rows <= 0 || a.Mp % kWideRows != 0 || a.G % kWw != 0 || a.gps % kWw != 0)
     return W4A16_ERR_UNSUPPORTED;
-  hipExtLaunchKernelGGL(wide_kernel, dim3(static_cast<unsigned>(num_tasks)), dim3(kWideThreads), 0, stream, start,
+  hipExtLaunchKernelGGL(wide_kernel, dim3(static_cast<unsigned>(num_tasks)), dim3(kWideWgThreads), 0, stream, start,
                         stop, 0, a);
   return launch_status();
 }
