@@ -35,6 +35,7 @@ inline int gemv_expert_rows(w4a16_dtype_t xt) {
 }
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kRouteLdsInts = 12288;  // 48 KiB: per-wave expert counts and totals
+constexpr int kRouteChunk = 8;       // 64-pair steps whose ids one wave loads together
 
 // Waves that place pairs for E experts: each keeps E counters in LDS, next to
 // one row of per-expert totals.
@@ -94,18 +95,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 
   for (int i = tid; i < (W + 1) * E; i += kRouteThreads) lds[i] = 0;
   __syncthreads();
+  // The keys of a wave's pairs are read kRouteChunk steps of 64 at a time,
+  // all loads in flight together, instead of one dependent load per step.
+  auto load_keys = [&](int c0, int p1, int key[kRouteChunk]) {
+#pragma unroll
+    for (int j = 0; j < kRouteChunk; ++j) {
+      const int p = c0 + j * kWave + lane;
+      const int e = p < p1 ? ids[p] : E;
+      key[j] = (e >= 0 && e < E) ? e : E;
+    }
+  };
   // A. per-wave counts
   if (wv < W) {
     const int p0 = wv * L, p1 = min(pairs, p0 + L);
-    for (int q = p0; q < p1; q += kWave) {
-      const int p = q + lane;
-      int key = E;
-      if (p < p1) {
-        const int e = ids[p];
-        if (e >= 0 && e < E) key = e;
+    for (int c0 = p0; c0 < p1; c0 += kRouteChunk * kWave) {
+      int key[kRouteChunk];
+      load_keys(c0, p1, key);
+#pragma unroll
+      for (int j = 0; j < kRouteChunk; ++j) {
+        if (c0 + j * kWave >= p1) break;  // (wave-uniform)
+        const uint64_t m = same_key_lanes(key[j], bits);
+        if ((m & below) == 0 && key[j] < E) wc[wv * E + key[j]] += __popcll(m);
       }
-      const uint64_t m = same_key_lanes(key, bits);
-      if ((m & below) == 0 && key < E) wc[wv * E + key] += __popcll(m);
     }
   }
   __syncthreads();
@@ -153,25 +164,26 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   // B. placement
   if (wv < W) {
     const int p0 = wv * L, p1 = min(pairs, p0 + L);
-    for (int q = p0; q < p1; q += kWave) {
-      const int p = q + lane;
-      int key = E;
-      if (p < p1) {
-        const int e = ids[p];
-        if (e >= 0 && e < E) key = e;
+    for (int c0 = p0; c0 < p1; c0 += kRouteChunk * kWave) {
+      int key[kRouteChunk];
+      load_keys(c0, p1, key);
+#pragma unroll
+      for (int j = 0; j < kRouteChunk; ++j) {
+        if (c0 + j * kWave >= p1) break;  // (wave-uniform)
+        const int p = c0 + j * kWave + lane;
+        const uint64_t m = same_key_lanes(key[j], bits);
+        if (key[j] < E) {
+          const int pos = wc[wv * E + key[j]] + __popcll(m & below);
+          sorted_pairs[pos] = p;
+          inv[p] = pos;
+          if (heavy != nullptr) heavy[pos] = counts[key[j]] > expert_rows ? 1 : 0;
+        } else if (p < p1) {
+          inv[p] = -1;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if ((m & below) == 0 && key[j] < E) wc[wv * E + key[j]] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
       }
-      const uint64_t m = same_key_lanes(key, bits);
-      if (key < E) {
-        const int pos = wc[wv * E + key] + __popcll(m & below);
-        sorted_pairs[pos] = p;
-        inv[p] = pos;
-        if (heavy != nullptr) heavy[pos] = counts[key] > expert_rows ? 1 : 0;
-      } else if (p < p1) {
-        inv[p] = -1;
-      }
-      __builtin_amdgcn_wave_barrier();
-      if ((m & below) == 0 && key < E) wc[wv * E + key] += __popcll(m);
-      __builtin_amdgcn_wave_barrier();
     }
   }
   // the shared expert's positions follow the routed pairs
