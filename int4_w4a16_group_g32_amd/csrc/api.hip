@@ -161,13 +161,16 @@ MlpPlan plan_mlp(int M, w4a16_dtype_t xt, const w4a16_weight_t* gate, const w4a1
     p.gu = plan_mfma(M, I, 1, H, xt, false);
     p.dn = plan_mfma(M, down->N, 0, I, xt, false);
     const int P = p.gu.P, Mp = p.gu.Mp;
+    // Both launches split K: h's pieces are made per down split, from the
+    // gate/up split sums, and h itself is never stored.
+    p.split_pieces = p.gu.S > 1 && p.dn.S > 1 && split_pieces_threads(p.dn.gps * kGroup) > 0;
     Carve c;
     c.take(p.counters_off, kCounterBytes);
     c.take(p.apx_off, static_cast<size_t>(P) * Mp * H * 2);
     c.take(p.rsx_off, static_cast<size_t>(Mp) * 4);
-    c.take(p.h_off, static_cast<size_t>(Mp) * I * 4);
+    c.take(p.h_off, p.split_pieces ? 0 : static_cast<size_t>(Mp) * I * 4);
     c.take(p.aph_off, static_cast<size_t>(P) * Mp * I * 2);
-    c.take(p.rsh_off, static_cast<size_t>(Mp) * 4);
+    c.take(p.rsh_off, static_cast<size_t>(Mp) * (p.split_pieces ? p.dn.S : 1) * 4);
     c.take(p.partials_off, std::max(mfma_partial_bytes(p.gu), mfma_partial_bytes(p.dn)));
     p.bytes = c.cursor;
     return p;
@@ -279,7 +282,7 @@ static w4a16_status_t gemm_impl(const void* x, w4a16_dtype_t xt, int32_t M, cons
     st = launch_mfma(a, p.mf.P, p.mf.tasks * p.mf.S, stream, b.start, b.stop);
     if (st != W4A16_OK) return st;
     b = ev.bracket();
-    return launch_plane_sum(a.planes, a.S, a.plane_rows, a.plane_ld, rs, M, w->N, y, stream, b.start, b.stop);
+    return launch_plane_sum(a.planes, a.S, a.plane_rows, a.plane_ld, rs, 0, M, w->N, y, stream, b.start, b.stop);
   }
   if (!counters_fit(p.tasks, p.S)) return W4A16_ERR_UNSUPPORTED;
   GemvArgs a = gemv_dense_args(M, w, nullptr, 0, x, xt == W4A16_BF16, gemv_pieces(xt), p.tiles, p.S, p.gps, wsb,
@@ -367,7 +370,10 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
     st = launch_mfma(a, p.gu.P, p.gu.tasks * p.gu.S, stream, b.start, b.stop);
     if (st != W4A16_OK) return st;
     b = ev.bracket();
-    if (p.gu.S > 1)  // h from the gate/up split sums, then its pieces
+    if (p.split_pieces)  // h's pieces per down split, from the gate/up split sums
+      st = launch_prep_split_pieces(a.planes, a.S, a.plane_rows, a.plane_ld, rsx, M, p.dn.Mp, I, p.dn.P,
+                                    p.dn.gps * kGroup, aph, rsh, stream, b.start, b.stop);
+    else if (p.gu.S > 1)  // h from the gate/up split sums, then its pieces
       st = launch_prep_planes(a.planes, a.S, a.plane_rows, a.plane_ld, rsx, M, p.dn.Mp, I, p.dn.P, h, aph, rsh,
                               stream, b.start, b.stop);
     else
@@ -383,7 +389,8 @@ static w4a16_status_t swiglu_mlp_impl(const void* x, w4a16_dtype_t xt, int32_t M
     st = launch_mfma(d, p.dn.P, p.dn.tasks * p.dn.S, stream, b.start, b.stop);
     if (st != W4A16_OK) return st;
     b = ev.bracket();
-    return launch_plane_sum(d.planes, d.S, d.plane_rows, d.plane_ld, rsh, M, down->N, y, stream, b.start, b.stop);
+    return launch_plane_sum(d.planes, d.S, d.plane_rows, d.plane_ld, rsh, p.split_pieces ? p.dn.Mp : 0, M, down->N,
+                            y, stream, b.start, b.stop);
   }
   if (!counters_fit(p.tasks_gu, p.S_gu) || !counters_fit(p.tasks_d, p.S_d))
     return W4A16_ERR_UNSUPPORTED;

@@ -44,6 +44,7 @@ struct MlpPlan {
   bool mfma = false;
   MfmaPlan gu, dn;
   size_t apx_off = 0, rsx_off = 0, aph_off = 0, rsh_off = 0;
+  bool split_pieces = false;  // h pieces per down K split (rsh: [S_down][Mp])
   size_t bytes = 0;
 };
 

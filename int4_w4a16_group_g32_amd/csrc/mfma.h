@@ -97,10 +97,12 @@ w4a16_status_t launch_wide(const MfmaArgs& a, size_t num_tasks, hipStream_t stre
                            hipEvent_t stop = nullptr);
 
 // Deferred split-K, plain output: out[m][n] = (sum over splits, in split
-// order, of planes[s][0][m][n]) * rs[m] for m < M, n < N (N a multiple of 4).
-w4a16_status_t launch_plane_sum(const float* planes, int S, int plane_rows, int plane_ld, const float* rs, int M,
-                                int N, float* out, hipStream_t stream, hipEvent_t start = nullptr,
-                                hipEvent_t stop = nullptr);
+// order, of planes[s][0][m][n]) * rs[m] for m < M, n < N (N a multiple of 4);
+// with rs_stride > 0, the split-order sum of planes[s][0][m][n] *
+// rs[s * rs_stride + m] (activations scaled per row and split).
+w4a16_status_t launch_plane_sum(const float* planes, int S, int plane_rows, int plane_ld, const float* rs,
+                                int rs_stride, int M, int N, float* out, hipStream_t stream,
+                                hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Deferred split-K, SwiGLU: h[m][n] = silu(g * f) * (u * f) with g, u the
 // split-order sums of planes[s][0] and planes[s][1] and f = rsx[m], written
 // to h[M][I], then the f16 pieces of h as launch_mfma_prep makes them
@@ -108,6 +110,17 @@ w4a16_status_t launch_plane_sum(const float* planes, int S, int plane_rows, int 
 w4a16_status_t launch_prep_planes(const float* planes, int S, int plane_rows, int plane_ld, const float* rsx,
                                   int M, int Mp, int I, int P, float* h, _Float16* ap, float* rs,
                                   hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+
+// Deferred split-K, SwiGLU, pieces per down split: the h columns [c * cols,
+// (c + 1) * cols) of row m, h = silu(g * f) * (u * f) as above, become f16
+// pieces scaled to that range's own largest magnitude, rs[c * Mp + m] =
+// 2^-e (rows M .. Mp-1: zero pieces, rs 0).  h itself is not stored.
+// UNSUPPORTED when a range holds more than split_pieces_threads' limit
+// (256 threads x 4 blocks of 8 = 8192 columns).
+int split_pieces_threads(int cols);  // 0: range too long
+w4a16_status_t launch_prep_split_pieces(const float* planes, int S, int plane_rows, int plane_ld, const float* rsx,
+                                        int M, int Mp, int I, int P, int cols, _Float16* ap, float* rs,
+                                        hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 // Rows of the piece planes for R positions.
 inline int mfma_rows_padded(int R) { return (R + kMfmaRows - 1) / kMfmaRows * kMfmaRows + kMfmaRows; }

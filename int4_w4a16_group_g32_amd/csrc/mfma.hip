@@ -657,11 +657,13 @@ void mfma_kernel(const MfmaArgs a) {
 
 // ------------------------------------------------------- deferred split-K
 
-// out[m][n..n+3] = (sum of the split planes, split order) * rs[m]: one thread
-// per four columns, every split's load in flight before the sum.
+// out[m][n..n+3] = (sum of the split planes, split order) * rs[m], or with
+// rs_stride > 0 the split-order sum of planes[s] * rs[s * rs_stride + m]
+// (activations scaled per row and split): one thread per four columns, every
+// split's loads in flight before the sum.
 __global__ __launch_bounds__(256) void plane_sum_kernel(const float* __restrict__ planes, int S, int plane_rows,
-                                                        int plane_ld, const float* __restrict__ rs, int M, int N,
-                                                        float* __restrict__ out) {
+                                                        int plane_ld, const float* __restrict__ rs, int rs_stride,
+                                                        int M, int N, float* __restrict__ out) {
   const int n4 = N / 4;
   const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= static_cast<size_t>(M) * n4) return;
@@ -673,6 +675,17 @@ __global__ __launch_bounds__(256) void plane_sum_kernel(const float* __restrict_
   for (int s = 0; s < kMaxSplits; ++s)
     if (s < S) v[s] = *reinterpret_cast<const f32x4*>(p + s * sstride);
   f32x4 t = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (rs_stride > 0) {
+    float f[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+      if (s < S) f[s] = rs[static_cast<size_t>(s) * rs_stride + m];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+      if (s < S) t += v[s] * f[s];
+    *reinterpret_cast<f32x4*>(out + static_cast<size_t>(m) * N + n) = t;
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s)
     if (s < S) t += v[s];
@@ -757,17 +770,148 @@ __global__ __launch_bounds__(kPrepThreads) void prep_planes_kernel(const float* 
   }
 }
 
+// The pieces of h per K split of the down projection, from the gate/up
+// split planes.  Workgroup (row, c) takes the h columns [c * cols, (c + 1) *
+// cols) of one row, which down split c reads: it sums the gate/up planes in
+// split order, forms h = silu(g * f) * (u * f) in registers, and scales the
+// pieces to the largest magnitude of that range alone (as mfma_prep_kernel
+// does for a whole row): rs[c * Mp + row] = 2^-e_c.  Down split c then sums
+// in units of 2^-e_c, which the plane sum multiplies back before it adds the
+// splits.  Each thread keeps up to kSplitPrepBlocks blocks of 8 values;
+// rows M .. Mp-1 get zero pieces and rs 0.
+constexpr int kSplitPrepThreads = 256;
+constexpr int kSplitPrepBlocks = 4;
+constexpr int kSplitPrepBatch = 4;  // gate/up split planes read together
+
+template <int P>
+__global__ __launch_bounds__(kSplitPrepThreads) void prep_split_pieces_kernel(
+    const float* __restrict__ planes, int S, int plane_rows, int plane_ld, const float* __restrict__ rsx, int M,
+    int Mp, int I, int cols, _Float16* __restrict__ ap, float* __restrict__ rs) {
+  __shared__ float red[kSplitPrepThreads / kWave];
+  const int row = blockIdx.x, c = blockIdx.y;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int n0 = c * cols;
+  const int nbc = min(cols, I - n0) / 8;
+  float v[kSplitPrepBlocks][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kSplitPrepBlocks; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+  if (row < M) {
+    const float f = rsx[row];
+    const size_t sstride = static_cast<size_t>(2) * plane_rows * plane_ld;  // one split: gate plane + up plane
+    const float* gp = planes + static_cast<size_t>(row) * plane_ld + n0;
+    const float* up = gp + static_cast<size_t>(plane_rows) * plane_ld;
+#pragma unroll
+    for (int i = 0; i < kSplitPrepBlocks; ++i) {
+      const int b = tid + i * nt;
+      if (b < nbc) {
+        f32x4 g0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, g1 = g0, u0 = g0, u1 = g0;
+        // kSplitPrepBatch splits' loads in flight together, summed in split order
+        for (int s0 = 0; s0 < S; s0 += kSplitPrepBatch) {
+          f32x4 q[kSplitPrepBatch][4];
+#pragma unroll
+          for (int j = 0; j < kSplitPrepBatch; ++j)
+            if (s0 + j < S) {
+              const size_t o = (s0 + j) * sstride + 8 * static_cast<size_t>(b);
+              q[j][0] = *reinterpret_cast<const f32x4*>(gp + o);
+              q[j][1] = *reinterpret_cast<const f32x4*>(gp + o + 4);
+              q[j][2] = *reinterpret_cast<const f32x4*>(up + o);
+              q[j][3] = *reinterpret_cast<const f32x4*>(up + o + 4);
+            }
+#pragma unroll
+          for (int j = 0; j < kSplitPrepBatch; ++j)
+            if (s0 + j < S) {
+              g0 += q[j][0];
+              g1 += q[j][1];
+              u0 += q[j][2];
+              u1 += q[j][3];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[i][j] = silu(g0[j] * f) * (u0[j] * f);
+          v[i][4 + j] = silu(g1[j] * f) * (u1[j] * f);
+          amax = fmaxf(amax, fmaxf(fabsf(v[i][j]), fabsf(v[i][4 + j])));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if (lane_id() == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = 0.0f;
+  for (int w = 0; w < nt / kWave; ++w) amax = fmaxf(amax, red[w]);
+  int e = 0;
+  if (amax > 0.0f) {
+    int lg = ilogbf(amax);
+    lg = lg > 120 ? 120 : (lg < -120 ? -120 : lg);
+    e = 14 - lg;
+  }
+  const float scale = amax > 0.0f ? ldexpf(1.0f, e) : 0.0f;
+  if (tid == 0) rs[static_cast<size_t>(c) * Mp + row] = scale > 0.0f ? ldexpf(1.0f, -e) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < kSplitPrepBlocks; ++i) {
+    const int b = tid + i * nt;
+    if (b < nbc) {
+      half8 h0, h1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float t = scale != 0.0f ? v[i][kCodeOrder[j]] * scale : 0.0f;
+        const _Float16 hi = static_cast<_Float16>(t);
+        h0[j] = hi;
+        if (P == 2) h1[j] = static_cast<_Float16>(t - static_cast<float>(hi));
+      }
+      _Float16* dst = ap + static_cast<size_t>(row) * I + n0 + 8 * b;
+      *reinterpret_cast<half8*>(dst) = h0;
+      if (P == 2) *reinterpret_cast<half8*>(dst + static_cast<size_t>(Mp) * I) = h1;
+    }
+  }
+}
+
 }  // namespace
 
-w4a16_status_t launch_plane_sum(const float* planes, int S, int plane_rows, int plane_ld, const float* rs, int M,
-                                int N, float* out, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+w4a16_status_t launch_plane_sum(const float* planes, int S, int plane_rows, int plane_ld, const float* rs,
+                                int rs_stride, int M, int N, float* out, hipStream_t stream, hipEvent_t start,
+                                hipEvent_t stop) {
   if (M == 0 || N == 0) return W4A16_OK;
-  if (S < 1 || S > kMaxSplits || N % 4 != 0 || plane_ld < N || plane_rows < M) return W4A16_ERR_INVALID_ARG;
+  if (S < 1 || S > kMaxSplits || N % 4 != 0 || plane_ld < N || plane_rows < M || rs_stride < 0 ||
+      (rs_stride > 0 && rs_stride < M))
+    return W4A16_ERR_INVALID_ARG;
   const size_t n = static_cast<size_t>(M) * (N / 4);
   const size_t blocks = (n + 255) / 256;
   if (blocks > 0x7fffffffu) return W4A16_ERR_UNSUPPORTED;
   hipExtLaunchKernelGGL(plane_sum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, start, stop,
-                        0, planes, S, plane_rows, plane_ld, rs, M, N, out);
+                        0, planes, S, plane_rows, plane_ld, rs, rs_stride, M, N, out);
+  return launch_status();
+}
+
+// One block of 8 per thread where the range allows (more loads in flight),
+// up to kSplitPrepBlocks per thread of a full workgroup.
+int split_pieces_threads(int cols) {
+  const int nb = cols / 8;
+  if (nb > kSplitPrepThreads * kSplitPrepBlocks) return 0;
+  const int t = (nb + kWave - 1) / kWave * kWave;
+  return t < kWave ? kWave : (t > kSplitPrepThreads ? kSplitPrepThreads : t);
+}
+
+w4a16_status_t launch_prep_split_pieces(const float* planes, int S, int plane_rows, int plane_ld, const float* rsx,
+                                        int M, int Mp, int I, int P, int cols, _Float16* ap, float* rs,
+                                        hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (Mp == 0 || I == 0) return W4A16_OK;
+  if (S < 1 || cols <= 0 || cols % 8 != 0 || I % 8 != 0 || plane_ld < I || plane_rows < M || Mp < M)
+    return W4A16_ERR_INVALID_ARG;
+  const int nt = split_pieces_threads(cols);
+  if (nt == 0) return W4A16_ERR_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(Mp), static_cast<unsigned>((I + cols - 1) / cols));
+  if (P == 2)
+    hipExtLaunchKernelGGL(prep_split_pieces_kernel<2>, grid, dim3(nt), 0, stream, start, stop, 0, planes, S,
+                          plane_rows, plane_ld, rsx, M, Mp, I, cols, ap, rs);
+  else
+    hipExtLaunchKernelGGL(prep_split_pieces_kernel<1>, grid, dim3(nt), 0, stream, start, stop, 0, planes, S,
+                          plane_rows, plane_ld, rsx, M, Mp, I, cols, ap, rs);
   return launch_status();
 }
 
