@@ -205,11 +205,13 @@ W4A16_API size_t w4a16_swiglu_mlp_workspace_bytes(int32_t M, w4a16_dtype_t xt, c
  * Weight of Precision", section "The Context That Produced This Message" names
  * SwiGLU).  gate and up are [H -> I], down is [I -> H], all dense GROUPED.
  * x is [M][H], y is [M][H] float32.  The gate and up projections run in one
- * pass with the SiLU-times-up product formed in the epilogue; the
- * intermediate h[M][I] lives in the workspace in float32 for both activation
- * types (the down projection then stages it as f16 pieces, two for float32
- * x and one for bf16 x).  Errors as w4a16_gemm, plus UNSUPPORTED if the three
- * shapes do not chain.
+ * pass with the SiLU-times-up product formed in the epilogue.  The down
+ * projection reads the intermediate h[M][I] as f16 pieces (two for float32 x,
+ * one for bf16 x), scaled by a power of two per row: on the GEMV path and
+ * when a tile launch runs unsplit, h is first stored in the workspace in
+ * float32; when both tile launches split K, the gate/up split sums become
+ * pieces directly, scaled per row and down K split, and h is not stored.
+ * Errors as w4a16_gemm, plus UNSUPPORTED if the three shapes do not chain.
  */
 W4A16_API w4a16_status_t w4a16_swiglu_mlp(const void* x, w4a16_dtype_t xt, int32_t M,
                                 const w4a16_weight_t* gate, const w4a16_weight_t* up,
@@ -225,9 +227,10 @@ W4A16_API w4a16_status_t w4a16_swiglu_mlp(const void* x, w4a16_dtype_t xt, int32
  * `capacity` events (kernels beyond capacity / 2 run unbracketed); *recorded
  * (if not NULL) receives how many were used.  Up to 8 rows (float32) or 16
  * (bf16) the dense MLP launches two kernels (fused gate/up
- * GEMV with the SwiGLU epilogue, down GEMV); for larger M four (activation
- * pieces, fused gate/up MFMA tiles, pieces of the intermediate, down MFMA).  Events are created and
- * owned by the caller.  Errors as w4a16_swiglu_mlp, plus INVALID_ARG for
+ * GEMV with the SwiGLU epilogue, down GEMV); for larger M four or five
+ * (activation pieces, fused gate/up MFMA tiles, pieces of the intermediate,
+ * down MFMA tiles, and the sum of the down projection's K splits when it is
+ * split).  Events are created and owned by the caller.  Errors as w4a16_swiglu_mlp, plus INVALID_ARG for
  * capacity < 0 or events == NULL with capacity > 0, and HIP if recording fails.
  */
 W4A16_API w4a16_status_t w4a16_swiglu_mlp_timed(const void* x, w4a16_dtype_t xt, int32_t M,
@@ -254,8 +257,9 @@ W4A16_API w4a16_status_t w4a16_swiglu_mlp_timed(const void* x, w4a16_dtype_t xt,
  * caller still passes x and y.  Errors as w4a16_swiglu_mlp, plus WORKSPACE
  * (nothing enqueued) when the call needs more scratch than the array holds
  * (w4a16_swiglu_mlp_workspace_bytes above W4A16_STATIC_SCRATCH_BYTES; the
- * hidden 7168 / intermediate 18432 MLP fits up to M = 128) and HIP if the
- * array's address cannot be looked up.
+ * hidden 7168 / intermediate 18432 MLP fits up to M = 64 with float32 x and
+ * up to M = 192 with bf16 x) and HIP if the array's address cannot be looked
+ * up.
  */
 W4A16_API w4a16_status_t w4a16_swiglu_mlp_static(const void* x, w4a16_dtype_t xt, int32_t M,
                                                  const w4a16_weight_t* gate, const w4a16_weight_t* up,
