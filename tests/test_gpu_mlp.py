@@ -177,3 +177,31 @@ def test_mlp_gemv_four_tile_workgroups_ragged(dtype):
     err = rel_err(y[:, torch.as_tensor(cols, device="cuda")], ref)
     print(f"mlp H={H} I={I} M={M} {dtype} relF={err:.3e} (512 sampled columns)", flush=True)
     assert err <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("M,dtype", [(64, "bf16"), (40, "f32")])
+def test_mlp_split_pieces_zero_and_small_ranges(M, dtype):
+    """Hidden 2048, intermediate 4096: both tile launches split K, so the
+    pieces of h are made per down split from the gate/up split sums (the five
+    kernels of test_mlp_timed_brackets_each_kernel).  Gate columns 0..1023 are
+    zero, so h is zero there and the down splits over that range get zero
+    pieces and a zero row factor; up columns 2048..3071 are scaled by 2^-20,
+    so those splits' largest magnitudes sit far below the row's.  Element-wise
+    bound and relF against the oracle."""
+    H, I, cfg = 2048, 4096, 640 + M
+    gate = W.weights(H, I, cfg, W.TAG_GATE).numpy()
+    up = W.weights(H, I, cfg, W.TAG_UP).numpy()
+    down = W.weights(I, H, cfg, W.TAG_DOWN).numpy()
+    gate[:, :1024] = 0.0
+    up[:, 2048:3072] *= np.float32(2.0 ** -20)
+    codes = [O.quantize_w4a16(w) for w in (gate, up, down)]
+    g, u, d = (weight_from_codes(*c) for c in codes)
+    x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
+    y = _mlp_gpu(x, g, u, d)
+    ref = O.swiglu_mlp64(x_values(x), *codes)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, mlp_bound(x_values(x), *codes, TAU[dtype]),
+                              f"mlp split pieces M={M} {dtype}")
+    print(f"mlp split pieces M={M} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
+    assert err <= tol_for(dtype)
+    assert torch.isfinite(y).all()
