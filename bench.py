@@ -15,7 +15,8 @@ that the library takes from the kernel's own dispatch) and the CPU oracle
 timed on a bounded sample of the same workload.  Under "workloads" the same
 record follows for every other configuration: the single GEMM (cold and
 warm), the tree-verify MLP at 64 tokens (float32 and bf16), the MoE decode
-and prefill layers and the hot-expert GEMM.
+and prefill layers, the hot-expert GEMM, and one GPU's share of the dense MLP
+under 8-way tensor parallelism (intermediate 2304) at 4 and 64 tokens.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20]
     python bench.py --workload NAME        # one workload's line only
@@ -42,7 +43,7 @@ METRIC = "W4A16 GEMM/MoE µs + achieved HBM GB/s (% of 8 TB/s) at decode M; TFLO
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / f16 matrix cores, published
 OTHER_WORKLOADS = ("gemm_m1", "mlp_verify_m64_f32", "mlp_verify_m64_bf16", "moe_decode_m64",
-                   "moe_prefill_m2048", "gemm_m2048_hot_expert")
+                   "moe_prefill_m2048", "gemm_m2048_hot_expert", "mlp_decode_m4_tp8", "mlp_verify_m64_bf16_tp8")
 CSRC = "int4_w4a16_group_g32_amd/csrc/"
 # Sources of each dominant kernel: a stored counter summary is used only
 # while they hash to the value it was taken on.

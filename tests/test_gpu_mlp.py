@@ -205,3 +205,32 @@ def test_mlp_split_pieces_zero_and_small_ranges(M, dtype):
     print(f"mlp split pieces M={M} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
     assert err <= tol_for(dtype)
     assert torch.isfinite(y).all()
+
+
+@pytest.mark.parametrize("name,dtype", [("mlp_decode_m4_tp8", "f32"), ("mlp_verify_m64_bf16_tp8", "bf16"),
+                                        ("mlp_verify_m64_bf16_tp8", "f32")])
+def test_mlp_tp8_share_full_size(name, dtype):
+    """One GPU's share of the dense MLP under 8-way tensor parallelism
+    (hidden 7168, intermediate 2304: gate/up column-parallel, down
+    row-parallel), every output element against the oracle; the library's
+    quantization of the weights is checked word for word against the
+    oracle's."""
+    cfg = W.CONFIGS[name]
+    H, I, M = cfg.K, cfg.N, cfg.M
+    gpu, codes = [], []
+    for K, N, tag in ((H, I, W.TAG_GATE), (H, I, W.TAG_UP), (I, H, W.TAG_DOWN)):
+        w = W.weights(K, N, cfg.index, tag, device="cuda")
+        gpu.append(L.quantize_to_weight(w))
+        codes.append(O.quantize_w4a16(w.cpu().numpy()))
+        del w
+    for wt, (qw, sc), (K, N) in zip(gpu, codes, ((H, I), (H, I), (I, H))):
+        assert np.array_equal(canonical_words(wt.qw.cpu().numpy(), K, N)[0], qw)
+        assert np.array_equal(wt.scales.cpu().numpy().reshape(sc.shape), sc)
+    x = x_for_dtype(W.activations(M, H, cfg.index).cuda(), dtype)
+    y = _mlp_gpu(x, *gpu)
+    xv = x_values(x)
+    ref = O.swiglu_mlp64(xv, *codes)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, mlp_bound(xv, *codes, TAU[dtype]), f"{name} {dtype}")
+    print(f"{name} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
+    assert err <= tol_for(dtype)

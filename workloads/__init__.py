@@ -58,6 +58,10 @@ CONFIGS = {
     "moe_prefill_m2048_shared": Config("moe_prefill_m2048_shared", 4, "moe", 2048, 7168, 2048, "bf16", 384, 8,
                                        "zipf", 1.1, shared=True),
     "gemm_m2048_hot_expert": Config("gemm_m2048_hot_expert", 5, "gemm", 2048, 7168, 4096, "bf16"),
+    # one GPU's share of the dense MLP under 8-way tensor parallelism: gate/up
+    # column-parallel (N = 18432 / 8), down row-parallel (K = 18432 / 8)
+    "mlp_decode_m4_tp8": Config("mlp_decode_m4_tp8", 6, "mlp", 4, 7168, 2304, "f32"),
+    "mlp_verify_m64_bf16_tp8": Config("mlp_verify_m64_bf16_tp8", 6, "mlp", 64, 7168, 2304, "bf16"),
     # router (top-k gating) ahead of the two MoE layers: float32 logits [M][384]
     "router_m64": Config("router_m64", 3, "router", 64, 0, 0, "f32", 384, 8),
     "router_m2048": Config("router_m2048", 4, "router", 2048, 0, 0, "f32", 384, 8),
