@@ -111,13 +111,14 @@ def test_mlp_full_size(dense_mlp, name, dtype):
     assert np.array_equal(qd, _sampled_down(w_down, cols)[0])
 
 
-@pytest.mark.parametrize("M,dtype,H,I,kernels", [(4, "f32", 256, 512, 2), (100, "bf16", 256, 512, 4),
+@pytest.mark.parametrize("M,dtype,H,I,kernels", [(4, "f32", 256, 512, 2), (100, "bf16", 128, 128, 4),
                                                  (64, "bf16", 2048, 4096, 5), (40, "f32", 2048, 4096, 5)])
 def test_mlp_timed_brackets_each_kernel(M, dtype, H, I, kernels):
     """w4a16_swiglu_mlp_timed does the same work as w4a16_swiglu_mlp (same
     output bits) and brackets each of its kernels with a start and a stop
     event.  From M = 9 (float32) or 17 (bf16): the activation pieces, the
-    gate/up tiles, the pieces of h and the down tiles; with K split across
+    gate/up tiles, the pieces of h and the down tiles (hidden and
+    intermediate 128: too few groups to split K); with K split across
     workgroups (hidden 2048, intermediate 4096) the pieces of h are formed
     from the gate/up split sums and a fifth kernel adds the down projection's
     splits."""
