@@ -96,6 +96,7 @@ def test_mlp_full_size(dense_mlp, name, dtype):
     cfg = W.CONFIGS[name]
     x = x_for_dtype(W.activations(cfg.M, H, cfg.index).cuda(), dtype)
     y = _mlp_gpu(x, g, u, d)
+    assert torch.equal(y, _mlp_gpu(x, g, u, d))  # deterministic across calls
     cols = np.sort(np.random.default_rng(cfg.M).choice(H, size=512, replace=False))
     xv = x_values(x)
     dq = _sampled_down(w_down, cols)

@@ -256,7 +256,8 @@ def _random_code_stacks(cfg, E, H, I):
 def _full_moe_every_token(name):
     """Every token of a full-size MoE layer (384 experts of 7168 -> 2048,
     top-8, bf16) against the oracle, with random code words (q = -8 included)
-    and the element-wise bound; the oracle's experts run in worker processes."""
+    and the element-wise bound; the oracle's experts run in worker processes.
+    A second call must reproduce the output bit for bit."""
     cfg = W.CONFIGS[name]
     E, H, I, M, k = cfg.experts, cfg.K, cfg.N, cfg.M, cfg.top_k
     if cfg.routing == "zipf":
@@ -267,6 +268,8 @@ def _full_moe_every_token(name):
     stacks, expert = _random_code_stacks(cfg, E, H, I)
     x = x_for_dtype(W.activations(M, H, cfg.index).cuda(), cfg.x_dtype)
     y = _moe_gpu(x, to_dev(ids), to_dev(wts), *stacks)
+    # deterministic: a second call (fresh workspace) gives the same bits
+    assert torch.equal(y, _moe_gpu(x, to_dev(ids), to_dev(wts), *stacks))
     counts = np.bincount(ids.ravel(), minlength=E)
     print(f"{name}: {int((counts > 0).sum())} experts active, rows per expert {counts.min()}..{counts.max()}",
           flush=True)
