@@ -192,3 +192,22 @@ def test_static_mlp_size_check_is_host_only(lib):
                                        None) == L.OK  # M == 0: nothing to do
     assert lib.w4a16_swiglu_mlp_static(None, 7, 4, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), None,
                                        None) == L.ERR_INVALID_ARG
+
+
+def test_static_scratch_limits_match_the_header(lib):
+    """The header's stated reach of w4a16_swiglu_mlp_static for the hidden
+    7168 / intermediate 18432 MLP: every M up to 64 (float32) and up to 192
+    (bf16) needs at most W4A16_STATIC_SCRATCH_BYTES of workspace, and the
+    next row count needs more."""
+    text = open(HEADER).read()
+    assert "up to M = 64 with float32 x" in text and "up to M = 192 with bf16 x" in text
+    limit = 64 << 20
+    assert re.search(r"#define W4A16_STATIC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", text)
+    g, u, dn = _desc(7168, 18432), _desc(7168, 18432), _desc(18432, 7168)
+
+    def need(M, xt):
+        return lib.w4a16_swiglu_mlp_workspace_bytes(M, xt, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn))
+
+    for xt, last in ((L.F32, 64), (L.BF16, 192)):
+        assert all(0 < need(M, xt) <= limit for M in range(1, last + 1))
+        assert need(last + 1, xt) > limit
