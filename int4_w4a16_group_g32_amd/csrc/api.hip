@@ -35,15 +35,15 @@ MfmaPlan plan_wide(int rows, int N, int K) {
          m.tasks * (S + 1) * sizeof(int) <= kCounterBytes)
     ++S;
   if (m.tasks * sizeof(int) > kCounterBytes) S = 1;
-  // an even number of groups per split (G is even): whole two-group windows
-  m.gps = G > 0 ? ((G + S - 1) / S + 1) / 2 * 2 : 2;
+  // a multiple of four groups per split (G is one): whole four-group windows
+  m.gps = G > 0 ? ((G + S - 1) / S + 3) / 4 * 4 : 4;
   m.S = G > 0 ? (G + m.gps - 1) / m.gps : 1;
   return m;
 }
 
 MfmaPlan plan_mfma(int rows, int N, int mode, int K, w4a16_dtype_t xt, bool allow_wide) {
   // (the wide kernel's buffer offsets are 32-bit: codes under 2 GiB)
-  if (allow_wide && xt == W4A16_BF16 && mode == 0 && rows >= W4_WIDE_MIN_ROWS && K % 64 == 0 &&
+  if (allow_wide && xt == W4A16_BF16 && mode == 0 && rows >= W4_WIDE_MIN_ROWS && K % 128 == 0 &&
       static_cast<size_t>(K) * N / 2 < (size_t{1} << 31))
     return plan_wide(rows, N, K);
   MfmaPlan m;

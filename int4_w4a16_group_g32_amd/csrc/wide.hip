@@ -14,16 +14,18 @@
 //
 // A workgroup computes 256 rows x 128 columns with eight waves, two per SIMD:
 // wave (kh, wr, wc) = (wv >> 2, (wv >> 1) & 1, wv & 1) owns rows 128wr ..
-// +127 and columns 64wc .. +63, and the K half kh: of each window's two
-// groups it takes group kh.  Per group a wave runs 8 x 4 MFMA blocks of
-// 16 x 16, so every expanded weight feeds 8 MFMAs, twice the 64-row tile's
-// reuse, and the vector work per matrix-core instruction halves.  The
-// 256 x 64 activation window (two groups) is staged once in LDS; each wave
-// streams its own 64 columns of codes of its own groups, one 16-byte GROUPED
-// slot per lane and group.  After the loop the second K half's sums are added
-// to the first half's through LDS, in that order.  (With one wave per SIMD and
-// every wave on both groups of a window, the 2048 x 7168 x 4096 GEMM took
-// 138-142 against 133 us here.)
+// +127 and columns 64wc .. +63, and the K half kh: of each window's four
+// groups it takes groups kh and kh + 2.  Per group a wave runs 8 x 4 MFMA
+// blocks of 16 x 16, so every expanded weight feeds 8 MFMAs, twice the 64-row
+// tile's reuse, and the vector work per matrix-core instruction halves.  The
+// 256 x 128 activation window (four groups, 64 KiB) is staged once in LDS,
+// double-buffered, with one workgroup barrier per window; each wave streams
+// its own 64 columns of codes of its own groups, one 16-byte GROUPED slot per
+// lane and group.  After the loop the second K half's sums are added to the
+// first half's through LDS, in that order.  (With one wave per SIMD and every
+// wave on both groups of a two-group window, the 2048 x 7168 x 4096 GEMM took
+// 138-142 us here; with two-group windows, a barrier every two groups,
+// 129-132 against 125-127 us.)
 //
 // Workgroups are numbered so that each XCD (the hardware deals workgroup b to
 // XCD b mod 8) takes a contiguous run of tiles, row tile major: the column
@@ -38,7 +40,7 @@
 namespace w4 {
 namespace {
 
-constexpr int kWw = 2;                                     // groups per staged activation window (one per K half)
+constexpr int kWw = 4;                                     // groups per staged activation window (two per K half)
 constexpr int kWideWgThreads = 2 * kWideThreads;           // two K halves of four waves
 constexpr int kWideRing = 2;                               // own groups of codes in flight per wave (two windows)
 constexpr int kWideWinUnits = kWw * kWideRows * 4;         // 16-byte units per window
@@ -71,7 +73,7 @@ __device__ __forceinline__ int w_off(int gl, int row, int kb) {
 }
 
 struct WideLds {
-  uint4 a[2][kWideWinUnits];  // double buffer, 2 x 32 KiB
+  uint4 a[2][kWideWinUnits];  // double buffer, 2 x 64 KiB
   float red[kAnchorPhases][kWideCols];  // anchor reduction
   int cexp[kWideCols];
   int last;
@@ -86,26 +88,29 @@ struct WideLds {
 // row of the plane, which the workspace pads), and is never used.
 __device__ __forceinline__ int stage_row(int u) { return 8 * (u >> 6) + ((u >> 2) & 7); }
 
-// A window is staged in two halves of kHalfUnits units per thread, so that
-// only one half is held in registers at a time.
-constexpr int kHalfUnits = kWideUnitsPerThread / 2;
-__device__ __forceinline__ void wide_load_a(__amdgpu_buffer_rsrc_t ra_src, int voff, int K, int gw, int hf,
-                                            uint4 r[kHalfUnits]) {
+// A window is staged in four parts of kPartUnits units per thread, so that
+// only one part is held in registers at a time.  Unit i of a thread covers
+// rows + 64 (i & 3) of the groups pair i >> 2 (window groups 0-1 or 2-3).
+constexpr int kParts = 4;
+constexpr int kPartUnits = kWideUnitsPerThread / kParts;
+__device__ __forceinline__ void wide_load_a(__amdgpu_buffer_rsrc_t ra_src, int voff, int K, int gw, int part,
+                                            uint4 r[kPartUnits]) {
 #pragma unroll
-  for (int j = 0; j < kHalfUnits; ++j) {
-    const int i = hf * kHalfUnits + j;
-    r[j] = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(ra_src, voff, (gw * kGroup + kWideWgThreads / 8 * i * K) * 2, 0));
+  for (int j = 0; j < kPartUnits; ++j) {
+    const int i = part * kPartUnits + j;
+    r[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         ra_src, voff, ((gw + 2 * (i >> 2)) * kGroup + 64 * (i & 3) * K) * 2, 0));
   }
 }
 
-// Every split holds an even number of groups (the launch checks it), so a
+// Every split holds a multiple of four groups (the launch checks it), so a
 // window is always whole.
-__device__ __forceinline__ void wide_store_a(uint4* buf, int hf, const uint4 r[kHalfUnits]) {
+__device__ __forceinline__ void wide_store_a(uint4* buf, int part, const uint4 r[kPartUnits]) {
 #pragma unroll
-  for (int j = 0; j < kHalfUnits; ++j) {
-    const int u = static_cast<int>(threadIdx.x) + kWideWgThreads * (hf * kHalfUnits + j);
-    buf[w_off((u >> 5) & 1, stage_row(u), u & 3)] = r[j];
+  for (int j = 0; j < kPartUnits; ++j) {
+    const int i = part * kPartUnits + j;
+    const int u = static_cast<int>(threadIdx.x) + kWideWgThreads * (i & 3);
+    buf[w_off(((u >> 5) & 1) + 2 * (i >> 2), stage_row(u), u & 3)] = r[j];
   }
 }
 
@@ -209,10 +214,11 @@ void wide_kernel(const MfmaArgs a) {
   const int g_lo = split * a.gps;
   const int g_hi = min(a.G, g_lo + a.gps);
   const int nwin = (g_hi - g_lo + kWw - 1) / kWw;
-  // this wave's own groups: g_lo + kh + kWw * j, one per window
-  auto own = [&](int j) { return g_lo + kh + kWw * j; };
+  // this wave's own groups: g_lo + kh + 2 j, two per window (window groups kh
+  // and kh + 2)
+  auto own = [&](int j) { return g_lo + kh + 2 * j; };
 
-  uint4 ra[kHalfUnits];
+  uint4 ra[kPartUnits];
   WideCodes ring[kWideRing];  // own group j sits in slot j % kWideRing
   wide_load_a(asrc, avoff, a.K, g_lo, 0, ra);
 #pragma unroll
@@ -252,8 +258,11 @@ void wide_kernel(const MfmaArgs a) {
     }
   }
   wide_store_a(lds.a[0], 0, ra);
-  wide_load_a(asrc, avoff, a.K, g_lo, 1, ra);
-  wide_store_a(lds.a[0], 1, ra);
+#pragma unroll
+  for (int part = 1; part < kParts; ++part) {
+    wide_load_a(asrc, avoff, a.K, g_lo, part, ra);
+    wide_store_a(lds.a[0], part, ra);
+  }
   __syncthreads();
   int cexp[4];
 #pragma unroll
@@ -265,15 +274,15 @@ void wide_kernel(const MfmaArgs a) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Window wi uses LDS buffer h = wi % 2 and this wave's own group wi (ring
-  // slot wi % 2); the loop body is two whole windows and an odd last window
-  // runs after it, so every path into the loop header has the same loads
-  // outstanding.  A window is a run of 8 row-block steps, each one A fragment
-  // read (kAhead steps ahead) and 4 MFMAs; between the MFMAs run the steps of
-  // the expansion of the wave's next own group, whose slot is then refilled
-  // with own group wi + 1 + kWideRing.  The schedule is pinned with
-  // scheduling barriers.
-  half8 bq[2][4];  // expanded weights, by window parity
+  // Window wi uses LDS buffer h = wi % 2 and holds this wave's own groups
+  // 2 wi and 2 wi + 1 (own group j sits in ring slot j % 2); the loop body is
+  // two whole windows and an odd last window runs after it, so every path into
+  // the loop header has the same loads outstanding.  An own group is a pass
+  // of 8 row-block steps, each one A fragment read (kAhead steps ahead) and 4
+  // MFMAs; between the MFMAs run the steps of the expansion of the wave's
+  // next own group, whose slot is then refilled with own group j + 1 +
+  // kWideRing.  The schedule is pinned with scheduling barriers.
+  half8 bq[2][4];  // expanded weights, by own-group parity
   {
     WordExp e;
 #pragma unroll
@@ -295,51 +304,65 @@ void wide_kernel(const MfmaArgs a) {
   auto window = [&](int wi, auto hc) {
     constexpr int h = decltype(hc)::value;
     const int gw = g_lo + wi * kWw;
-    wide_load_a(asrc, avoff, a.K, gw + kWw, 0, ra);  // the next window's first half, in flight
+    wide_load_a(asrc, avoff, a.K, gw + kWw, 0, ra);  // part 0 of the next window, in flight
     const uint4* buf = lds.a[h];
-    auto rd = [&](int st) {
-      return __builtin_bit_cast(half8, buf[w_off(kh, wr * 128 + st * 16 + lc, kb)]);
-    };
-    half8 af[4];
+    static_assert(2 % kWideRing == 0, "ring slots repeat with the two passes of a window");
+    // Pass p computes this wave's own group 2 wi + p (window group kh + 2 p).
+    // The next window's parts are stored (buffer 1 - h is free) and fetched
+    // at rb = 4 of pass 0, rb = 0 and rb = 4 of pass 1, and after pass 1.
+    auto pass = [&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      auto rd = [&](int st) {
+        return __builtin_bit_cast(half8, buf[w_off(kh + 2 * p, wr * 128 + st * 16 + lc, kb)]);
+      };
+      half8 af[4];
 #pragma unroll
-    for (int st = 0; st < kAhead; ++st) af[st] = rd(st);
-    __builtin_amdgcn_sched_barrier(0);
-    static_assert(2 % kWideRing == 0, "ring slots repeat with the loop body");
-    constexpr int cur = h;                      // this window's expanded weights
-    constexpr int nslot = (h + 1) % kWideRing;  // ring slot of the next own group
-    WordExp e;
+      for (int st = 0; st < kAhead; ++st) af[st] = rd(st);
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int cur = p;                      // this own group's expanded weights
+      constexpr int nslot = (p + 1) % kWideRing;  // ring slot of the next own group
+      WordExp e;
 #pragma unroll
-    for (int rb = 0; rb < 8; ++rb) {
-      if (rb == 4) {  // the first half is in: store it (buffer 1 - h is free) and fetch the second
-        wide_store_a(lds.a[1 - h], 0, ra);
-        wide_load_a(asrc, avoff, a.K, gw + kWw, 1, ra);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (rb + kAhead < 8) af[(rb + kAhead) & 3] = rd(rb + kAhead);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        mfma_tied(acc[rb][cb], af[rb & 3], bq[cur][cb]);
-        // expansion step (rb * 4 + cb) % 8 of word (rb * 4 + cb) / 8
-        const int x = rb * 4 + cb, word = x >> 3;
-        const uint32_t wd = ring[nslot].w[word];
-        const float sc = ring[nslot].s[word];
-        half8& o = bq[cur ^ 1][word];
-        switch (x & 7) {
-          case 0: expand_step<0>(wd, sc, cexp[word], magic, e, o); break;
-          case 1: expand_step<1>(wd, sc, cexp[word], magic, e, o); break;
-          case 2: expand_step<2>(wd, sc, cexp[word], magic, e, o); break;
-          case 3: expand_step<3>(wd, sc, cexp[word], magic, e, o); break;
-          case 4: expand_step<4>(wd, sc, cexp[word], magic, e, o); break;
-          case 5: expand_step<5>(wd, sc, cexp[word], magic, e, o); break;
-          case 6: expand_step<6>(wd, sc, cexp[word], magic, e, o); break;
-          default: expand_step<7>(wd, sc, cexp[word], magic, e, o); break;
+      for (int rb = 0; rb < 8; ++rb) {
+        if (p == 1 && rb == 0) {
+          wide_store_a(lds.a[1 - h], 1, ra);
+          wide_load_a(asrc, avoff, a.K, gw + kWw, 2, ra);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if (rb == 4) {
+          wide_store_a(lds.a[1 - h], 2 * p, ra);
+          wide_load_a(asrc, avoff, a.K, gw + kWw, 2 * p + 1, ra);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (rb + kAhead < 8) af[(rb + kAhead) & 3] = rd(rb + kAhead);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          mfma_tied(acc[rb][cb], af[rb & 3], bq[cur][cb]);
+          // expansion step (rb * 4 + cb) % 8 of word (rb * 4 + cb) / 8
+          const int x = rb * 4 + cb, word = x >> 3;
+          const uint32_t wd = ring[nslot].w[word];
+          const float sc = ring[nslot].s[word];
+          half8& o = bq[cur ^ 1][word];
+          switch (x & 7) {
+            case 0: expand_step<0>(wd, sc, cexp[word], magic, e, o); break;
+            case 1: expand_step<1>(wd, sc, cexp[word], magic, e, o); break;
+            case 2: expand_step<2>(wd, sc, cexp[word], magic, e, o); break;
+            case 3: expand_step<3>(wd, sc, cexp[word], magic, e, o); break;
+            case 4: expand_step<4>(wd, sc, cexp[word], magic, e, o); break;
+            case 5: expand_step<5>(wd, sc, cexp[word], magic, e, o); break;
+            case 6: expand_step<6>(wd, sc, cexp[word], magic, e, o); break;
+            default: expand_step<7>(wd, sc, cexp[word], magic, e, o); break;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-    wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, own(wi + 1 + kWideRing), a.G - 1, a.gshift, ring[nslot]);
-    __builtin_amdgcn_sched_barrier(0);
-    wide_store_a(lds.a[1 - h], 1, ra);
+      wide_load_codes(wsrc, ssrc, wvoff, svoff, a.N, own(2 * wi + p + 1 + kWideRing), a.G - 1, a.gshift,
+                      ring[nslot]);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    pass(std::integral_constant<int, 0>{});
+    pass(std::integral_constant<int, 1>{});
+    wide_store_a(lds.a[1 - h], 3, ra);
     __syncthreads();
   };
   int w = 0;
