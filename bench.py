@@ -220,6 +220,9 @@ DOMINANT = {
     "moe_prefill_m2048": ("mfma_gate_up", "mfma_kernel<1, 4, 3, false> (gate/up)",
                           lambda n: "mfma_kernel<1, 4, 3, false>" in n, (0, 2)),
     "gemm_m2048_hot_expert": ("wide", "wide_kernel", lambda n: "wide_kernel" in n, None),
+    "mlp_decode_m4_tp8": ("gate_up", "gemv_kernel<1, 2> (gate/up)", lambda n: "gemv_kernel<1, 2>" in n, (0, 2)),
+    "mlp_verify_m64_bf16_tp8": ("mfma_gate_up", "mfma_kernel<1, 8, 2, true> (gate/up)",
+                                lambda n: "mfma_kernel<1, 8, 2, true>" in n, (0, 2)),
 }
 
 
