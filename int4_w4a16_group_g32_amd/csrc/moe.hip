@@ -44,6 +44,34 @@ __host__ __device__ inline int route_waves(int E) {
   return w < 1 ? 1 : (w > kRouteWaves ? kRouteWaves : w);
 }
 
+// Inclusive scan of v over the block's threads in thread order: a shuffle
+// scan within each wave, then over the wave totals (wsum, kRouteWaves
+// entries).  Every thread calls it; it begins and ends with a barrier, so
+// back-to-back calls may reuse wsum.
+__device__ __forceinline__ int block_scan_incl(int v, int* wsum) {
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid % kWave, wv = tid / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) wsum[wv] = v;
+  __syncthreads();
+  if (wv == 0) {
+    int s = lane < kRouteWaves ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kRouteWaves; off <<= 1) {
+      const int t = __shfl_up(s, off);
+      if (lane >= off) s += t;
+    }
+    if (lane < kRouteWaves) wsum[lane] = s;
+  }
+  __syncthreads();
+  return wv > 0 ? v + wsum[wv - 1] : v;
+}
+
 // Lanes of this wave whose key equals this lane's key (keys < 2^bits): one
 // ballot per key bit, intersected.
 __device__ __forceinline__ uint64_t same_key_lanes(int key, int bits) {
@@ -81,7 +109,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     int32_t* __restrict__ heavy, int shared_rows, int gemv_rows, int expert_rows) {
   extern __shared__ int lds[];  // wc[W][E], then tot[E]
   __shared__ int carry;
-  __shared__ int scan[kRouteThreads];
+  __shared__ int any_mfma;  // some expert has more than expert_rows rows
+  __shared__ int wsum[kRouteWaves];
   const int tid = threadIdx.x;
   const int W = route_waves(E);
   int* wc = lds;
@@ -94,6 +123,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const uint64_t below = (1ull << lane) - 1;
 
   for (int i = tid; i < (W + 1) * E; i += kRouteThreads) lds[i] = 0;
+  if (tid == 0) any_mfma = 0;
   __syncthreads();
   // The keys of a wave's pairs are read kRouteChunk steps of 64 at a time,
   // all loads in flight together, instead of one dependent load per step.
@@ -126,6 +156,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     for (int w = 0; w < W; ++w) run += wc[w * E + e];
     tot[e] = run;
     counts[e] = run;
+    if (run > expert_rows) any_mfma = 1;
   }
   __syncthreads();
   // offsets = exclusive scan of the totals (blocks of kRouteThreads, serial carry)
@@ -134,20 +165,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   for (int base = 0; base < E; base += kRouteThreads) {
     const int e = base + tid;
     const int v = e < E ? tot[e] : 0;
-    scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kRouteThreads; off <<= 1) {
-      const int t = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += t;
-      __syncthreads();
-    }
+    const int incl = block_scan_incl(v, wsum);
     if (e < E) {
-      offsets[e] = carry + scan[tid] - v;
-      tot[e] = carry + scan[tid] - v;
+      offsets[e] = carry + incl - v;
+      tot[e] = carry + incl - v;
     }
     __syncthreads();
-    if (tid == kRouteThreads - 1) carry += scan[tid];
+    if (tid == kRouteThreads - 1) carry += incl;
     __syncthreads();
   }
   if (tid == 0) offsets[E] = carry;
@@ -196,44 +220,60 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   // C. work items: exclusive scans over experts of the GEMV and MFMA item counts.
   // The shared expert's items (all of one kind) take the first indices of
   // their launch, so they are dispatched first and the routed experts' items
-  // fill in behind them.
+  // fill in behind them.  MFMA items are laid out longest first: every full
+  // 64-row item (expert order), then the experts' partial last items with 33
+  // to 63 rows, 17 to 32 and 1 to 16, so the cheap items (whose row blocks
+  // without rows skip their MFMAs) run in the launch's last, partly filled
+  // round of workgroups.
   const int shared_kind = shared_rows > kSharedGemvRows ? 1 : 0;
   const int shared_step = shared_kind == 1 ? kMfmaRows : kMaxGemvRows;
   const int shared_items = (shared_rows + shared_step - 1) / shared_step;
-  for (int kind = 0; kind < 2; ++kind) {
-    const int lead = (kSharedFirst && kind == shared_kind) ? shared_items : 0;
-    if (tid == 0) carry = lead;
+  // pass 0: GEMV items; 1: full MFMA items; 2, 3, 4: partial MFMA items by
+  // row class
+  for (int pass = 0; pass < 5; ++pass) {
+    const int kind = pass == 0 ? 0 : 1;
+    if (pass == 1 && any_mfma == 0) {  // no MFMA items but the shared expert's
+      if (tid == 0) n_items[1] = shared_kind == 1 ? shared_items : 0;
+      break;
+    }
+    if (pass < 2) {
+      const int lead = (kSharedFirst && kind == shared_kind) ? shared_items : 0;
+      if (tid == 0) carry = lead;
+    }
     __syncthreads();
     for (int base = 0; base < E; base += kRouteThreads) {
       const int e = base + tid;
       const int c0 = e < E ? counts[e] : 0;
+      const int rem = c0 % kMfmaRows;
       int n = 0;
-      if (kind == 0) n = (c0 > 0 && c0 <= expert_rows) ? (c0 + gemv_rows - 1) / gemv_rows : 0;
-      else n = c0 > expert_rows ? (c0 + kMfmaRows - 1) / kMfmaRows : 0;
-      scan[tid] = n;
-      __syncthreads();
-      for (int off = 1; off < kRouteThreads; off <<= 1) {
-        const int t = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += t;
-        __syncthreads();
+      if (kind == 0) {
+        n = (c0 > 0 && c0 <= expert_rows) ? (c0 + gemv_rows - 1) / gemv_rows : 0;
+      } else if (c0 > expert_rows) {
+        if (pass == 1) n = c0 / kMfmaRows;
+        else if (pass == 2) n = rem > 32 ? 1 : 0;
+        else if (pass == 3) n = rem > 16 && rem <= 32 ? 1 : 0;
+        else n = rem > 0 && rem <= 16 ? 1 : 0;
       }
+      const int incl = block_scan_incl(n, wsum);
       if (n > 0) {
-        int it = carry + scan[tid] - n;
+        int it = carry + incl - n;
         const int o0 = offsets[e];
         if (kind == 0) {
           for (int r = 0; r < c0; r += gemv_rows, ++it)
             items_g[it] = make_int4(e, o0 + r, min(gemv_rows, c0 - r), 0);
+        } else if (pass == 1) {
+          for (int r = 0; r + kMfmaRows <= c0; r += kMfmaRows, ++it)
+            items_m[it] = make_int4(e, o0 + r, kMfmaRows, 0);
         } else {
-          for (int r = 0; r < c0; r += kMfmaRows, ++it)
-            items_m[it] = make_int4(e, o0 + r, min(kMfmaRows, c0 - r), 0);
+          items_m[it] = make_int4(e, o0 + c0 - rem, rem, 0);
         }
       }
       __syncthreads();
-      if (tid == kRouteThreads - 1) carry += scan[tid];
+      if (tid == kRouteThreads - 1) carry += incl;
       __syncthreads();
     }
-    if (tid == 0) n_items[kind] = carry + ((!kSharedFirst && kind == shared_kind) ? shared_items : 0);
+    if ((pass == 0 || pass == 4) && tid == 0)
+      n_items[kind] = carry + ((!kSharedFirst && kind == shared_kind) ? shared_items : 0);
     __syncthreads();
   }
   if (shared_rows > 0 && tid == 0) {
