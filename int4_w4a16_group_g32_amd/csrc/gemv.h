@@ -36,7 +36,8 @@ struct GemvArgs {
   const int4* items;     // grouped mode: {expert, first position, rows, 0}
   const int* n_items;    // grouped mode: number of valid items (device)
   int mode;              // 0: plain, out[position][N]; 1: SwiGLU, h[position][N]
-  float* out;
+  float* out;            // float32, or bf16 (round to nearest even) with out_bf16
+  int out_bf16;
   float* h;              // SwiGLU output h = silu(x Wg) * (x Wu), float32
   float* partials;       // split-K partial tiles
   int* counters;         // split-K arrival counters (zero between calls)

@@ -486,9 +486,17 @@ void gemv_kernel(const GemvArgs a) {
   if (a.mode == 0) {
     const int n = ttile * kGemvCols + t;
     if (mine && n < a.N) {
+      uint16_t* ob = reinterpret_cast<uint16_t*>(a.out);
 #pragma unroll
-      for (int r = 0; r < kRows; ++r)
-        if (r < nrows) a.out[static_cast<size_t>(pos0 + r) * a.N + n] = v[r];
+      for (int r = 0; r < kRows; ++r) {
+        if (r < nrows) {
+          const size_t at = static_cast<size_t>(pos0 + r) * a.N + n;
+          if (a.out_bf16)
+            ob[at] = f32_to_bf16(v[r]);
+          else
+            a.out[at] = v[r];
+        }
+      }
     }
     return;
   }

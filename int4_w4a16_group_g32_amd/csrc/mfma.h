@@ -68,8 +68,9 @@ struct MfmaArgs {
   int dense_rows;        // > 0: dense rows, items of 64 rows
   const int4* items;     // grouped mode: {expert, first position, rows, 0}
   const int* n_items;
-  int mode;              // 0: plain float32 out[pos][N]; 1: SwiGLU, h[pos][N]
-  float* out;
+  int mode;              // 0: plain out[pos][N]; 1: SwiGLU, h[pos][N]
+  float* out;            // float32, or bf16 (round to nearest even) with out_bf16
+  int out_bf16;
   float* h;              // SwiGLU output h[pos][N], float32
   float* partials;
   int* counters;

@@ -508,8 +508,16 @@ __device__ __forceinline__ void tile_finish(const MfmaArgs& a, MfmaLds<P>& lds, 
       if (r < nrows) {
         const size_t prow = static_cast<size_t>(pos0 + r);
         const float f = a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow];
+        if (a.out_bf16) {
+          uint32_t b[4];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) a.out[prow * a.N + col0 + cb] = acc[rb][cb][i] * f;
+          for (int cb = 0; cb < 4; ++cb) b[cb] = f32_to_bf16(acc[rb][cb][i] * f);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + prow * a.N + col0) =
+              make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) a.out[prow * a.N + col0 + cb] = acc[rb][cb][i] * f;
+        }
       }
     }
 }

@@ -285,11 +285,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 }
 
 // y[t][n] = sum over slots, in slot order, of w[t][s] * o[inv[t*top_k+s]][n].
-// A thread produces four consecutive columns (16-byte loads and stores; H is
-// a multiple of 32).
+// A thread produces four consecutive columns (16-byte loads and stores of
+// float32 o, 8-byte loads of bf16 o; H is a multiple of 32).
 // With shared0 >= 0 the shared expert's output row o[shared0 + t] is added
 // last, with weight 1.
-__global__ void combine_kernel(const float* __restrict__ o, const int32_t* __restrict__ inv,
+__device__ __forceinline__ float4 load_o4(const float* o, size_t at) {
+  return *reinterpret_cast<const float4*>(o + at);
+}
+__device__ __forceinline__ float4 load_o4(const uint16_t* o, size_t at) {
+  const uint2 b = *reinterpret_cast<const uint2*>(o + at);
+  return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u), __uint_as_float(b.y << 16),
+                     __uint_as_float(b.y & 0xffff0000u));
+}
+
+template <typename OT>
+__global__ void combine_kernel(const OT* __restrict__ o, const int32_t* __restrict__ inv,
                                const float* __restrict__ topk_w, int M, int top_k, int H, int shared0,
                                float* __restrict__ y) {
   const int H4 = H / 4;
@@ -313,7 +323,7 @@ __global__ void combine_kernel(const float* __restrict__ o, const int32_t* __res
     }
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i)
-      v[i] = reinterpret_cast<const float4*>(o + static_cast<size_t>(pos[i] < 0 ? 0 : pos[i]) * H)[n4];
+      v[i] = load_o4(o, static_cast<size_t>(pos[i] < 0 ? 0 : pos[i]) * H + 4 * static_cast<size_t>(n4));
 #pragma unroll
     for (int i = 0; i < kCombineBatch; ++i) {
       if (pos[i] < 0) continue;
@@ -324,7 +334,7 @@ __global__ void combine_kernel(const float* __restrict__ o, const int32_t* __res
     }
   }
   if (shared0 >= 0) {
-    const float4 v = reinterpret_cast<const float4*>(o + static_cast<size_t>(shared0 + t) * H)[n4];
+    const float4 v = load_o4(o, static_cast<size_t>(shared0 + t) * H + 4 * static_cast<size_t>(n4));
     acc.x += v.x;
     acc.y += v.y;
     acc.z += v.z;
@@ -399,7 +409,7 @@ MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate,
   c.take(p.nitems_off, 16);
   c.take(p.heavy_off, p.positions * 4);
   c.take(p.h_off, std::max<size_t>(p.positions, p.Mp) * I * 4);
-  c.take(p.o_off, p.positions * H * 4);
+  c.take(p.o_off, p.positions * H * (xt == W4A16_BF16 ? 2 : 4));  // per-pair outputs: bf16 for bf16 x
   // activation pieces: one row per token (the tiles map positions to tokens)
   const size_t xrows = p.mfma ? static_cast<size_t>(M) : 0;
   c.take(p.apx_off, static_cast<size_t>(p.P) * xrows * H * 2);
@@ -621,6 +631,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   d.n_items = n_items;
   d.mode = 0;
   d.out = o;
+  d.out_bf16 = xt == W4A16_BF16;
   if (shared) {
     d.extra_plus1 = E + 1;
     d.qw0x = reinterpret_cast<const u32x4*>(sd->qw);
@@ -651,6 +662,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     md.gps = md.G;
     md.mode = 0;
     md.out = o;
+    md.out_bf16 = xt == W4A16_BF16;
     md.h = nullptr;
     md.extra_plus1 = d.extra_plus1;
     md.qw0x = d.qw0x;
@@ -665,8 +677,13 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   // 4. weighted combine in slot order
   bk = ev.bracket();
   const size_t total = static_cast<size_t>(M) * (H / 4);
-  hipExtLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, stream,
-                        bk.start, bk.stop, 0, o, inv, topk_w, M, top_k, H, shared ? R : -1, y);
+  const dim3 cgrid(static_cast<unsigned>((total + 255) / 256));
+  if (xt == W4A16_BF16)
+    hipExtLaunchKernelGGL(combine_kernel<uint16_t>, cgrid, dim3(256), 0, stream, bk.start, bk.stop, 0,
+                          reinterpret_cast<const uint16_t*>(o), inv, topk_w, M, top_k, H, shared ? R : -1, y);
+  else
+    hipExtLaunchKernelGGL(combine_kernel<float>, cgrid, dim3(256), 0, stream, bk.start, bk.stop, 0, o, inv, topk_w,
+                          M, top_k, H, shared ? R : -1, y);
   return launch_status();
 }
 }  // namespace w4
