@@ -312,8 +312,9 @@ W4A16_API size_t w4a16_moe_workspace_bytes(int32_t M, int32_t top_k, w4a16_dtype
  * and topk_w [M][top_k] (int32 / float32), y [M][H] float32.  The routing lists
  * (as w4a16_moe_route), the per-pair intermediate and the per-pair outputs
  * live in the workspace; per-expert row counts never leave the device.  The
- * per-pair outputs are stored in float32 with float32 x and in bf16 (round
- * to nearest even) with bf16 x; the combine sums them in float32.
+ * per-pair intermediate and outputs are stored in float32 with float32 x and
+ * in bf16 (round to nearest even) with bf16 x; the combine sums the outputs
+ * in float32.
  * Experts with at most 8 rows (float32 activations) or 16 rows (bf16) run on
  * the GEMV kernels, heavier experts on MFMA tiles of 64 rows.
  * Errors as w4a16_swiglu_mlp plus INVALID_ARG for top_k < 1 or top_k > E and

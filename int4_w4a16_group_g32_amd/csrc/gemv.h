@@ -38,7 +38,8 @@ struct GemvArgs {
   int mode;              // 0: plain, out[position][N]; 1: SwiGLU, h[position][N]
   float* out;            // float32, or bf16 (round to nearest even) with out_bf16
   int out_bf16;
-  float* h;              // SwiGLU output h = silu(x Wg) * (x Wu), float32
+  float* h;              // SwiGLU output h = silu(x Wg) * (x Wu): float32, or bf16 with h_bf16
+  int h_bf16;
   float* partials;       // split-K partial tiles
   int* counters;         // split-K arrival counters (zero between calls)
 };

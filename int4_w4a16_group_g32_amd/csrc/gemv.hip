@@ -510,10 +510,16 @@ void gemv_kernel(const GemvArgs a) {
   const int n = ttile * (kGemvCols / 2) + t;
   if (mine && t < kGemvCols / 2 && n < a.N) {
 #pragma unroll
-    for (int r = 0; r < kRows; ++r)
-      if (r < nrows)
-        a.h[static_cast<size_t>(pos0 + r) * a.N + n] =
-            silu(tred[r * kGemvCols + t]) * tred[r * kGemvCols + kGemvCols / 2 + t];
+    for (int r = 0; r < kRows; ++r) {
+      if (r < nrows) {
+        const size_t at = static_cast<size_t>(pos0 + r) * a.N + n;
+        const float hv = silu(tred[r * kGemvCols + t]) * tred[r * kGemvCols + kGemvCols / 2 + t];
+        if (a.h_bf16)
+          reinterpret_cast<uint16_t*>(a.h)[at] = f32_to_bf16(hv);
+        else
+          a.h[at] = hv;
+      }
+    }
   }
 }
 

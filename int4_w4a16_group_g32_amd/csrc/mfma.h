@@ -71,7 +71,8 @@ struct MfmaArgs {
   int mode;              // 0: plain out[pos][N]; 1: SwiGLU, h[pos][N]
   float* out;            // float32, or bf16 (round to nearest even) with out_bf16
   int out_bf16;
-  float* h;              // SwiGLU output h[pos][N], float32
+  float* h;              // SwiGLU output h[pos][N]: float32, or bf16 with h_bf16
+  int h_bf16;
   float* partials;
   int* counters;
   // Deferred split-K (dense launches with S > 1): with `planes` set, each

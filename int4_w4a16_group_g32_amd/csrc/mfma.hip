@@ -490,10 +490,19 @@ __device__ __forceinline__ void tile_finish(const MfmaArgs& a, MfmaLds<P>& lds, 
         if (r < nrows) {
           const size_t prow = static_cast<size_t>(pos0 + r);
           const float f = a.rs[a.arow != nullptr ? a.arow[prow] / a.arow_div : prow];
+          float hv[4];
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
             const float up = xu[(((wv & 1) * 64 + (rb * 4 + cb) * 4 + i) << 6) + lane];
-            a.h[prow * a.N + col0 + cb] = silu(acc[rb][cb][i] * f) * (up * f);
+            hv[cb] = silu(acc[rb][cb][i] * f) * (up * f);
+          }
+          if (a.h_bf16) {
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + prow * a.N + col0) =
+                make_uint2(f32_to_bf16(hv[0]) | (static_cast<uint32_t>(f32_to_bf16(hv[1])) << 16),
+                           f32_to_bf16(hv[2]) | (static_cast<uint32_t>(f32_to_bf16(hv[3])) << 16));
+          } else {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) a.h[prow * a.N + col0 + cb] = hv[cb];
           }
         }
       }

@@ -408,7 +408,7 @@ MoePlan plan_moe(int M, int top_k, w4a16_dtype_t xt, const w4a16_weight_t* gate,
   c.take(p.mitems_off, std::max<size_t>(p.max_mitems, 1) * 16);
   c.take(p.nitems_off, 16);
   c.take(p.heavy_off, p.positions * 4);
-  c.take(p.h_off, std::max<size_t>(p.positions, p.Mp) * I * 4);
+  c.take(p.h_off, std::max<size_t>(p.positions, p.Mp) * I * (xt == W4A16_BF16 ? 2 : 4));  // bf16 for bf16 x
   c.take(p.o_off, p.positions * H * (xt == W4A16_BF16 ? 2 : 4));  // per-pair outputs: bf16 for bf16 x
   // activation pieces: one row per token (the tiles map positions to tokens)
   const size_t xrows = p.mfma ? static_cast<size_t>(M) : 0;
@@ -557,6 +557,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   a.n_items = n_items;
   a.mode = 1;
   a.h = hraw;
+  a.h_bf16 = xt == W4A16_BF16;
   if (shared) {
     a.extra_plus1 = E + 1;
     a.qw0x = reinterpret_cast<const u32x4*>(sg->qw);
@@ -601,6 +602,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
     ma.n_items = n_items + 1;
     ma.mode = 1;
     ma.h = hraw;
+    ma.h_bf16 = xt == W4A16_BF16;
     ma.extra_plus1 = a.extra_plus1;
     ma.qw0x = a.qw0x;
     ma.sc0x = a.sc0x;
@@ -614,7 +616,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   // 3. down projection into per-pair outputs
   GemvArgs d{};
   d.x = hraw;
-  d.x_bf16 = 0;
+  d.x_bf16 = xt == W4A16_BF16;
   d.pieces = gemv_pieces(xt);  // the items hold up to gemv_rows(xt) rows
   d.G = I / kGroup;
   d.K = I;
@@ -642,7 +644,7 @@ static w4a16_status_t moe_impl(const void* x, w4a16_dtype_t xt, int32_t M, const
   if (st != W4A16_OK) return st;
   if (p.mfma) {
     bk = ev.bracket();
-    st = launch_mfma_prep(hraw, W4A16_F32, T, p.Mp, I, p.P, nullptr, 0, heavy, aph, rsh, stream, bk.start, bk.stop);
+    st = launch_mfma_prep(hraw, xt, T, p.Mp, I, p.P, nullptr, 0, heavy, aph, rsh, stream, bk.start, bk.stop);
     if (st != W4A16_OK) return st;
     MfmaArgs md = ma;
     md.ap = aph;
