@@ -200,7 +200,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
           const int pos = wc[wv * E + key[j]] + __popcll(m & below);
           sorted_pairs[pos] = p;
           inv[p] = pos;
-          if (heavy != nullptr) heavy[pos] = counts[key[j]] > expert_rows ? 1 : 0;
+          if (heavy != nullptr) {
+            // the expert's row count from the offsets in LDS (no global load per step)
+            const int cnt = (key[j] + 1 < E ? tot[key[j] + 1] : carry) - tot[key[j]];
+            heavy[pos] = cnt > expert_rows ? 1 : 0;
+          }
         } else if (p < p1) {
           inv[p] = -1;
         }
