@@ -111,6 +111,49 @@ def _random_expert_codes(E, H, I, seed):
     return out
 
 
+# Rows per expert on both sides of every item boundary: the GEMV limit
+# (8 rows with float32 activations, 16 with bf16), the partial 64-row tile
+# classes (1-16, 17-32, 33-63 rows) and whole tiles (64, 128) plus one row.
+_ROW_COUNTS = [1, 8, 9, 15, 16, 17, 31, 32, 33, 42, 63, 64, 65, 127, 128, 129]
+
+
+def _ids_with_counts(counts, M, k):
+    """Top-k ids [M][k] in which expert e appears counts[e] times, never twice
+    in one token: the pairs of expert 0, then 1, ... are dealt column-major
+    (pair j to token j % M), so a run of at most M pairs covers distinct
+    tokens."""
+    pairs = np.repeat(np.arange(len(counts)), counts)
+    assert len(pairs) == M * k and max(counts) <= M
+    ids = np.empty((M, k), dtype=np.int32)
+    for j, e in enumerate(pairs):
+        ids[j % M, j // M] = e
+    return ids
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_moe_item_boundaries(dtype):
+    """Experts whose row counts sit on both sides of every item boundary, so
+    the route kernel emits GEMV items, whole 64-row items and partial items
+    of each class, in one layer."""
+    M, k, H, I = 130, 6, 128, 128
+    E = len(_ROW_COUNTS)
+    assert sum(_ROW_COUNTS) == M * k
+    cfg = 650
+    ids = _ids_with_counts(_ROW_COUNTS, M, k)
+    assert (np.bincount(ids.ravel(), minlength=E) == np.array(_ROW_COUNTS)).all()
+    assert all(len(set(r)) == k for r in ids.tolist())
+    (gq, gs), (uq, us), (dq, ds) = _experts(E, H, I, cfg)
+    g, u, d = weight_from_codes(gq, gs), weight_from_codes(uq, us), weight_from_codes(dq, ds)
+    wts = W.gate_weights(M, k, cfg)
+    x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
+    y = _moe_gpu(x, to_dev(ids), to_dev(wts), g, u, d)
+    ref, bound = _moe_ref(x, ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E, dtype)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, bound, f"moe item boundaries {dtype}")
+    print(f"moe item boundaries {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
+    assert err <= tol_for(dtype)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M,E,k,H,I", [(5, 8, 3, 128, 64), (24, 16, 8, 128, 128), (200, 4, 2, 128, 256)])
 def test_moe_random_codes_include_nibble_zero(M, E, k, H, I, dtype):
