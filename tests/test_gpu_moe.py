@@ -28,7 +28,10 @@ def _route_gpu(ids_np, E):
 
 @pytest.mark.parametrize("M,E,k,kind", [(1, 8, 2, "uniform"), (64, 384, 8, "uniform"),
                                         (2048, 384, 8, "zipf"), (300, 16, 4, "uniform"),
-                                        (5000, 1000, 6, "uniform"), (4096, 3, 1, "uniform")])
+                                        (5000, 1000, 6, "uniform"), (4096, 3, 1, "uniform"),
+                                        # more experts than the route kernel's 1024 threads: its scans
+                                        # over experts run in several blocks with a carry
+                                        (3000, 2500, 4, "uniform"), (1024, 6144, 8, "zipf")])
 def test_route_bit_exact(M, E, k, kind):
     ids = (W.topk_zipf(M, E, k, 1.1, 900) if kind == "zipf" else W.topk_uniform(M, E, k, 900 + M))
     got = _route_gpu(ids, E)
@@ -109,6 +112,27 @@ def _random_expert_codes(E, H, I, seed):
         qw = rng.integers(0, 2 ** 32, size=(E, K // 8, N), dtype=np.uint64).astype(np.uint32).view(np.int32)
         out.append((qw, (rng.random((E, K // 32, N)) * 0.005 + 0.004).astype(np.float32)))
     return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_moe_more_experts_than_route_threads(dtype):
+    """1500 experts under Zipf routing: the work-item scans over experts run
+    in two blocks of 1024, with both GEMV and MFMA items."""
+    M, E, k, H, I = 300, 1500, 4, 64, 64
+    cfg = 660
+    ids = W.topk_zipf(M, E, k, 1.1, cfg)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    assert counts.max() > 64 and ((counts > 0) & (counts <= 8)).sum() > 100
+    (gq, gs), (uq, us), (dq, ds) = _experts(E, H, I, cfg)
+    g, u, d = weight_from_codes(gq, gs), weight_from_codes(uq, us), weight_from_codes(dq, ds)
+    wts = W.gate_weights(M, k, cfg)
+    x = x_for_dtype(W.activations(M, H, cfg).cuda(), dtype)
+    y = _moe_gpu(x, to_dev(ids), to_dev(wts), g, u, d)
+    ref, bound = _moe_ref(x, ids, wts, lambda e: ((gq[e], gs[e]), (uq[e], us[e]), (dq[e], ds[e])), E, dtype)
+    err = rel_err(y, ref)
+    worst = check_elementwise(y.cpu().numpy(), ref, bound, f"moe E={E} {dtype}")
+    print(f"moe E={E} M={M} k={k} {dtype} relF={err:.3e} worst/bound={worst:.2e}", flush=True)
+    assert err <= tol_for(dtype)
 
 
 # Rows per expert on both sides of every item boundary: the GEMV limit
