@@ -329,15 +329,21 @@ void gemv_kernel(const GemvArgs a) {
   f32x4 tot[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) tot[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // ring of kRing groups in flight: group g sits in slot (g - g_lo) % kRing
-  GroupCodes ring[kRing];
+  // ring of kR groups in flight: group g sits in slot (g - g_lo) % kR.
+  // Four-quad workgroups (the decode gate/up) take a ring of 2 and so meet
+  // at a pacing barrier every 2 groups: 33.0-33.4 against 33.8-34.1 us for
+  // that launch (a ring of 2 with the barrier every 2 groups made the
+  // two-quad down projection slower, 23.2 against 21.3 us).
+  constexpr int kR = kT >= 4 ? 2 : kRing;
+  static_assert(kWin % kR == 0, "ring slots must stay aligned across windows");
+  GroupCodes ring[kR];
   float xv[St::kHold][16];
   load_window<kW, kRows>(a, g_lo, min(kWin, g_hi - g_lo), pos0, nrows, wv, lane, 0, xv);  // ahead of the weights
   // A wave past the matrix's last column streams column block 0 and stores
   // nothing: the ring loads stay unconditional, so the compiler's waits can
   // count them.
 #pragma unroll
-  for (int j = 0; j < kRing; ++j) load_group(wp, sp, gstride, g_lo + j, g_last, a.gshift, ring[j]);
+  for (int j = 0; j < kR; ++j) load_group(wp, sp, gstride, g_lo + j, g_last, a.gshift, ring[j]);
 
   for (int gw = g_lo; gw < g_hi; gw += kWin) {
     const int nw = min(kWin, g_hi - gw);
@@ -366,14 +372,14 @@ void gemv_kernel(const GemvArgs a) {
           for (int i = 0; i < 4; ++i) tot[cb][i] *= fr[i];
       }
       f32x4* acc = tot;
-      // kWin is a multiple of kRing, so slots stay aligned across windows; the
-      // loads run kRing groups ahead
-      for (int gl = 0; gl < nw; gl += kRing) {
+      // kWin is a multiple of kR, so slots stay aligned across windows; the
+      // loads run kR groups ahead
+      for (int gl = 0; gl < nw; gl += kR) {
 #pragma unroll
-        for (int j = 0; j < kRing; ++j) {
+        for (int j = 0; j < kR; ++j) {
           const bool on = gl + j < nw;
           mma_group(lds, on ? gl + j : gl, lc, kb, arow && on, magic, ring[j], acc);
-          load_group(wp, sp, gstride, gw + gl + j + kRing, g_last, a.gshift, ring[j]);
+          load_group(wp, sp, gstride, gw + gl + j + kR, g_last, a.gshift, ring[j]);
           // keep each refill right behind its consumer: the scheduler would
           // otherwise sink all refills to the end and drain the ring
           __builtin_amdgcn_sched_barrier(0);
@@ -382,7 +388,7 @@ void gemv_kernel(const GemvArgs a) {
         // barrier the quads of a workgroup finish one after another and the
         // CU's loads in flight fall off long before the end.  A bare barrier
         // (no memory fence, so no wait on the ring) keeps them in step.
-        if (kT > 1 && kPace > 0 && (gl / kRing) % kPace == kPace - 1) __builtin_amdgcn_s_barrier();
+        if (kT > 1 && kPace > 0 && (gl / kR) % kPace == kPace - 1) __builtin_amdgcn_s_barrier();
       }
     }
   }
