@@ -274,12 +274,15 @@ def test_gemm_hot_expert_full_size():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M", [1, 4, 8])
-def test_gemv_four_tile_workgroups_ragged(M, dtype):
+@pytest.mark.parametrize("K", [16384, 16352])
+def test_gemv_four_tile_workgroups_ragged(M, dtype, K):
     """K = 16384, N = 16128: 63 column tiles of 256 and 16 K splits, 1008 tasks,
     which the GEMV runs as 256 workgroups of four column tiles; the last
-    workgroup has one quad past the matrix.  Sampled columns (the last tiles
-    among them) against the oracle, which quantizes the same float32 weights."""
-    K, N, cfg = 16384, 16128, 520
+    workgroup has one quad past the matrix.  K = 16352 (511 groups): the last
+    split holds 31 groups, an odd count for the two-group ring of four-quad
+    workgroups.  Sampled columns (the last tiles among them) against the
+    oracle, which quantizes the same float32 weights."""
+    N, cfg = 16128, 520
     wd = W.weights(K, N, cfg, W.TAG_GATE, device="cuda")
     w = L.quantize_to_weight(wd)
     x = x_for_dtype(W.activations(M, K, cfg + M).cuda(), dtype)
